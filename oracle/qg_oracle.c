@@ -1,0 +1,298 @@
+/*
+ * qg_oracle.c -- CPU oracle for the quantized decode matrix-vector product.
+ *
+ * TEST INFRASTRUCTURE. This is the plain, slow, obviously correct definition
+ * of what the GPU library computes, in double precision, written from the
+ * pages that describe the method. Only the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it. It shares no code, header,
+ * table or helper with the GPU library, and the GPU library never calls it.
+ *
+ * Sources (page title, then the section used):
+ *  [F]  "Booster la vitesse d'inference sur Apple Silicon -- avec le format
+ *       .forge" (web research report): TL;DR (decode is bandwidth bound),
+ *       section 1 "Le chemin de decodage rapide" (fused-dequant GEMV, the
+ *       fusions: rmsnorm+QKV, residual+norm, gate.up SwiGLU, logits+top-k),
+ *       section 3 item 4 (planar 4-bit codes packed in uint32 with separate
+ *       scale and bias tensors, group 64; LUT type with 16 fp16 entries).
+ *  [G]  GeekNews item on a C/Metal engine running a 397B MoE on a MacBook
+ *       Pro: "Architecture du modele" (512 experts, K=4 active incl. one
+ *       shared), "Noyau de dequantification optimise FMA" (the weight is
+ *       nibble*scale+bias), "Shaders de calcul Metal" and "Deferred GPU
+ *       Expert Compute" (MoE combine + residual + norm on the GPU).
+ *
+ * Readings where the pages are silent:
+ *  - code k of a row sits in word k/(32/bits) at bit offset bits*(k mod
+ *    32/bits), least significant field first;
+ *  - a group is 64 consecutive k of one row;
+ *  - LUT format: one 16-entry fp16 table per output row, no scale/bias;
+ *  - RMSNorm: x_k * g_k / sqrt(mean_j x_j^2 + eps);
+ *  - SwiGLU: silu(gate) * up, silu(z) = z / (1 + exp(-z));
+ *  - top-k order: larger value first, equal values by lower index; NaN is
+ *    below every number;
+ *  - routing weights: softmax over the selected logits only.
+ *
+ * Everything is computed in double. Dequantized weights q*s+b are exact in
+ * double (q has 4 bits, s and b are fp16). Dot products run in k order.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OG_AFFINE 0
+#define OG_LUT 1
+
+/* A planar quantized matrix as the oracle sees it ([F] section 3 item 4). */
+typedef struct og_qmat {
+    const uint32_t *q;      /* [N][K*bits/32] code words */
+    const uint16_t *scales; /* [N][K/group] fp16 bits, affine only */
+    const uint16_t *biases; /* [N][K/group] fp16 bits, affine only */
+    const uint16_t *lut;    /* [N][2^bits] fp16 bits, LUT only */
+    int N, K, group, bits, fmt;
+} og_qmat;
+
+/* IEEE 754 binary16 -> double, from the format definition: 1 sign bit,
+ * 5 exponent bits (bias 15), 10 fraction bits; exponent 0 encodes zero and
+ * subnormals (fraction * 2^-24), exponent 31 encodes infinities and NaN. */
+double og_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+static int valid_qmat(const og_qmat *W)
+{
+    if (!W || !W->q || W->N < 0 || W->K < 0)
+        return 0;
+    if (W->bits != 2 && W->bits != 4)
+        return 0;
+    if (W->group <= 0 || W->K % W->group || (W->K * W->bits) % 32)
+        return 0;
+    if (W->fmt == OG_AFFINE)
+        return W->scales && W->biases;
+    if (W->fmt == OG_LUT)
+        return W->lut != NULL;
+    return 0;
+}
+
+/* Code (quantized value) of element (n, k). */
+static unsigned code_at(const og_qmat *W, int n, int k)
+{
+    int per_word = 32 / W->bits;
+    size_t words_per_row = (size_t)W->K / per_word;
+    uint32_t word = W->q[(size_t)n * words_per_row + k / per_word];
+    unsigned shift = (unsigned)(W->bits * (k % per_word));
+    return (word >> shift) & ((1u << W->bits) - 1u);
+}
+
+/* Dequantized weight W[n][k]: code*scale + bias for the affine format
+ * ([G] FMA section writes the weight as nibble*scale + bias), or the row's
+ * table entry for the LUT format ([F] section 3 item 4). */
+static double weight_at(const og_qmat *W, int n, int k)
+{
+    unsigned c = code_at(W, n, k);
+    if (W->fmt == OG_LUT)
+        return og_half_to_double(W->lut[(size_t)n * (1u << W->bits) + c]);
+    size_t groups_per_row = (size_t)W->K / W->group;
+    size_t gi = (size_t)n * groups_per_row + k / W->group;
+    return (double)c * og_half_to_double(W->scales[gi]) + og_half_to_double(W->biases[gi]);
+}
+
+/* Codes of rows [0,N): codes[n*K + k]. */
+int og_unpack(const og_qmat *W, uint8_t *codes)
+{
+    if (!valid_qmat(W) || !codes)
+        return -1;
+    for (int n = 0; n < W->N; ++n)
+        for (int k = 0; k < W->K; ++k)
+            codes[(size_t)n * W->K + k] = (uint8_t)code_at(W, n, k);
+    return 0;
+}
+
+/* Dense dequantized matrix: out[n*K + k] = W[n][k]. */
+int og_dequant(const og_qmat *W, double *out)
+{
+    if (!valid_qmat(W) || !out)
+        return -1;
+    for (int n = 0; n < W->N; ++n)
+        for (int k = 0; k < W->K; ++k)
+            out[(size_t)n * W->K + k] = weight_at(W, n, k);
+    return 0;
+}
+
+/* ---- matrix-vector product ---------------------------------------------
+ * y[m][n] = r[m][n] + sum_k W[n][k] * x[m][k]  ([F] section 1: the decode
+ * matvec that dequantizes inside its loop; r is the optional residual). Rows
+ * are independent, so splitting them over threads does not change any
+ * result. */
+typedef struct {
+    const og_qmat *W;
+    int M, n0, n1;
+    const double *x, *residual;
+    double *y;
+} gemv_job;
+
+static void *gemv_rows(void *arg)
+{
+    gemv_job *j = (gemv_job *)arg;
+    const og_qmat *W = j->W;
+    for (int m = 0; m < j->M; ++m) {
+        const double *xm = j->x + (size_t)m * W->K;
+        for (int n = j->n0; n < j->n1; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < W->K; ++k)
+                acc += weight_at(W, n, k) * xm[k];
+            size_t o = (size_t)m * W->N + n;
+            j->y[o] = (j->residual ? j->residual[o] : 0.0) + acc;
+        }
+    }
+    return NULL;
+}
+
+int og_gemv(const og_qmat *W, int M, const double *x, const double *residual, double *y,
+            int nthreads)
+{
+    if (!valid_qmat(W) || M < 1 || !x || !y)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (nthreads > W->N)
+        nthreads = W->N > 0 ? W->N : 1;
+    gemv_job jobs[256];
+    pthread_t tids[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].W = W;
+        jobs[t].M = M;
+        jobs[t].n0 = (int)((long long)W->N * t / nthreads);
+        jobs[t].n1 = (int)((long long)W->N * (t + 1) / nthreads);
+        jobs[t].x = x;
+        jobs[t].residual = residual;
+        jobs[t].y = y;
+    }
+    if (nthreads == 1) {
+        gemv_rows(&jobs[0]);
+        return 0;
+    }
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, gemv_rows, &jobs[t]) != 0)
+            break;
+        ++started;
+    }
+    for (int t = started; t < nthreads; ++t) /* could not spawn: do it here */
+        gemv_rows(&jobs[t]);
+    for (int t = 0; t < started; ++t)
+        pthread_join(tids[t], NULL);
+    return 0;
+}
+
+/* ---- RMSNorm ([F] section 1, fused into the QKV matvec) -----------------
+ * out_k = x_k * g_k / sqrt((1/K) sum_j x_j^2 + eps). */
+int og_rmsnorm(const double *x, int K, const uint16_t *g, double eps, double *out)
+{
+    if (!x || !g || !out || K < 1)
+        return -1;
+    double ss = 0.0;
+    for (int k = 0; k < K; ++k)
+        ss += x[k] * x[k];
+    double denom = sqrt(ss / K + eps);
+    for (int k = 0; k < K; ++k)
+        out[k] = x[k] * og_half_to_double(g[k]) / denom;
+    return 0;
+}
+
+/* silu(z) = z / (1 + exp(-z)). */
+double og_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* ---- gate.up SwiGLU in one step ([F] section 1) --------------------------
+ * u[m][j] = silu((Wg x_m)_j) * (Wu x_m)_j. */
+int og_swiglu(const og_qmat *Wg, const og_qmat *Wu, int M, const double *x, double *u,
+              int nthreads)
+{
+    if (!valid_qmat(Wg) || !valid_qmat(Wu) || Wg->N != Wu->N || Wg->K != Wu->K || !u)
+        return -1;
+    size_t n = (size_t)M * Wg->N;
+    double *a = (double *)malloc(n * sizeof(double));
+    double *c = (double *)malloc(n * sizeof(double));
+    int rc = -1;
+    if (a && c && og_gemv(Wg, M, x, NULL, a, nthreads) == 0 &&
+        og_gemv(Wu, M, x, NULL, c, nthreads) == 0) {
+        for (size_t i = 0; i < n; ++i)
+            u[i] = og_silu(a[i]) * c[i];
+        rc = 0;
+    }
+    free(a);
+    free(c);
+    return rc;
+}
+
+/* ---- top-k -------------------------------------------------------------
+ * "a before b": a larger, or equal and with a lower index. NaN is below every
+ * number (equal NaNs again by index). +0 and -0 are equal. */
+static int before(double va, int ia, double vb, int ib)
+{
+    int na = isnan(va), nb = isnan(vb);
+    if (na || nb) {
+        if (na && nb)
+            return ia < ib;
+        return nb; /* a number is before NaN */
+    }
+    if (va != vb)
+        return va > vb;
+    return ia < ib;
+}
+
+/* The first k elements of z under the order above, by repeated selection of
+ * the best element not yet taken ([F] section 1: logits matvec + top-k on
+ * the GPU, returning only the chosen entries). */
+int og_topk(const double *z, int V, int k, int32_t *idx, double *vals)
+{
+    if (!z || !idx || V < 1 || k < 1 || k > V)
+        return -1;
+    unsigned char *taken = (unsigned char *)calloc((size_t)V, 1);
+    if (!taken)
+        return -1;
+    for (int r = 0; r < k; ++r) {
+        int best = -1;
+        for (int i = 0; i < V; ++i) {
+            if (taken[i])
+                continue;
+            if (best < 0 || before(z[i], i, z[best], best))
+                best = i;
+        }
+        taken[best] = 1;
+        idx[r] = best;
+        if (vals)
+            vals[r] = z[best];
+    }
+    free(taken);
+    return 0;
+}
+
+/* ---- MoE routing ([G] "Architecture du modele") ---------------------------
+ * ids = top-k of the router logits; w_i = exp(l_i - l_max) / sum_{j in ids}
+ * exp(l_j - l_max): softmax over the selected logits. */
+int og_route(const double *logits, int E, int k, int32_t *ids, double *w)
+{
+    if (og_topk(logits, E, k, ids, NULL) != 0 || !w)
+        return -1;
+    double lmax = logits[ids[0]];
+    double den = 0.0;
+    for (int i = 0; i < k; ++i)
+        den += exp(logits[ids[i]] - lmax);
+    for (int i = 0; i < k; ++i)
+        w[i] = exp(logits[ids[i]] - lmax) / den;
+    return 0;
+}

@@ -1,0 +1,344 @@
+"""Pins for the CPU oracle: every check compares it with something other than
+itself (hand-computed values, closed forms, invariants, library routines,
+brute force on tiny inputs). CPU only."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import synth
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Independent packer: field j of each word holds codes[..., j]."""
+    per = 32 // bits
+    c = codes.astype(np.uint64).reshape(codes.shape[0], -1, per)
+    shifts = (np.arange(per, dtype=np.uint64) * np.uint64(bits))
+    return (c << shifts).sum(axis=-1).astype(np.uint32)
+
+
+def make_mat(codes, bits, scales=None, biases=None, lut=None, group=64):
+    N, K = codes.shape
+    fmt = synth.LUT if lut is not None else synth.AFFINE
+    return {"N": N, "K": K, "bits": bits, "fmt": fmt, "group": group,
+            "q": pack_codes(codes, bits),
+            "scales": None if scales is None else np.asarray(scales, np.float16),
+            "biases": None if biases is None else np.asarray(biases, np.float16),
+            "lut": None if lut is None else np.asarray(lut, np.float16)}
+
+
+def const_mat(N, K, bits, word, scale, bias, group=64):
+    per_row = K * bits // 32
+    return {"N": N, "K": K, "bits": bits, "fmt": synth.AFFINE, "group": group,
+            "q": np.full((N, per_row), word, np.uint32),
+            "scales": np.full((N, K // group), scale, np.float16),
+            "biases": np.full((N, K // group), bias, np.float16), "lut": None}
+
+
+# ---------------------------------------------------------------------------
+def test_half_decoder_all_patterns():
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(p)) for p in pats])
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (got == ref))
+    assert np.array_equal(np.signbit(got[~both_nan]), np.signbit(ref[~both_nan]))
+
+
+@pytest.mark.parametrize("case", GOLDEN["unpack"])
+def test_unpack_hand_words(case):
+    bits = case["bits"]
+    per = 32 // bits
+    W = const_mat(1, 64, bits, int(case["word"], 16), 1.0, 0.0)
+    codes = oracle.unpack(W)[0]
+    for w in range(64 // per):
+        assert list(codes[w * per:(w + 1) * per]) == case["codes"]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_unpack_roundtrip_independent_packer(bits):
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 1 << bits, size=(5, 192), dtype=np.uint8)
+    W = make_mat(codes, bits, np.ones((5, 3)), np.zeros((5, 3)))
+    assert np.array_equal(oracle.unpack(W), codes)
+    # and the other way: random words survive unpack -> pack
+    W2 = synth.qmat(3, "rt", 4, 256, bits)
+    assert np.array_equal(pack_codes(oracle.unpack(W2), bits), W2["q"])
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_dequant_special_cases(bits):
+    rng = np.random.default_rng(11)
+    N, K = 6, 256
+    codes = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    s = synth.uniform(rng, (N, K // 64), 0.005, 0.02)
+    b = synth.uniform(rng, (N, K // 64), -0.1, 0.1)
+    ones = np.ones((N, K // 64), np.float16)
+    zeros = np.zeros((N, K // 64), np.float16)
+    # s=1, b=0: the weights are the codes
+    assert np.array_equal(oracle.dequant(make_mat(codes, bits, ones, zeros)), codes)
+    # s=0: every weight of a group is its bias (64 consecutive k of one row)
+    Wb = oracle.dequant(make_mat(codes, bits, zeros, b))
+    assert np.array_equal(Wb, np.repeat(b.astype(np.float64), 64, axis=1))
+    # codes all 1, b=0: every weight of a group is its scale
+    Ws = oracle.dequant(make_mat(np.ones_like(codes), bits, s, zeros))
+    assert np.array_equal(Ws, np.repeat(s.astype(np.float64), 64, axis=1))
+    # the affine form is additive in (s, b) and exact in double
+    W = oracle.dequant(make_mat(codes, bits, s, b))
+    W0 = oracle.dequant(make_mat(codes, bits, s, zeros))
+    assert np.array_equal(W, W0 + Wb)
+    # round trip: the codes are recovered from the dequantized weights
+    rec = np.rint((W - np.repeat(b.astype(np.float64), 64, 1)) / np.repeat(s.astype(np.float64), 64, 1))
+    assert np.array_equal(rec, codes)
+
+
+def test_dequant_lut():
+    rng = np.random.default_rng(12)
+    N, K = 3, 128
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    ident = np.tile(np.arange(16, dtype=np.float16), (N, 1))
+    assert np.array_equal(oracle.dequant(make_mat(codes, 4, lut=ident)), codes)
+    lut = synth.normal(rng, (N, 16), 0.0, 0.02)
+    W = oracle.dequant(make_mat(codes, 4, lut=lut))
+    for n in range(N):
+        for k in range(K):
+            assert W[n, k] == float(lut[n, codes[n, k]])
+
+
+@pytest.mark.parametrize("case", GOLDEN["gemv"])
+def test_gemv_hand_cases(case):
+    W = const_mat(1, case["K"], case["bits"], int(case["word"], 16), case["scale"], case["bias"])
+    x = np.ones(case["K"]) if case["x"] == "ones" else np.tile([1.0, -1.0], case["K"] // 2)
+    assert oracle.gemv(W, x)[0] == case["y"]
+
+
+@pytest.mark.parametrize("bits,fmt", [(4, synth.AFFINE), (2, synth.AFFINE), (4, synth.LUT)])
+def test_gemv_matches_library_matmul(bits, fmt):
+    W = synth.qmat(5, ("mm", bits, fmt), 37, 320, bits, fmt)
+    X = synth.activations(5, "mmx", (3, 320), np.float32)
+    dense = oracle.dequant(W)
+    ref = np.matmul(X.astype(np.float64), dense.T)
+    got = oracle.gemv(W, X)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # rows are independent of the thread split
+    assert np.array_equal(oracle.gemv(W, X, nthreads=4), got)
+    # each activation vector alone gives the same row
+    for m in range(3):
+        assert np.array_equal(oracle.gemv(W, X[m]), got[m])
+
+
+def test_gemv_power16_probe_decodes_codes():
+    """s=1, b=0 and x = 16^j at four columns: y_n spells out the four codes."""
+    W = synth.qmat(9, "p16", 50, 128, 4)
+    W["scales"][:] = 1
+    W["biases"][:] = 0
+    codes = oracle.unpack(W)
+    cols = [3, 64, 70, 127]
+    x = np.zeros(128)
+    for j, c in enumerate(cols):
+        x[c] = 16.0 ** j
+    y = oracle.gemv(W, x).astype(np.int64)
+    for j, c in enumerate(cols):
+        assert np.array_equal((y >> (4 * j)) & 15, codes[:, c])
+
+
+def test_gemv_all_ones_closed_form():
+    W = synth.qmat(4, "ones", 20, 256, 4)
+    codes = oracle.unpack(W).astype(np.float64)
+    s = W["scales"].astype(np.float64)
+    b = W["biases"].astype(np.float64)
+    gsum = codes.reshape(20, 4, 64).sum(-1)
+    ref = (s * gsum + 64 * b).sum(-1)
+    np.testing.assert_allclose(oracle.gemv(W, np.ones(256)), ref, rtol=1e-13)
+
+
+def test_gemv_zero_scale_is_bias_times_group_sums():
+    W = synth.qmat(4, "s0", 10, 256, 4)
+    W["scales"][:] = 0
+    x = synth.activations(4, "s0x", 256, np.float32).astype(np.float64)
+    ref = (W["biases"].astype(np.float64) * x.reshape(4, 64).sum(-1)).sum(-1)
+    np.testing.assert_allclose(oracle.gemv(W, x), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_gemv_residual_and_linearity():
+    W = synth.qmat(6, "lin", 16, 128, 4)
+    x1 = synth.activations(6, "x1", 128, np.float32).astype(np.float64)
+    x2 = synth.activations(6, "x2", 128, np.float32).astype(np.float64)
+    r = synth.activations(6, "r", 16, np.float32).astype(np.float64)
+    y1, y2 = oracle.gemv(W, x1), oracle.gemv(W, x2)
+    np.testing.assert_allclose(oracle.gemv(W, x1 + x2), y1 + y2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.gemv(W, x1, r), y1 + r, rtol=1e-15, atol=1e-15)
+
+
+def test_oracle_rejects_bad_shapes():
+    W = synth.qmat(1, "bad", 4, 128, 4)
+    W["K"] = 100
+    with pytest.raises(ValueError):
+        oracle.gemv(W, np.ones(100))
+    W = synth.qmat(1, "bad", 4, 128, 4)
+    W["bits"] = 3
+    with pytest.raises(ValueError):
+        oracle.gemv(W, np.ones(128))
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", GOLDEN["rmsnorm"])
+def test_rmsnorm_hand_case(case):
+    got = oracle.rmsnorm(case["x"], np.asarray(case["g"], np.float16), case["eps"])
+    np.testing.assert_allclose(got, case["y"], rtol=1e-15)
+
+
+def test_rmsnorm_closed_forms():
+    g = synth.norm_weight(2, "g", 64)
+    c = 0.37
+    got = oracle.rmsnorm(np.full(64, c), g, 1e-5)
+    np.testing.assert_allclose(got, g.astype(np.float64) * c / np.sqrt(c * c + 1e-5), rtol=1e-14)
+    x = synth.activations(2, "x", 333, np.float32).astype(np.float64)
+    out = oracle.rmsnorm(x, np.ones(333, np.float16), 0.0)
+    assert abs(np.mean(out ** 2) - 1.0) < 1e-13
+    assert np.array_equal(np.sign(out), np.sign(x))
+
+
+def test_silu_library():
+    for z in [-30.0, -3.5, -1.0, -1e-3, 0.0, 1e-3, 0.5, 2.0, 17.0]:
+        assert oracle.silu(z) == pytest.approx(z * scipy.special.expit(z), rel=1e-15, abs=1e-300)
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+
+
+def test_swiglu_closed_forms():
+    K, F = 128, 12
+    x = synth.activations(3, "x", K, np.float32).astype(np.float64)
+    Wg = synth.qmat(3, "g", F, K, 4)
+    Wu = synth.qmat(3, "u", F, K, 4)
+    # zero gate weights: silu(0) = 0 kills every output
+    Z = dict(Wg, scales=np.zeros_like(Wg["scales"]), biases=np.zeros_like(Wg["biases"]))
+    assert np.array_equal(oracle.swiglu(Z, Wu, x), np.zeros(F))
+    # constant gate weight b: a_j = b * sum(x) for every row
+    C = dict(Wg, scales=np.zeros_like(Wg["scales"]), biases=np.full_like(Wg["biases"], 0.25))
+    a = 0.25 * x.sum()
+    c = oracle.gemv(Wu, x)
+    np.testing.assert_allclose(oracle.swiglu(C, Wu, x), a * scipy.special.expit(a) * c, rtol=1e-12)
+    # general: silu of one pinned matvec times another
+    ref = oracle.gemv(Wg, x)
+    np.testing.assert_allclose(oracle.swiglu(Wg, Wu, x), ref * scipy.special.expit(ref) * c,
+                               rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", GOLDEN["topk"])
+def test_topk_hand_cases(case):
+    idx, _ = oracle.topk(case["z"], case["k"])
+    assert list(idx) == case["idx"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    V = int(rng.integers(1, 300))
+    z = rng.integers(-5, 6, size=V).astype(np.float64)  # many ties
+    k = int(rng.integers(1, V + 1))
+    order = np.lexsort((np.arange(V), -z))
+    idx, vals = oracle.topk(z, k)
+    assert np.array_equal(idx, order[:k])
+    assert np.array_equal(vals, z[order[:k]])
+
+
+def test_topk_nan_last():
+    idx, _ = oracle.topk([np.nan, 1.0, -np.inf, np.nan], 4)
+    assert list(idx) == [1, 2, 0, 3]
+
+
+def test_route_equal_and_softmax():
+    ids, w = oracle.route(np.zeros(512), 3)
+    assert list(ids) == [0, 1, 2]
+    np.testing.assert_allclose(w, [1 / 3] * 3, rtol=1e-15)
+    lg = synth.router_logits(1, "r", 512).astype(np.float64)
+    ids, w = oracle.route(lg, 3)
+    assert np.array_equal(ids, np.lexsort((np.arange(512), -lg))[:3])
+    np.testing.assert_allclose(w, scipy.special.softmax(lg[ids]), rtol=1e-14)
+    assert abs(w.sum() - 1) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+def _experts(seed, E, F, H):
+    gate = synth.qmat(seed, "gate", E * F, H, 4)
+    up = synth.qmat(seed, "up", E * F, H, 4)
+    down = synth.qmat(seed, "down", E * H, F, 4)
+    for W in (gate, up, down):
+        W["E"] = E
+    return gate, up, down
+
+
+def test_moe_zero_experts_is_identity():
+    E, F, H = 6, 64, 128
+    gate, up, down = _experts(1, E, F, H)
+    down["scales"][:] = 0
+    down["biases"][:] = 0
+    x = synth.activations(1, "x", H, np.float32).astype(np.float64)
+    lg = synth.router_logits(1, "l", E)
+    y, ids, w = oracle.moe_layer(gate, up, down, None, lg, 3, x, None)
+    assert np.array_equal(y, x)
+
+
+def test_moe_k_concatenation_identity():
+    """sum_e w_e D_e u_e equals one matvec over the K-concatenated experts."""
+    E, F, H = 5, 64, 128
+    gate, up, down = _experts(2, E, F, H)
+    shared = tuple(synth.qmat(2, ("sh", t), *s, 4) for t, s in
+                   (("g", (F, H)), ("u", (F, H)), ("d", (H, F))))
+    x = synth.activations(2, "x", H, np.float32).astype(np.float64)
+    g = synth.norm_weight(2, "g", H)
+    lg = synth.router_logits(2, "l", E)
+    y, ids, w = oracle.moe_layer(gate, up, down, shared, lg, 3, x, g)
+    xn = oracle.rmsnorm(x, g)
+    parts, mats = [], []
+    for e, we in zip(ids, w):
+        u = oracle.swiglu(oracle.expert_slice(gate, e), oracle.expert_slice(up, e), xn)
+        parts.append(we * u)
+        mats.append(oracle.expert_slice(down, e))
+    parts.append(oracle.swiglu(shared[0], shared[1], xn))
+    mats.append(shared[2])
+    cat = {"N": H, "K": F * len(mats), "bits": 4, "fmt": synth.AFFINE, "group": 64,
+           "q": np.hstack([m["q"] for m in mats]),
+           "scales": np.hstack([m["scales"] for m in mats]),
+           "biases": np.hstack([m["biases"] for m in mats]), "lut": None}
+    ref = x + oracle.gemv(cat, np.concatenate(parts))
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_single_expert_closed_form():
+    E, F, H = 4, 64, 128
+    gate, up, down = _experts(3, E, F, H)
+    x = synth.activations(3, "x", H, np.float32).astype(np.float64)
+    lg = np.array([0.1, 2.0, -1.0, 0.3])
+    y, ids, w = oracle.moe_layer(gate, up, down, None, lg, 1, x, None)
+    assert list(ids) == [1] and w[0] == 1.0
+    u = oracle.swiglu(oracle.expert_slice(gate, 1), oracle.expert_slice(up, 1), x)
+    np.testing.assert_allclose(y, x + oracle.gemv(oracle.expert_slice(down, 1), u), rtol=1e-14)
+
+
+def test_decoder_layer_zero_weights_identity():
+    model = dict(name="tiny", layers=1, hidden=128, qkv=192, q_dim=128, o_in=128, ffn=256)
+    w = synth.layer_weights(1, model, 0)
+    for name in ("o", "down"):
+        w[name]["scales"][:] = 0
+        w[name]["biases"][:] = 0
+    x = synth.activations(1, "x", 128, np.float32).astype(np.float64)
+    assert np.array_equal(oracle.decoder_layer(w, x, 128), x)
+
+
+def test_expert_bytes_match_page():
+    """The page's per-expert size pins 4-bit codes + fp16 scale + fp16 bias per 64."""
+    c = GOLDEN["expert_bytes"]
+    H, F = c["hidden"], c["ffn"]
+    mats = [synth.qmat(0, "e", F, H), synth.qmat(0, "e", F, H), synth.qmat(0, "e", H, F)]
+    nbytes = sum(m["q"].nbytes + m["scales"].nbytes + m["biases"].nbytes for m in mats)
+    assert nbytes == c["bytes"]
+    assert nbytes / 2 ** 20 == c["mib"]

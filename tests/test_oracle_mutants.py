@@ -1,0 +1,56 @@
+"""The oracle's pins are sharp: each plausible mistake planted in a copy of
+the oracle's C source (a dropped term, a wrong sign or index, a transposed
+field order) makes the pin suite fail. CPU only; the planted copies live in a
+temporary directory and are loaded through QG_ORACLE_LIB in a subprocess."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "qg_oracle.c")
+
+MUTANTS = [
+    ("msb_first_fields", "unsigned shift = (unsigned)(W->bits * (k % per_word));",
+     "unsigned shift = (unsigned)(W->bits * (per_word - 1 - k % per_word));"),
+    ("wrong_code_mask", "return (word >> shift) & ((1u << W->bits) - 1u);",
+     "return (word >> shift) & 0xFu;"),
+    ("neighbour_group", "size_t gi = (size_t)n * groups_per_row + k / W->group;",
+     "size_t gi = (size_t)n * groups_per_row + (k / W->group + 1) % groups_per_row;"),
+    ("dropped_bias", "(double)c * og_half_to_double(W->scales[gi]) + og_half_to_double(W->biases[gi])",
+     "(double)c * og_half_to_double(W->scales[gi])"),
+    ("bias_sign", "(double)c * og_half_to_double(W->scales[gi]) + og_half_to_double(W->biases[gi])",
+     "(double)c * og_half_to_double(W->scales[gi]) - og_half_to_double(W->biases[gi])"),
+    ("lut_row_zero", "return og_half_to_double(W->lut[(size_t)n * (1u << W->bits) + c]);",
+     "return og_half_to_double(W->lut[c]);"),
+    ("reversed_k", "acc += weight_at(W, n, k) * xm[k];",
+     "acc += weight_at(W, n, W->K - 1 - k) * xm[k];"),
+    ("dropped_residual", "j->y[o] = (j->residual ? j->residual[o] : 0.0) + acc;",
+     "j->y[o] = acc;"),
+    ("half_subnormal_exp", "v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    ("eps_outside_sqrt", "double denom = sqrt(ss / K + eps);", "double denom = sqrt(ss / K) + eps;"),
+    ("sum_not_mean", "double denom = sqrt(ss / K + eps);", "double denom = sqrt(ss + eps);"),
+    ("silu_sign", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    ("topk_tie_high_index", "    if (va != vb)\n        return va > vb;\n    return ia < ib;",
+     "    if (va != vb)\n        return va > vb;\n    return ia > ib;"),
+    ("route_bad_norm", "w[i] = exp(logits[ids[i]] - lmax) / den;",
+     "w[i] = exp(logits[ids[i]] - lmax) / (den + 1.0);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mut_c = tmp_path / f"{name}.c"
+    mut_so = tmp_path / f"{name}.so"
+    mut_c.write_text(src.replace(old, new))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-o", str(mut_so), str(mut_c), "-lm", "-lpthread"], check=True)
+    env = dict(os.environ, QG_ORACLE_LIB=str(mut_so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
