@@ -1,0 +1,380 @@
+// qg_api.hip -- the extern "C" entry points declared in include/qgemv.h:
+// argument validation, variant selection (lanes per row, rows per lane,
+// split-K) from the shape and the device's compute-unit count, and launches.
+// Nothing here allocates, frees or synchronizes.
+#include <atomic>
+#include <mutex>
+#include <string.h>
+
+#include "../../include/qgemv.h"
+#include "qg_internal.h"
+
+namespace qg {
+int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg_qmat* down_all,
+                        int n_experts, int F, int H, int bits, int fmt, const qg_qmat* shared3,
+                        const float* router_logits, int top_k, const uint16_t* norm_w, float eps,
+                        const float* x, float* y, int32_t* sel_ids, float* sel_w, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+size_t moe_workspace_bytes(int F, int H, int top_k);
+int plan_and_launch_topk(const float* logits, int V, int k, int32_t* idx, float* vals, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+size_t topk_workspace_bytes(int V, int k);
+}  // namespace qg
+
+using namespace qg;
+
+namespace {
+
+// ---- tuning knobs (tests and benchmarks; 0 = automatic) --------------------
+std::atomic<int> g_knob[8];
+
+struct DevInfo {
+  int ok;
+  int cus;
+};
+
+DevInfo device_info() {
+  static std::mutex mu;
+  static DevInfo cache[64];
+  static bool have[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return {0, 0};
+  std::lock_guard<std::mutex> lk(mu);
+  if (!have[dev]) {
+    hipDeviceProp_t prop;
+    DevInfo d{0, 0};
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      d.cus = prop.multiProcessorCount;
+    }
+    cache[dev] = d;
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges)
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_common(int N, int K, int M, int group, int bits, int fmt, int x_dtype) {
+  if (N < 0 || K <= 0 || M < 1) return QG_EINVAL;
+  if (x_dtype != QG_F16 && x_dtype != QG_F32) return QG_EINVAL;
+  if (fmt != QG_AFFINE && fmt != QG_LUT) return QG_EINVAL;
+  if (group != 64 || (bits != 4 && bits != 2)) return QG_EUNSUPPORTED;
+  if (fmt == QG_LUT && bits != 4) return QG_EUNSUPPORTED;
+  if (K % 64) return QG_EINVAL;
+  if (K > QG_MAX_K) return QG_EUNSUPPORTED;
+  if (M > QG_MAX_M) return QG_EUNSUPPORTED;
+  if ((size_t)N * (size_t)K * (size_t)bits / 8 >= ((size_t)1 << 31)) return QG_EUNSUPPORTED;
+  return QG_OK;
+}
+
+int check_qmat(const qg_qmat* W, int fmt) {
+  if (!W || !W->q || !aligned(W->q, 16)) return QG_EINVAL;
+  if (fmt == QG_AFFINE) {
+    if (!W->scales || !W->biases || !aligned(W->scales, 2) || !aligned(W->biases, 2))
+      return QG_EINVAL;
+  } else {
+    if (!W->lut || !aligned(W->lut, 2)) return QG_EINVAL;
+  }
+  return QG_OK;
+}
+
+QMat to_dev(const qg_qmat* W) {
+  QMat m{nullptr, nullptr, nullptr, nullptr};
+  if (W) {
+    m.q = W->q;
+    m.s = W->scales;
+    m.b = W->biases;
+    m.lut = W->lut;
+  }
+  return m;
+}
+
+constexpr int kMaxSplits = 16;
+constexpr size_t kLdsBudget = 64 * 1024;
+
+int codes_per_chunk(int bits) { return 128 / bits; }
+int pieces_per_chunk(int bits) { return 128 / bits / 4; }
+
+// Lanes per row: the widest of 64/32/16 that leaves no lane idle in any pass,
+// else the one that idles the fewest.
+int pick_lpr(int C) {
+  const int cands[3] = {64, 32, 16};
+  int best = 64;
+  double best_eff = -1.0;
+  for (int l : cands) {
+    const int passes = (C + l - 1) / l;
+    const double eff = (double)C / (double)(passes * l);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = l;
+    }
+  }
+  return best;
+}
+
+struct MvShape {
+  int N, K, bits, fmt, epi;
+  int col_seg_chunks;  // K-segment length in chunks (0: one matrix along K)
+};
+
+// Chooses lanes per row, rows per lane, split-K and grid for one launch.
+MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
+  MvPlan pl{};
+  const int C = s.K / codes_per_chunk(s.bits);
+  pl.lpr = g_knob[2].load() ? g_knob[2].load() : pick_lpr(C);
+  if (s.col_seg_chunks > 0 && !g_knob[2].load()) {
+    // keep every pass inside one K segment when the segments allow it
+    for (int l : {64, 32, 16})
+      if (s.col_seg_chunks % l == 0) {
+        pl.lpr = l;
+        break;
+      }
+  }
+  pl.rows = g_knob[1].load() ? g_knob[1].load() : 1;
+  const int rpb = (64 / pl.lpr) * pl.rows;
+  const int nbands = (s.N + rpb - 1) / rpb;
+  const int tiles = (nbands + kWaves - 1) / kWaves;
+  const size_t per_chunk = (size_t)pieces_per_chunk(s.bits) * 16 + 4;
+  const size_t lut_bytes = (s.fmt == QG_LUT) ? (size_t)kWaves * rpb * 2 * 16 * 4 : 0;
+  int max_chunks = (int)((kLdsBudget - lut_bytes) / per_chunk);
+  max_chunks = (max_chunks / pl.lpr) * pl.lpr;
+  const int passes = (C + pl.lpr - 1) / pl.lpr;
+  int splits = (C + max_chunks - 1) / max_chunks;
+  if (g_knob[0].load()) {
+    splits = g_knob[0].load();
+  } else {
+    // Small N: more workgroups in flight by splitting K (keep >= 2 passes per slice).
+    const int target = 2 * cus;
+    if (tiles < target && passes >= 4) {
+      int want = (target + tiles - 1) / tiles;
+      if (want > passes / 2) want = passes / 2;
+      if (want > splits) splits = want;
+    }
+  }
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits > passes) splits = passes;
+  if (splits < 1) splits = 1;
+  if (!have_ws) splits = 1;
+  int slice_passes = (passes + splits - 1) / splits;
+  pl.slice_chunks = slice_passes * pl.lpr;
+  pl.splits = (C + pl.slice_chunks - 1) / pl.slice_chunks;
+  const int slice_npass = slice_passes;
+  pl.lds_bytes = (size_t)slice_npass * pl.lpr * per_chunk + lut_bytes;
+  // Resident workgroups per CU: two 8-wave groups keep 16 waves in flight.
+  const int wg_per_cu = g_knob[3].load() ? g_knob[3].load() : 2;
+  int gx = tiles;
+  const int cap = (cus * wg_per_cu + pl.splits - 1) / pl.splits;
+  if (gx > cap) gx = cap;
+  gx = ((gx + 7) / 8) * 8;  // slices of one tile share an XCD (workgroups go round-robin over 8)
+  pl.grid_x = gx;
+  return pl;
+}
+
+size_t mv_ws_bytes(int N, int M, int epi) {
+  const size_t tickets = ((size_t)(N + 7) / 8 + 64) * 4;
+  const size_t tickets_al = (tickets + 255) / 256 * 256;
+  return tickets_al + (size_t)kMaxSplits * (epi == kEpiSwiglu ? 2 : 1) * M * N * 4;
+}
+
+int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, int bits, int fmt,
+           int epi, const void* x, int x_dtype, const uint16_t* norm_w, float eps,
+           const float* residual, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_common(N, K, M, group, bits, fmt, x_dtype);
+  if (rc) return rc;
+  if ((rc = check_qmat(A, fmt))) return rc;
+  if (epi == kEpiSwiglu && (rc = check_qmat(B, fmt))) return rc;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return QG_EINVAL;
+  if (norm_w && !aligned(norm_w, 16)) return QG_EINVAL;
+  if (residual && !aligned(residual, 4)) return QG_EINVAL;
+  const size_t xbytes = (size_t)M * K * (x_dtype == QG_F32 ? 4 : 2);
+  const size_t ybytes = (size_t)M * N * 4;
+  if (overlaps(x, xbytes, y, ybytes)) return QG_EINVAL;
+  if (residual && residual != y && overlaps(residual, ybytes, y, ybytes)) return QG_EINVAL;
+  if (M != 1) return QG_EUNSUPPORTED;
+  if (N == 0) return QG_OK;
+  const DevInfo dev = device_info();
+  if (!dev.ok) return QG_EDEVICE;
+  const bool have_ws = ws && ws_bytes >= mv_ws_bytes(N, M, epi) && aligned(ws, 256);
+  const MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0}, dev.cus, have_ws);
+  if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;  // K too long for one slice: needs ws
+  MvParams p;
+  memset(&p, 0, sizeof(p));
+  p.A[0] = to_dev(A);
+  p.B[0] = to_dev(B);
+  p.nseg = 1;
+  p.seg_mode = kSegNone;
+  p.seg_len = 0;
+  p.N = N;
+  p.K = K;
+  p.wpr = K * bits / 32;
+  p.gpr = K / 64;
+  p.x = x;
+  p.x_f32 = x_dtype == QG_F32;
+  p.norm_w = norm_w;
+  p.eps = eps;
+  p.residual = residual;
+  p.y = y;
+  p.splits = pl.splits;
+  p.slice_chunks = pl.slice_chunks;
+  p.grid_x = pl.grid_x;
+  if (pl.splits > 1) {
+    const size_t tickets = ((size_t)(N + 7) / 8 + 64) * 4;
+    const size_t tickets_al = (tickets + 255) / 256 * 256;
+    p.tickets = static_cast<uint32_t*>(ws);
+    p.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + tickets_al);
+  }
+  const hipError_t e = launch_mv(bits, fmt, epi, pl, p, stream);
+  return e == hipSuccess ? QG_OK : QG_ELAUNCH;
+}
+
+}  // namespace
+
+namespace qg {
+// Shared with the MoE launcher.
+int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have_ws, void* ws,
+                       size_t ws_bytes, size_t ws_offset, hipStream_t stream) {
+  const DevInfo dev = device_info();
+  if (!dev.ok) return QG_EDEVICE;
+  MvParams p = p0;
+  const MvPlan pl = plan_mv({p.N, p.K, bits, fmt, epi, p.seg_mode == kSegCols ? p.seg_len : 0}, dev.cus, have_ws);
+  if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;
+  p.splits = pl.splits;
+  p.slice_chunks = pl.slice_chunks;
+  p.grid_x = pl.grid_x;
+  if (pl.splits > 1) {
+    const size_t tickets = ((size_t)(p.N + 7) / 8 + 64) * 4;
+    const size_t tickets_al = (tickets + 255) / 256 * 256;
+    if (ws_offset + mv_ws_bytes(p.N, 1, epi) > ws_bytes) return QG_EWORKSPACE;
+    char* base = static_cast<char*>(ws) + ws_offset;
+    p.tickets = reinterpret_cast<uint32_t*>(base);
+    p.partials = reinterpret_cast<float*>(base + tickets_al);
+  }
+  const hipError_t e = launch_mv(bits, fmt, epi, pl, p, stream);
+  return e == hipSuccess ? QG_OK : QG_ELAUNCH;
+}
+size_t mv_workspace_bytes(int N, int epi) { return mv_ws_bytes(N, 1, epi); }
+int device_ok() { return device_info().ok; }
+}  // namespace qg
+
+extern "C" {
+
+const char* qg_status_str(int status) {
+  switch (status) {
+    case QG_OK: return "QG_OK";
+    case QG_EINVAL: return "QG_EINVAL: invalid argument (NULL pointer, size, alignment or aliasing)";
+    case QG_EUNSUPPORTED: return "QG_EUNSUPPORTED: valid but not provided (group, bits, format, M, K or k)";
+    case QG_EWORKSPACE: return "QG_EWORKSPACE: workspace missing or too small";
+    case QG_ELAUNCH: return "QG_ELAUNCH: the HIP runtime reported an error while enqueueing";
+    case QG_EDEVICE: return "QG_EDEVICE: the current HIP device is not a usable gfx950";
+    default: return "unknown qgemv status";
+  }
+}
+
+int qg_workspace_bytes(int op, int N, int K, int M, int bits, int fmt, int k, size_t* bytes) {
+  if (!bytes) return QG_EINVAL;
+  if (N < 0 || K < 0 || M < 1) return QG_EINVAL;
+  (void)bits;
+  (void)fmt;
+  switch (op) {
+    case QG_OP_GEMV:
+    case QG_OP_GEMV_RMSNORM: *bytes = mv_ws_bytes(N, M, kEpiStore); return QG_OK;
+    case QG_OP_SWIGLU: *bytes = mv_ws_bytes(N, M, kEpiSwiglu); return QG_OK;
+    case QG_OP_MOE:
+      if (k < 1 || k > kMaxRoutes) return QG_EUNSUPPORTED;
+      *bytes = moe_workspace_bytes(K, N, k);
+      return QG_OK;
+    case QG_OP_LOGITS_TOPK:
+      if (k < 1 || k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
+      *bytes = topk_workspace_bytes(N, k) + mv_ws_bytes(N, 1, kEpiStore);
+      return QG_OK;
+    default: return QG_EINVAL;
+  }
+}
+
+int qg_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || ws_bytes % 4 || !aligned(ws, 4)) return QG_EINVAL;
+  const hipError_t e = launch_fill_u32(static_cast<uint32_t*>(ws), ws_bytes / 4, 0u, stream);
+  return e == hipSuccess ? QG_OK : QG_ELAUNCH;
+}
+
+// Tuning override for tests and benchmarks: knob 0 = split count, 1 = rows per
+// lane, 2 = lanes per row, 3 = workgroups per CU; value 0 restores automatic.
+int qg_tune(int knob, int value) {
+  if (knob < 0 || knob > 3 || value < 0) return QG_EINVAL;
+  if (knob == 1 && value != 0 && value != 1 && value != 2) return QG_EINVAL;
+  if (knob == 2 && value != 0 && value != 16 && value != 32 && value != 64) return QG_EINVAL;
+  if (knob == 0 && value > kMaxSplits) return QG_EINVAL;
+  g_knob[knob].store(value);
+  return QG_OK;
+}
+
+int qgemv(const qg_qmat* W, int N, int K, int M, int group, int bits, int fmt, const void* x,
+          int x_dtype, const float* residual, float* y, void* ws, size_t ws_bytes,
+          hipStream_t stream) {
+  return run_mv(W, nullptr, N, K, M, group, bits, fmt, kEpiStore, x, x_dtype, nullptr, 0.f,
+                residual, y, ws, ws_bytes, stream);
+}
+
+int qgemv_rmsnorm(const qg_qmat* W, int N, int K, int M, int group, int bits, int fmt,
+                  const void* x, int x_dtype, const uint16_t* norm_w, float eps,
+                  const float* residual, float* y, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  if (!norm_w || !(eps >= 0.f)) return QG_EINVAL;
+  return run_mv(W, nullptr, N, K, M, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps,
+                residual, y, ws, ws_bytes, stream);
+}
+
+int qswiglu(const qg_qmat* Wgate, const qg_qmat* Wup, int F, int K, int M, int group, int bits,
+            int fmt, const void* x, int x_dtype, const uint16_t* norm_w, float eps, float* u,
+            void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (norm_w && !(eps >= 0.f)) return QG_EINVAL;
+  return run_mv(Wgate, Wup, F, K, M, group, bits, fmt, kEpiSwiglu, x, x_dtype, norm_w, eps,
+                nullptr, u, ws, ws_bytes, stream);
+}
+
+int qmoe_experts(const qg_qmat* gate_all, const qg_qmat* up_all, const qg_qmat* down_all,
+                 int n_experts, int F, int H, int group, int bits, int fmt,
+                 const qg_qmat* shared3, const float* router_logits, int top_k,
+                 const uint16_t* norm_w, float eps, const float* x, float* y, int32_t* sel_ids,
+                 float* sel_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_common(F, H, 1, group, bits, fmt, QG_F32);
+  if (rc) return rc;
+  if ((rc = check_common(H, F, 1, group, bits, fmt, QG_F32))) return rc;
+  if (n_experts < 1 || F < 1 || H < 1) return QG_EINVAL;
+  if (top_k < 1 || top_k > kMaxRoutes || top_k > n_experts) return QG_EUNSUPPORTED;
+  if (fmt != QG_AFFINE) return QG_EUNSUPPORTED;  // expert layers take the affine format
+  return plan_and_launch_moe(gate_all, up_all, down_all, n_experts, F, H, bits, fmt, shared3,
+                             router_logits, top_k, norm_w, eps, x, y, sel_ids, sel_w, ws,
+                             ws_bytes, stream);
+}
+
+int qlogits_topk(const qg_qmat* W, int V, int K, int group, int bits, int fmt, const void* x,
+                 int x_dtype, const uint16_t* norm_w, float eps, float* logits, int k,
+                 int32_t* idx, float* vals, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_common(V, K, 1, group, bits, fmt, x_dtype);
+  if (rc) return rc;
+  if (V < 1) return QG_EINVAL;
+  if (k < 1 || k > V) return QG_EINVAL;
+  if (k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
+  if (!logits || !idx || !vals || !aligned(logits, 4) || !aligned(idx, 4) || !aligned(vals, 4))
+    return QG_EINVAL;
+  if (norm_w && !(eps >= 0.f)) return QG_EINVAL;
+  const size_t tk = topk_workspace_bytes(V, k);
+  const size_t need = tk + mv_ws_bytes(V, 1, kEpiStore);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return QG_EWORKSPACE;
+  char* mvws = static_cast<char*>(ws) + tk;
+  rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps, nullptr,
+              logits, mvws, ws_bytes - tk, stream);
+  if (rc) return rc;
+  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// qg_internal.h -- types shared by the kernels and the C-ABI layer of the
+// gfx950 quantized matvec library. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kThreads = 512;          // threads per workgroup (8 wave64s)
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxSeg = 8;             // matrices one launch can gather
+constexpr int kMaxRoutes = 8;          // routed experts per token
+
+// Device pointers of one planar quantized matrix.
+struct QMat {
+  const uint32_t* q;
+  const uint16_t* s;
+  const uint16_t* b;
+  const uint16_t* lut;
+};
+
+enum Epi : int {
+  kEpiStore = 0,   // y = acc (+ residual)
+  kEpiSwiglu = 1,  // y = silu(acc_A) * acc_B
+};
+
+// Where the rows / columns of the logical matrix come from.
+//  kSegNone: one matrix, A[0] (and B[0] for SwiGLU).
+//  kSegRows: logical row r belongs to matrix A[r / seg_len] (local row r % seg_len).
+//  kSegCols: logical chunk c belongs to matrix A[c / seg_len] (local chunk c % seg_len),
+//            all matrices having the same N; x is the concatenation of the segments' inputs.
+enum SegMode : int { kSegNone = 0, kSegRows = 1, kSegCols = 2 };
+
+// Routing input: when `ids` is set, segments [0, n_routed) are expert ids[i]
+// of a stacked tensor whose expert e starts at row e * expert_rows of
+// `all_A`/`all_B`; segment n_routed (if any) is the fixed A[n_routed].
+struct Routing {
+  const int32_t* ids;     // device [n_routed] or nullptr
+  const float* weights;   // device [n_routed] (K-segment input scaling) or nullptr
+  int n_routed;
+  int expert_rows;
+  QMat all_A, all_B;
+};
+
+struct MvParams {
+  QMat A[kMaxSeg];
+  QMat B[kMaxSeg];
+  int nseg;
+  int seg_mode;
+  int seg_len;        // rows (kSegRows) or chunks (kSegCols) per segment
+  int N;              // logical rows
+  int K;              // logical columns (sum over K segments)
+  int wpr;            // uint32 words per row of each underlying matrix
+  int gpr;            // groups of 64 per row of each underlying matrix
+  const void* x;      // [K] activations (fp16 or fp32)
+  int x_f32;
+  const uint16_t* norm_w;  // [K] fp16 or nullptr
+  float eps;
+  const float* residual;   // [N] or nullptr
+  float* y;                // [N]
+  Routing route;
+  // split-K
+  int splits;         // number of K slices (1 = none)
+  int slice_chunks;   // chunks per slice (multiple of the lanes per row)
+  int grid_x;         // workgroups per slice (multiple of 8: slice s of tile t lands on XCD t%8)
+  float* partials;    // [splits][n_acc][N] when splits > 1
+  uint32_t* tickets;  // [grid_x] zero-initialized when splits > 1
+};
+
+// Launch configuration chosen on the host.
+struct MvPlan {
+  int lpr;            // lanes per row: 64, 32 or 16
+  int rows;           // rows per lane slot (R)
+  int splits;
+  int slice_chunks;
+  int grid_x;
+  size_t lds_bytes;
+};
+
+hipError_t launch_mv(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
+                     hipStream_t stream);
+
+// Fill kernel (graph-safe replacement for hipMemsetAsync).
+hipError_t launch_fill_u32(uint32_t* dst, size_t n, uint32_t value, hipStream_t stream);
+
+}  // namespace qg

@@ -1,0 +1,151 @@
+// qg_moe.hip -- one MoE expert layer per token, entirely on the device
+// (GeekNews item on the 397B MoE engine: "Architecture du modele" -- 512
+// experts, 4 active per token of which one is shared; "Deferred GPU Expert
+// Compute" -- the combine, norm and residual run on the GPU and go straight to
+// the next layer, with no host round trip).
+//
+// Three launches on one stream:
+//  1. route: top_k of the router logits and softmax over the chosen ones,
+//     written to the workspace (and to sel_ids / sel_w when given);
+//  2. gate.up SwiGLU over the chosen experts plus the shared one, as one
+//     matvec over (top_k+1)*F gathered rows; each workgroup reads the chosen
+//     ids and points its row segments at those experts;
+//  3. down + combine + residual, as one matvec over the K-concatenation
+//     [Down_e0 | Down_e1 | ... | Down_shared] against [w0*u0, w1*u1, ..., u_sh]:
+//     sum_e w_e (Down_e u_e) is that single row-by-row dot product, so the
+//     weighted combine costs no extra pass.
+#include <string.h>
+
+#include "../../include/qgemv.h"
+#include "qg_internal.h"
+
+namespace qg {
+
+hipError_t launch_route(const float* logits, int E, int top_k, int32_t* ids_ws, float* w_ws,
+                        int32_t* ids_out, float* w_out, hipStream_t stream);
+int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have_ws, void* ws,
+                       size_t ws_bytes, size_t ws_offset, hipStream_t stream);
+size_t mv_workspace_bytes(int N, int epi);
+int device_ok();
+
+namespace {
+constexpr size_t kRouteBytes = 256;
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_mat(const qg_qmat* W, int fmt) {
+  if (!W || !W->q || !aligned(W->q, 16)) return QG_EINVAL;
+  if (fmt == QG_AFFINE) {
+    if (!W->scales || !W->biases || !aligned(W->scales, 2) || !aligned(W->biases, 2))
+      return QG_EINVAL;
+  } else if (!W->lut || !aligned(W->lut, 2)) {
+    return QG_EINVAL;
+  }
+  return QG_OK;
+}
+
+QMat dev(const qg_qmat* W) { return QMat{W->q, W->scales, W->biases, W->lut}; }
+}  // namespace
+
+size_t moe_workspace_bytes(int F, int H, int top_k) {
+  const int nseg = top_k + 1;
+  const size_t u = align256((size_t)nseg * F * 4);
+  const size_t gu = mv_workspace_bytes(nseg * F, kEpiSwiglu);
+  const size_t dn = mv_workspace_bytes(H, kEpiStore);
+  return kRouteBytes + u + (gu > dn ? gu : dn);
+}
+
+int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg_qmat* down_all,
+                        int n_experts, int F, int H, int bits, int fmt, const qg_qmat* shared3,
+                        const float* router_logits, int top_k, const uint16_t* norm_w, float eps,
+                        const float* x, float* y, int32_t* sel_ids, float* sel_w, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  if ((rc = check_mat(gate_all, fmt)) || (rc = check_mat(up_all, fmt)) ||
+      (rc = check_mat(down_all, fmt)))
+    return rc;
+  if (shared3) {
+    for (int i = 0; i < 3; ++i)
+      if ((rc = check_mat(&shared3[i], fmt))) return rc;
+  }
+  if (!router_logits || !x || !y || !aligned(router_logits, 4) || !aligned(x, 16) ||
+      !aligned(y, 4))
+    return QG_EINVAL;
+  if (norm_w && (!aligned(norm_w, 16) || !(eps >= 0.f))) return QG_EINVAL;
+  if ((sel_ids && !aligned(sel_ids, 4)) || (sel_w && !aligned(sel_w, 4))) return QG_EINVAL;
+  if (x != y) {
+    const uintptr_t a = (uintptr_t)x, b = (uintptr_t)y, n = (uintptr_t)H * 4;
+    if (a < b + n && b < a + n) return QG_EINVAL;
+  }
+  if (!ws || !aligned(ws, 256) || ws_bytes < moe_workspace_bytes(F, H, top_k))
+    return QG_EWORKSPACE;
+  if (!device_ok()) return QG_EDEVICE;
+
+  const int nseg = top_k + (shared3 ? 1 : 0);
+  char* base = static_cast<char*>(ws);
+  int32_t* ids_ws = reinterpret_cast<int32_t*>(base);
+  float* w_ws = reinterpret_cast<float*>(base + 64);
+  float* u = reinterpret_cast<float*>(base + kRouteBytes);
+  const size_t mv_off = kRouteBytes + align256((size_t)(top_k + 1) * F * 4);
+
+  // 1. routing
+  if (launch_route(router_logits, n_experts, top_k, ids_ws, w_ws, sel_ids, sel_w, stream) !=
+      hipSuccess)
+    return QG_ELAUNCH;
+
+  // 2. gate.up SwiGLU over the chosen experts' rows (+ shared)
+  MvParams p;
+  memset(&p, 0, sizeof(p));
+  p.nseg = nseg;
+  p.seg_mode = kSegRows;
+  p.seg_len = F;
+  if (shared3) {
+    p.A[top_k] = dev(&shared3[0]);
+    p.B[top_k] = dev(&shared3[1]);
+  }
+  p.route.ids = ids_ws;
+  p.route.weights = nullptr;
+  p.route.n_routed = top_k;
+  p.route.expert_rows = F;
+  p.route.all_A = dev(gate_all);
+  p.route.all_B = dev(up_all);
+  p.N = nseg * F;
+  p.K = H;
+  p.wpr = H * bits / 32;
+  p.gpr = H / 64;
+  p.x = x;
+  p.x_f32 = 1;
+  p.norm_w = norm_w;
+  p.eps = eps;
+  p.residual = nullptr;
+  p.y = u;
+  rc = mv_launch_internal(bits, fmt, kEpiSwiglu, p, true, ws, ws_bytes, mv_off, stream);
+  if (rc) return rc;
+
+  // 3. down over the K-concatenated experts, weighted, + residual
+  MvParams d;
+  memset(&d, 0, sizeof(d));
+  d.nseg = nseg;
+  d.seg_mode = kSegCols;
+  d.seg_len = F / (128 / bits);  // chunks per expert segment
+  if (shared3) d.A[top_k] = dev(&shared3[2]);
+  d.route.ids = ids_ws;
+  d.route.weights = w_ws;
+  d.route.n_routed = top_k;
+  d.route.expert_rows = H;
+  d.route.all_A = dev(down_all);
+  d.route.all_B = QMat{nullptr, nullptr, nullptr, nullptr};
+  d.N = H;
+  d.K = nseg * F;
+  d.wpr = F * bits / 32;
+  d.gpr = F / 64;
+  d.x = u;
+  d.x_f32 = 1;
+  d.norm_w = nullptr;
+  d.residual = x;
+  d.y = y;
+  return mv_launch_internal(bits, fmt, kEpiStore, d, true, ws, ws_bytes, mv_off, stream);
+}
+
+}  // namespace qg

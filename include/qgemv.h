@@ -1,0 +1,198 @@
+/*
+ * qgemv.h -- C ABI of the MI355X (gfx950) quantized decode matrix-vector
+ * library: batch-1 (and small-M) matvecs over planar 4-bit / 2-bit
+ * group-quantized weights, dequantized inside the inner loop, with the decode
+ * fusions around them.
+ *
+ * Sources (page title, then the section that defines each operation):
+ *  [F] "Booster la vitesse d'inference sur Apple Silicon -- avec le format
+ *      .forge" (web research report, August 2026):
+ *        TL;DR -- decode is bandwidth bound: time per token is about the
+ *                 bytes read divided by the memory bandwidth;
+ *        section 1 "Le chemin de decodage rapide" -- the matvec that
+ *                 dequantizes inside its inner loop; the fusions rmsnorm +
+ *                 QKV matvec, residual + norm, gate.up SwiGLU in one kernel,
+ *                 logits matvec + top-k on the GPU returning only the chosen
+ *                 entries; a decode loop that allocates nothing;
+ *        section 3 item 4 -- planar quantization: 4-bit codes packed in
+ *                 uint32 with separate scale and bias tensors (group 64);
+ *                 a palettized type with 4-bit indices into a 16-entry fp16
+ *                 table.
+ *  [G] GeekNews item on a C/Metal engine running a 397B MoE on a 48 GB
+ *      MacBook Pro (fr.news.hada.io topic 27758):
+ *        "Architecture du modele" -- 512 experts per layer, 4 active per
+ *                 token including one shared expert, hidden size 4096;
+ *        "Noyau de dequantification optimise FMA" -- the weight is
+ *                 nibble*scale + bias, and the product with x is rewritten
+ *                 as fma(nibble, scale*x, bias*x);
+ *        "Shaders de calcul Metal" / "Deferred GPU Expert Compute" -- 4-bit
+ *                 and 2-bit dequant matvecs, SwiGLU, RMS norm, and the MoE
+ *                 combine + residual on the GPU, handed straight to the next
+ *                 layer.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except the qg_qmat descriptor itself is a DEVICE
+ *    pointer owned by the caller. The descriptor (qg_qmat) is a HOST struct
+ *    read during the call only. Buffers must stay alive until the work queued
+ *    on `stream` has finished.
+ *  - Calls are asynchronous: they validate, enqueue kernels on `stream`
+ *    (NULL = the device's default stream) and return. They never allocate,
+ *    free or synchronize, and print nothing.
+ *  - Return value: QG_OK (0) or a negative status. Validation happens before
+ *    anything is enqueued; a call that fails validation enqueues nothing.
+ *    QG_ELAUNCH reports an error from the HIP runtime after enqueueing.
+ *  - Weight layout (planar, [F] section 3 item 4): row n of an N x K matrix
+ *    is contiguous along K. Codes: q[n][K*bits/32] uint32; element k sits in
+ *    word k/(32/bits) at bit offset bits*(k mod 32/bits), least significant
+ *    field first. Affine format: scales[n][K/64], biases[n][K/64] fp16, and
+ *    W[n][k] = code*scale + bias for the group of 64 consecutive k that holds
+ *    k. LUT format (bits = 4 only): lut[n][16] fp16 and W[n][k] = lut[n][code].
+ *  - fp16 arrays are passed as uint16_t bit patterns (IEEE 754 binary16).
+ *  - Activations x are [M][K] row-major (fp16 or fp32); outputs are fp32.
+ *  - Accumulation is fp32. Results are deterministic: the same call on the
+ *    same inputs gives bitwise the same outputs (no floating-point atomics).
+ *  - Alignment: q and x must be 16-byte aligned; fp16 arrays 2-byte aligned;
+ *    fp32 arrays 4-byte aligned. Otherwise QG_EINVAL.
+ *  - Workspace: calls that need scratch device memory take (ws, ws_bytes);
+ *    qg_workspace_bytes() sizes it. The caller allocates it once, clears it
+ *    once with qg_workspace_init(), and may then reuse it for every call on
+ *    one stream (each call leaves it ready for the next). Two calls that run
+ *    at the same time must not share a workspace.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define QG_OK 0
+#define QG_EINVAL (-1)        /* NULL required pointer, bad size, misalignment, bad aliasing */
+#define QG_EUNSUPPORTED (-2)  /* valid but not provided: group != 64, bits not 2/4, LUT with
+                                 bits != 4, M outside [1,8], K or k beyond the limits below */
+#define QG_EWORKSPACE (-3)    /* ws NULL or smaller than qg_workspace_bytes() */
+#define QG_ELAUNCH (-4)       /* the HIP runtime reported an error while enqueueing */
+#define QG_EDEVICE (-5)       /* no usable gfx950 device for the current HIP device */
+
+/* ---- enums ------------------------------------------------------------- */
+#define QG_AFFINE 0 /* W = code*scale + bias per group of 64 */
+#define QG_LUT 1    /* W = lut[row][code], 16 fp16 entries per row, bits = 4 */
+
+#define QG_F16 0 /* activation dtype: IEEE binary16 */
+#define QG_F32 1 /* activation dtype: IEEE binary32 */
+
+#define QG_OP_GEMV 0
+#define QG_OP_GEMV_RMSNORM 1
+#define QG_OP_SWIGLU 2
+#define QG_OP_MOE 3
+#define QG_OP_LOGITS_TOPK 4
+
+/* Limits. K counts columns of one matrix (for qmoe_experts: the hidden size
+ * and the expert FFN size); k counts top-k entries. */
+#define QG_MAX_K 65536
+#define QG_MAX_M 8
+#define QG_MAX_TOPK 1024
+/* One matrix (or one expert's rows) may hold at most 2^31 - 1 bytes of codes. */
+
+/* A planar quantized matrix ([F] section 3 item 4). Host struct holding
+ * device pointers; see the layout above. Unused members must be NULL. */
+typedef struct qg_qmat {
+    const uint32_t *q;      /* [N][K*bits/32] code words, 16-byte aligned */
+    const uint16_t *scales; /* [N][K/64] fp16 (QG_AFFINE) */
+    const uint16_t *biases; /* [N][K/64] fp16 (QG_AFFINE) */
+    const uint16_t *lut;    /* [N][16] fp16 (QG_LUT) */
+} qg_qmat;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qg_status_str(int status);
+
+/* Bytes of workspace that `op` needs for these sizes (0 if none). For
+ * QG_OP_MOE, N is the hidden size, K the expert FFN size and k the number of
+ * routed experts; for QG_OP_LOGITS_TOPK, N is the vocabulary size and k the
+ * number of entries returned. Returns a status; *bytes is set on QG_OK. */
+int qg_workspace_bytes(int op, int N, int K, int M, int bits, int fmt, int k, size_t *bytes);
+
+/* Clears a workspace before its first use (a fill kernel on `stream`, safe to
+ * record in a HIP graph). ws_bytes must be a multiple of 4. */
+int qg_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Variant override for tests and benchmarks; normal callers never need it.
+ * knob 0 = number of K slices (split-K, needs a workspace), 1 = rows per lane
+ * (1 or 2), 2 = lanes per row (16, 32 or 64), 3 = resident workgroups per
+ * compute unit; value 0 restores the automatic choice. Process-wide; affects
+ * calls made after it returns. QG_EINVAL for an unknown knob or value. */
+int qg_tune(int knob, int value);
+
+/* qgemv -- y[m][n] = residual[m][n] + sum_k W[n][k] * x[m][k]
+ * The decode matvec that dequantizes inside its inner loop ([F] section 1;
+ * the weight form and the fma(code, scale*x, bias*x) rewrite: [G] FMA
+ * section). residual may be NULL; it may be the same pointer as y (in-place
+ * residual add) but must not overlap it otherwise. x must not overlap y.
+ *   W      quantized N x K matrix (fmt, bits as above; group must be 64)
+ *   x      [M][K] activations of dtype x_dtype
+ *   y      [M][N] fp32 output
+ *   M      number of activation vectors, 1..8 */
+int qgemv(const qg_qmat *W, int N, int K, int M, int group, int bits, int fmt,
+          const void *x, int x_dtype, const float *residual, float *y,
+          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* qgemv_rmsnorm -- y = residual + W . rmsnorm(x), with
+ *   rmsnorm(x)_k = x_k * norm_w[k] / sqrt((1/K) sum_j x_j^2 + eps)
+ * per activation vector ([F] section 1: rmsnorm fused into the QKV matvec).
+ * norm_w: [K] fp16. Other arguments as qgemv. */
+int qgemv_rmsnorm(const qg_qmat *W, int N, int K, int M, int group, int bits, int fmt,
+                  const void *x, int x_dtype, const uint16_t *norm_w, float eps,
+                  const float *residual, float *y, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/* qswiglu -- u[m][j] = silu((Wgate x')_j) * (Wup x')_j, silu(z) = z/(1+e^-z),
+ * where x' = rmsnorm(x) when norm_w is non-NULL and x otherwise ([F]
+ * section 1: gate.up SwiGLU in one kernel, residual + norm). Wgate and Wup
+ * are both F x K with the same bits/fmt. u: [M][F] fp32, must not overlap x. */
+int qswiglu(const qg_qmat *Wgate, const qg_qmat *Wup, int F, int K, int M, int group,
+            int bits, int fmt, const void *x, int x_dtype, const uint16_t *norm_w, float eps,
+            float *u, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* qmoe_experts -- one MoE expert layer for one token ([G] "Architecture du
+ * modele", "Deferred GPU Expert Compute"):
+ *   ids   = the top_k router logits (larger first, equal values by lower
+ *           index); w_i = softmax over the chosen logits only;
+ *   x'    = rmsnorm(x; norm_w) (x itself when norm_w is NULL);
+ *   y     = x + sum_i w_i * Down_{ids_i}(SwiGLU_{ids_i}(x'))
+ *             + Down_sh(SwiGLU_sh(x'))            (shared expert, weight 1)
+ * Expert e's gate/up are rows [e*F, (e+1)*F) of gate_all/up_all (each
+ * (n_experts*F) x H), its down is rows [e*H, (e+1)*H) of down_all
+ * ((n_experts*H) x F). shared3 = {gate, up, down} of the always-on expert
+ * (F x H, F x H, H x F) or NULL for none. Routing, expert selection and the
+ * combine all stay on the device. x, y: [H] fp32, y may equal x.
+ * router_logits: [n_experts] fp32. sel_ids/sel_w (device, [top_k], int32 /
+ * fp32) receive the routing decision when non-NULL. 1 <= top_k <= 8. */
+int qmoe_experts(const qg_qmat *gate_all, const qg_qmat *up_all, const qg_qmat *down_all,
+                 int n_experts, int F, int H, int group, int bits, int fmt,
+                 const qg_qmat *shared3, const float *router_logits, int top_k,
+                 const uint16_t *norm_w, float eps, const float *x, float *y,
+                 int32_t *sel_ids, float *sel_w, void *ws, size_t ws_bytes,
+                 hipStream_t stream);
+
+/* qlogits_topk -- z = W . x' (x' = rmsnorm(x; norm_w), or x when norm_w is
+ * NULL), written to logits[V]; then the k largest entries of z, larger first
+ * and equal values by lower index, into idx[k] (int32) and vals[k] (fp32)
+ * ([F] section 1: logits matvec + top-k on the GPU, only the chosen entries
+ * need to come back). M must be 1 (x is [K]). 1 <= k <= min(V, QG_MAX_TOPK). */
+int qlogits_topk(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
+                 const void *x, int x_dtype, const uint16_t *norm_w, float eps,
+                 float *logits, int k, int32_t *idx, float *vals,
+                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

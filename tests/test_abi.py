@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry
+point that include/qgemv.h declares, and rejects invalid arguments with the
+documented status before touching the GPU. No kernel runs here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dequant_gemv_qgemv_amd as qg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qg.LIB_PATH):
+        from dequant_gemv_qgemv_amd import build
+        build.build()
+    return qg.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qg\w+|qgemv\w*|qswiglu|qmoe_experts|qlogits_topk)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("qgemv", "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk",
+              "qg_workspace_bytes", "qg_workspace_init", "qg_status_str", "qg_tune"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) <= set(qg.EXPORTED)
+
+
+def test_status_strings(L):
+    for s in (qg.QG_OK, qg.QG_EINVAL, qg.QG_EUNSUPPORTED, qg.QG_EWORKSPACE, qg.QG_ELAUNCH,
+              qg.QG_EDEVICE, 12345):
+        assert isinstance(qg.qg_status_str(s), str) and qg.qg_status_str(s)
+
+
+def _mat(q=0x1000, s=0x2000, b=0x3000, lut=None):
+    return qg.qg_qmat(q, s, b, lut)
+
+
+X = ctypes.c_void_p(0x10000)
+Y = ctypes.c_void_p(0x80000000)
+
+
+def call_gemv(L, W=None, N=64, K=128, M=1, group=64, bits=4, fmt=0, x=X, xdt=1, res=None, y=Y):
+    W = _mat() if W is None else W
+    return L.qgemv(ctypes.byref(W) if W is not False else None, N, K, M, group, bits, fmt, x, xdt,
+                   res, y, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=False), qg.QG_EINVAL),                 # NULL descriptor
+    (dict(W=_mat(q=0)), qg.QG_EINVAL),            # NULL codes
+    (dict(W=_mat(q=0x1008)), qg.QG_EINVAL),       # codes not 16-byte aligned
+    (dict(W=_mat(s=0)), qg.QG_EINVAL),            # affine without scales
+    (dict(K=100), qg.QG_EINVAL),                  # K not a multiple of 64
+    (dict(K=0), qg.QG_EINVAL),
+    (dict(N=-1), qg.QG_EINVAL),
+    (dict(M=0), qg.QG_EINVAL),
+    (dict(group=32), qg.QG_EUNSUPPORTED),
+    (dict(bits=3), qg.QG_EUNSUPPORTED),
+    (dict(bits=8), qg.QG_EUNSUPPORTED),
+    (dict(fmt=1, W=_mat(s=0, b=0, lut=0x4000), bits=2), qg.QG_EUNSUPPORTED),  # LUT needs 4 bits
+    (dict(fmt=1, W=_mat()), qg.QG_EINVAL),        # LUT without a table
+    (dict(fmt=7), qg.QG_EINVAL),
+    (dict(M=9), qg.QG_EUNSUPPORTED),
+    (dict(K=65536 + 64), qg.QG_EUNSUPPORTED),
+    (dict(xdt=5), qg.QG_EINVAL),
+    (dict(x=None), qg.QG_EINVAL),
+    (dict(y=None), qg.QG_EINVAL),
+    (dict(x=ctypes.c_void_p(0x10004)), qg.QG_EINVAL),           # x not 16-byte aligned
+    (dict(y=ctypes.c_void_p(0x10000 + 64)), qg.QG_EINVAL),      # y overlaps x
+    (dict(res=ctypes.c_void_p(0x80000000 + 4)), qg.QG_EINVAL),  # residual partly overlaps y
+    (dict(N=1 << 20, K=8192), qg.QG_EUNSUPPORTED),              # matrix over 2^31 bytes
+])
+def test_qgemv_rejects_before_launch(L, kw, status):
+    assert call_gemv(L, **kw) == status
+
+
+def test_other_entry_points_reject(L):
+    W = _mat()
+    # rmsnorm without norm weights
+    assert L.qgemv_rmsnorm(ctypes.byref(W), 64, 128, 1, 64, 4, 0, X, 1, None, 1e-5, None, Y,
+                           None, 0, None) == qg.QG_EINVAL
+    # negative eps
+    assert L.qgemv_rmsnorm(ctypes.byref(W), 64, 128, 1, 64, 4, 0, X, 1, ctypes.c_void_p(0x20000),
+                           -1.0, None, Y, None, 0, None) == qg.QG_EINVAL
+    # swiglu without the up matrix
+    assert L.qswiglu(ctypes.byref(W), None, 64, 128, 1, 64, 4, 0, X, 1, None, 0.0, Y, None, 0,
+                     None) == qg.QG_EINVAL
+    # top-k: k out of range, then missing workspace
+    logits, idx, vals = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000))
+    assert L.qlogits_topk(ctypes.byref(W), 64, 128, 64, 4, 0, X, 1, None, 0.0, logits, 0, idx,
+                          vals, None, 0, None) == qg.QG_EINVAL
+    assert L.qlogits_topk(ctypes.byref(W), 64, 128, 64, 4, 0, X, 1, None, 0.0, logits, 65, idx,
+                          vals, None, 0, None) == qg.QG_EINVAL
+    assert L.qlogits_topk(ctypes.byref(W), 2048, 128, 64, 4, 0, X, 1, None, 0.0, logits, 1025,
+                          idx, vals, None, 0, None) == qg.QG_EUNSUPPORTED
+    assert L.qlogits_topk(ctypes.byref(W), 64, 128, 64, 4, 0, X, 1, None, 0.0, logits, 8, idx,
+                          vals, None, 0, None) == qg.QG_EWORKSPACE
+    # MoE: top_k above the limit, then more than the experts
+    lg = ctypes.c_void_p(0x400000)
+    assert L.qmoe_experts(ctypes.byref(W), ctypes.byref(W), ctypes.byref(W), 16, 128, 256, 64, 4,
+                          0, None, lg, 9, None, 0.0, X, X, None, None, None, 0,
+                          None) == qg.QG_EUNSUPPORTED
+    assert L.qmoe_experts(ctypes.byref(W), ctypes.byref(W), ctypes.byref(W), 2, 128, 256, 64, 4,
+                          0, None, lg, 3, None, 0.0, X, X, None, None, None, 0,
+                          None) == qg.QG_EUNSUPPORTED
+    # MoE without a workspace
+    assert L.qmoe_experts(ctypes.byref(W), ctypes.byref(W), ctypes.byref(W), 16, 128, 256, 64, 4,
+                          0, None, lg, 3, None, 0.0, X, X, None, None, None, 0,
+                          None) == qg.QG_EWORKSPACE
+
+
+def test_workspace_queries(L):
+    for op in (qg.QG_OP_GEMV, qg.QG_OP_GEMV_RMSNORM, qg.QG_OP_SWIGLU):
+        assert qg.qg_workspace_bytes(op, 4096, 4096) > 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_MOE, 4096, 1024, 1, 4, 0, 3) > 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_LOGITS_TOPK, 151936, 1024, 1, 4, 0, 40) > 0
+    with pytest.raises(qg.QgError):
+        qg.qg_workspace_bytes(qg.QG_OP_LOGITS_TOPK, 100, 64, 1, 4, 0, 2000)
+    with pytest.raises(qg.QgError):
+        qg.qg_workspace_bytes(99, 1, 1)
+    assert L.qg_workspace_init(None, 256, None) == qg.QG_EINVAL
+    assert L.qg_workspace_init(ctypes.c_void_p(0x1000), 6, None) == qg.QG_EINVAL
+
+
+def test_tune_rejects_bad_values(L):
+    assert L.qg_tune(9, 1) == qg.QG_EINVAL
+    assert L.qg_tune(1, 3) == qg.QG_EINVAL
+    assert L.qg_tune(2, 48) == qg.QG_EINVAL
+    assert L.qg_tune(0, 17) == qg.QG_EINVAL
+    for k in range(4):
+        assert L.qg_tune(k, 0) == qg.QG_OK
+
+
+def test_empty_rows_is_a_no_op(L):
+    # N = 0 is valid and enqueues nothing (it returns before any HIP call)
+    assert call_gemv(L, N=0) == qg.QG_OK

@@ -1,0 +1,389 @@
+"""GPU parity: every entry point of the HIP library against the CPU oracle on
+the same seeded inputs.
+
+Bars: code unpacking and top-k indices bit-exact; floating outputs within
+max|y_gpu - y_ref| <= 2e-3 * max|y_ref| per output vector (fp32 accumulation
+against the fp64 oracle). Large shapes are checked on sampled rows that the
+oracle computes one by one."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def qg():
+    import dequant_gemv_qgemv_amd as qg
+    import os
+    if not os.path.exists(qg.LIB_PATH):
+        from dequant_gemv_qgemv_amd import build
+        build.build()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qg.lib()
+    yield qg
+    for k in range(4):
+        qg.qg_tune(k, 0)
+
+
+DEV = "cuda"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def close(got, ref, tol=TOL, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    bound = tol * max(np.max(np.abs(ref)) if ref.size else 0.0, 1e-30)
+    assert err <= bound, f"{what}: max err {err:.3e} > {bound:.3e}"
+
+
+def dev_mat(qg, W):
+    return qg.QMat.from_host(W, DEV)
+
+
+def to_dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return torch.from_numpy(a).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+def rows_of(W, rows):
+    out = dict(W)
+    out["N"] = len(rows)
+    for k in ("q", "scales", "biases", "lut"):
+        if W.get(k) is not None:
+            out[k] = W[k][rows]
+    return out
+
+
+def sample_rows(N, n=256, seed=0):
+    if N <= n:
+        return np.arange(N)
+    rng = np.random.default_rng(seed)
+    r = np.unique(np.concatenate([[0, N - 1], rng.choice(N, n - 2, replace=False)]))
+    return r
+
+
+def ws_for(qg, op, N, K, k=1):
+    return qg.workspace(op, N, K, 1, 4, 0, k, DEV)
+
+
+# ---------------------------------------------------------------------------
+SHAPES = [(1, 64), (7, 128), (300, 1024), (1000, 3072), (513, 4096), (64, 14336), (2048, 2048)]
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("xdt", ["f16", "f32"])
+def test_qgemv_4bit(qg, N, K, xdt):
+    say(f"qgemv 4-bit N={N} K={K} x={xdt}")
+    W = synth.qmat(11, ("g4", N, K), N, K, 4)
+    x = synth.activations(11, ("x", K), K, np.float16 if xdt == "f16" else np.float32)
+    ws = ws_for(qg, qg.QG_OP_GEMV, N, K)
+    y = qg.qgemv(dev_mat(qg, W), to_dev(x), ws=ws)
+    torch.cuda.synchronize()
+    close(y.cpu().numpy(), oracle.gemv(W, x.astype(np.float64), nthreads=8), what="qgemv")
+
+
+def test_qgemv_config0(qg):
+    """N=K=2048, 4-bit g64, x fp16 N(0,1), y fp32: the single-matvec workload."""
+    say("qgemv config0 2048x2048")
+    W = synth.qmat(1234, "cfg0", 2048, 2048, 4)
+    x = synth.activations(1234, "cfg0", 2048, np.float16)
+    y = qg.qgemv(dev_mat(qg, W), to_dev(x))
+    torch.cuda.synchronize()
+    close(y.cpu().numpy(), oracle.gemv(W, x, nthreads=8), what="cfg0")
+
+
+@pytest.mark.parametrize("lpr", [16, 32, 64])
+@pytest.mark.parametrize("rows", [1, 2])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_qgemv_variants(qg, lpr, rows, splits):
+    N, K = 333, 3072
+    say(f"qgemv variant lpr={lpr} rows={rows} splits={splits}")
+    W = synth.qmat(5, "var", N, K, 4)
+    x = synth.activations(5, "varx", K, np.float32)
+    r = synth.activations(5, "varr", N, np.float32)
+    ws = ws_for(qg, qg.QG_OP_GEMV, N, K)
+    qg.qg_tune(2, lpr)
+    qg.qg_tune(1, rows)
+    qg.qg_tune(0, splits)
+    try:
+        y = qg.qgemv(dev_mat(qg, W), to_dev(x), residual=to_dev(r), ws=ws)
+        y2 = qg.qgemv(dev_mat(qg, W), to_dev(x), residual=to_dev(r), ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        for k in range(3):
+            qg.qg_tune(k, 0)
+    ref = oracle.gemv(W, x, r, nthreads=8)
+    close(y.cpu().numpy(), ref, what="variant")
+    assert torch.equal(y, y2), "not deterministic"
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_unpack_bit_exact(qg, bits):
+    """s=1, b=0 and x = e_k: y_n is code[n][k] exactly (any summation order)."""
+    N, K = 96, 512
+    say(f"unpack probe bits={bits}")
+    W = synth.qmat(3, ("unpack", bits), N, K, bits)
+    W["scales"][:] = 1
+    W["biases"][:] = 0
+    codes = oracle.unpack(W)
+    Wd = dev_mat(qg, W)
+    for k in [0, 1, 2, 7, 8, 15, 16, 31, 33, 63, 64, 100, 255, 256, 511]:
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        y = qg.qgemv(Wd, to_dev(x)).cpu().numpy()
+        assert np.array_equal(y, codes[:, k].astype(np.float32)), f"column {k}"
+    # 16^j at four columns (fp32): decodes four codes per launch, exactly
+    cols = [5, 70, 200, 511]
+    x = np.zeros(K, np.float32)
+    for j, c in enumerate(cols):
+        x[c] = float(16 ** j)
+    y = qg.qgemv(Wd, to_dev(x)).cpu().numpy().astype(np.int64)
+    for j, c in enumerate(cols):
+        assert np.array_equal((y >> (4 * j)) & 15, codes[:, c])
+
+
+def test_dequant_single_rounding_bit_exact(qg):
+    """x = e_k gives y_n = fl32(code*s + b) with one rounding."""
+    N, K = 64, 256
+    W = synth.qmat(4, "dq", N, K, 4)
+    dense = oracle.dequant(W)
+    Wd = dev_mat(qg, W)
+    for k in [0, 3, 64, 129, 255]:
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        y = qg.qgemv(Wd, to_dev(x)).cpu().numpy()
+        assert np.array_equal(y, dense[:, k].astype(np.float32)), f"column {k}"
+
+
+def test_lut_one_hot_bit_exact(qg):
+    N, K = 48, 256
+    W = synth.qmat(6, "lut1h", N, K, 4, synth.LUT)
+    dense = oracle.dequant(W)
+    Wd = dev_mat(qg, W)
+    for k in [0, 1, 31, 32, 200]:
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        y = qg.qgemv(Wd, to_dev(x)).cpu().numpy()
+        assert np.array_equal(y, dense[:, k].astype(np.float32)), f"column {k}"
+
+
+@pytest.mark.parametrize("bits,fmt", [(2, synth.AFFINE), (4, synth.LUT)])
+@pytest.mark.parametrize("N,K", [(5, 64), (777, 1024), (640, 4096), (96, 14336)])
+def test_qgemv_2bit_and_lut(qg, bits, fmt, N, K):
+    say(f"qgemv bits={bits} fmt={fmt} N={N} K={K}")
+    W = synth.qmat(8, ("b", bits, fmt, N, K), N, K, bits, fmt)
+    x = synth.activations(8, ("x", K), K, np.float16)
+    ws = ws_for(qg, qg.QG_OP_GEMV, N, K)
+    y = qg.qgemv(dev_mat(qg, W), to_dev(x), ws=ws)
+    torch.cuda.synchronize()
+    close(y.cpu().numpy(), oracle.gemv(W, x, nthreads=8), what="2bit/lut")
+
+
+@pytest.mark.parametrize("N,K", [(6144, 4096), (2048, 1024), (100, 14336)])
+def test_qgemv_rmsnorm(qg, N, K):
+    say(f"qgemv_rmsnorm N={N} K={K}")
+    W = synth.qmat(9, ("rn", N, K), N, K, 4)
+    g = synth.norm_weight(9, ("g", K), K)
+    x = synth.activations(9, ("x", K), K, np.float32) * 3.0
+    r = synth.activations(9, ("r", N), N, np.float32)
+    ws = ws_for(qg, qg.QG_OP_GEMV_RMSNORM, N, K)
+    rows = sample_rows(N)
+    y = qg.qgemv_rmsnorm(dev_mat(qg, W), to_dev(x), to_dev(g), 1e-5, residual=to_dev(r), ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_gemv(rows_of(W, rows), x, g, 1e-5, r[rows])
+    close(y.cpu().numpy()[rows], ref, what="rmsnorm")
+
+
+@pytest.mark.parametrize("F,K,norm", [(14336, 4096, True), (3072, 1024, True), (1000, 2048, False),
+                                      (8, 64, True)])
+def test_qswiglu(qg, F, K, norm):
+    say(f"qswiglu F={F} K={K} norm={norm}")
+    Wg = synth.qmat(10, ("gate", F, K), F, K, 4)
+    Wu = synth.qmat(10, ("up", F, K), F, K, 4)
+    g = synth.norm_weight(10, ("g", K), K) if norm else None
+    x = synth.activations(10, ("x", K), K, np.float32)
+    ws = ws_for(qg, qg.QG_OP_SWIGLU, F, K)
+    rows = sample_rows(F)
+    u = qg.qswiglu(dev_mat(qg, Wg), dev_mat(qg, Wu), to_dev(x),
+                   None if g is None else to_dev(g), 1e-5, ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_swiglu(rows_of(Wg, rows), rows_of(Wu, rows), x, g, 1e-5)
+    close(u.cpu().numpy()[rows], ref, what="swiglu")
+
+
+def test_residual_in_place(qg):
+    N, K = 4096, 4096
+    W = synth.qmat(12, "inplace", N, K, 4)
+    x = synth.activations(12, "x", K, np.float32)
+    r = synth.activations(12, "r", N, np.float32)
+    rows = sample_rows(N)
+    yd = to_dev(r.copy())
+    qg.qgemv(dev_mat(qg, W), to_dev(x), residual=yd, y=yd)
+    torch.cuda.synchronize()
+    close(yd.cpu().numpy()[rows], oracle.gemv(rows_of(W, rows), x, r[rows]), what="in-place")
+
+
+# ---------------------------------------------------------------------------
+def test_topk_ties_bit_exact(qg):
+    """s = 0 and x = 1 make logit_n = 64 * b_n exactly; duplicate b give ties."""
+    V, K, k = 5000, 64, 40
+    W = synth.qmat(13, "ties", V, K, 4)
+    W["scales"][:] = 0
+    rng = np.random.default_rng(1)
+    W["biases"][:, 0] = rng.choice(np.array([0.5, 0.25, -0.0, 0.0, 0.125], np.float16), V)
+    x = np.ones(K, np.float32)
+    ws = qg.workspace(qg.QG_OP_LOGITS_TOPK, V, K, 1, 4, 0, k, DEV)
+    z, idx, vals = qg.qlogits_topk(dev_mat(qg, W), to_dev(x), k, ws=ws)
+    torch.cuda.synchronize()
+    zc = z.cpu().numpy()
+    assert np.array_equal(zc, (64.0 * W["biases"][:, 0].astype(np.float64)).astype(np.float32))
+    ridx, rvals = oracle.topk(zc, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.array_equal(vals.cpu().numpy(), rvals.astype(np.float32))
+
+
+@pytest.mark.parametrize("V,K,k,norm", [(151936, 1024, 40, True), (1000, 256, 1, False),
+                                        (40, 128, 40, True), (9000, 64, 1024, False)])
+def test_qlogits_topk(qg, V, K, k, norm):
+    say(f"qlogits_topk V={V} K={K} k={k}")
+    W = synth.qmat(14, ("lm", V, K), V, K, 4)
+    g = synth.norm_weight(14, "gf", K) if norm else None
+    x = synth.activations(14, "x", K, np.float32) * 5.0
+    ws = qg.workspace(qg.QG_OP_LOGITS_TOPK, V, K, 1, 4, 0, k, DEV)
+    z, idx, vals = qg.qlogits_topk(dev_mat(qg, W), to_dev(x), k,
+                                   None if g is None else to_dev(g), 1e-5, ws=ws)
+    torch.cuda.synchronize()
+    zc = z.cpu().numpy()
+    rows = sample_rows(V)
+    ref = oracle.gemv(rows_of(W, rows), oracle.rmsnorm(x, g) if norm else x)
+    close(zc[rows], ref, what="logits")
+    ridx, rvals = oracle.topk(zc, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.array_equal(vals.cpu().numpy(), rvals.astype(np.float32))
+    # a second call on the same workspace gives the same answer
+    _, idx2, _ = qg.qlogits_topk(dev_mat(qg, W), to_dev(x), k,
+                                 None if g is None else to_dev(g), 1e-5, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+
+
+# ---------------------------------------------------------------------------
+def moe_weights(seed, E, F, H):
+    gate = synth.qmat(seed, "gate_all", E * F, H, 4)
+    up = synth.qmat(seed, "up_all", E * F, H, 4)
+    down = synth.qmat(seed, "down_all", E * H, F, 4)
+    for Wt in (gate, up, down):
+        Wt["E"] = E
+    shared = (synth.qmat(seed, "sh_gate", F, H, 4), synth.qmat(seed, "sh_up", F, H, 4),
+              synth.qmat(seed, "sh_down", H, F, 4))
+    return gate, up, down, shared
+
+
+@pytest.mark.parametrize("E,F,H,top_k,shared", [(16, 128, 256, 3, True), (8, 64, 128, 1, False),
+                                                (512, 1024, 4096, 3, True)])
+def test_qmoe_experts(qg, E, F, H, top_k, shared):
+    say(f"qmoe_experts E={E} F={F} H={H} top_k={top_k}")
+    gate, up, down, sh = moe_weights(15, E, F, H)
+    g = synth.norm_weight(15, "g", H)
+    x = synth.activations(15, "x", H, np.float32)
+    Gd, Ud, Dd = dev_mat(qg, gate), dev_mat(qg, up), dev_mat(qg, down)
+    shd = tuple(dev_mat(qg, m) for m in sh) if shared else None
+    ws = qg.workspace(qg.QG_OP_MOE, H, F, 1, 4, 0, top_k, DEV)
+    for draw in range(3):
+        lg = synth.router_logits(15, ("route", draw), E)
+        ids = torch.empty(top_k, dtype=torch.int32, device=DEV)
+        w = torch.empty(top_k, dtype=torch.float32, device=DEV)
+        y = qg.qmoe_experts(Gd, Ud, Dd, E, shd, to_dev(lg), top_k, to_dev(x), to_dev(g), 1e-5,
+                            sel_ids=ids, sel_w=w, ws=ws)
+        torch.cuda.synchronize()
+        yref, rid, rw = oracle.moe_layer(gate, up, down, sh if shared else None, lg, top_k, x, g,
+                                         nthreads=8)
+        assert np.array_equal(ids.cpu().numpy(), rid)
+        close(w.cpu().numpy(), rw, tol=1e-6, what="routing weights")
+        close(y.cpu().numpy(), yref, what="moe")
+
+
+# ---------------------------------------------------------------------------
+def test_llama_layer_full_size(qg):
+    """One Llama-3-8B-shaped decode layer through the four fused calls."""
+    say("llama layer full size")
+    model = synth.LLAMA3_8B
+    w = synth.layer_weights(1234, model, 0)
+    H = model["hidden"]
+    x = synth.activations(1234, "x0", H, np.float32)
+    d = {k: dev_mat(qg, v) for k, v in w.items() if isinstance(v, dict)}
+    ws = qg.workspace(qg.QG_OP_SWIGLU, model["ffn"], H, 1, 4, 0, 1, DEV)
+    xd = to_dev(x)
+    qkv = qg.qgemv_rmsnorm(d["qkv"], xd, to_dev(w["g_attn"]), 1e-5, ws=ws)
+    h = qg.qgemv(d["o"], qkv[:model["q_dim"]], residual=xd, ws=ws)
+    u = qg.qswiglu(d["gate"], d["up"], h, to_dev(w["g_ffn"]), 1e-5, ws=ws)
+    y = qg.qgemv(d["down"], u, residual=h, ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle.decoder_layer(w, x, model["q_dim"], 1e-5, nthreads=8)
+    close(y.cpu().numpy(), ref, what="layer")
+
+
+def test_graph_replay_matches_eager(qg):
+    """Two Llama-shaped layers captured in a HIP graph, replayed several times
+    with eager work between the replays; every replay equals the eager run."""
+    model = dict(synth.LLAMA3_8B)
+    H, QD = model["hidden"], model["q_dim"]
+    ws_ = [synth.layer_weights(77, model, li) for li in range(2)]
+    layers = []
+    for w in ws_:
+        d = {k: dev_mat(qg, v) for k, v in w.items() if isinstance(v, dict)}
+        d["ga"], d["gf"] = to_dev(w["g_attn"]), to_dev(w["g_ffn"])
+        layers.append(d)
+    ws = ws_for(qg, qg.QG_OP_SWIGLU, model["ffn"], H)
+    x0 = to_dev(synth.activations(77, "x0", H, np.float32))
+    x = torch.empty_like(x0)
+    qkv = torch.empty(model["qkv"], dtype=torch.float32, device=DEV)
+    h = torch.empty(H, dtype=torch.float32, device=DEV)
+    u = torch.empty(model["ffn"], dtype=torch.float32, device=DEV)
+
+    def token():
+        x.copy_(x0)
+        for d in layers:
+            qg.qgemv_rmsnorm(d["qkv"], x, d["ga"], 1e-5, y=qkv, ws=ws)
+            qg.qgemv(d["o"], qkv[:QD], residual=x, y=h, ws=ws)
+            qg.qswiglu(d["gate"], d["up"], h, d["gf"], 1e-5, u=u, ws=ws)
+            qg.qgemv(d["down"], u, residual=h, y=x, ws=ws)
+
+    token()
+    torch.cuda.synchronize()
+    eager = x.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        token()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        token()
+    for rep in range(4):
+        x.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x, eager), f"replay {rep}"
+        token()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(x, eager)
