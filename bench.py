@@ -11,7 +11,8 @@ graph and replayed.
 
 Prints ONE JSON line: value = algorithmic bytes per token / time per token
 (GB/s), plus equivalent tokens/s, the roofline of the dominant kernel (the
-gate.up SwiGLU launch, timed per launch with HIP events on its stream), the
+gate.up SwiGLU launch: 32 back-to-back launches over distinct weights in a
+graph, timed with HIP events on the stream that replays it), the
 measured device-to-device copy bandwidth, and the CPU oracle's throughput on a
 bounded sample of the same workload.
 """
@@ -49,6 +50,91 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+REF_READ_BYTES = 64 << 20  # reference streaming read of known size for counter calibration
+
+
+def pmc_pass(qg, layers, model, dev):
+    import torch
+    H, FF = model["hidden"], model["ffn"]
+    h = torch.randn(H, device=dev)
+    u = torch.empty(FF, dtype=torch.float32, device=dev)
+    ws = qg.workspace(qg.QG_OP_SWIGLU, FF, H, 1, 4, 0, 1, dev)
+    for i in range(8):
+        d = layers[i % len(layers)]
+        qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
+    buf = torch.ones(2 * REF_READ_BYTES // 4, dtype=torch.float32, device=dev)
+    out = torch.empty(512 * 256, dtype=torch.int32, device=dev)
+    for i in range(2):
+        qg.qg_probe_read(buf[i * REF_READ_BYTES // 4:(i + 1) * REF_READ_BYTES // 4], out, 512)
+    torch.cuda.synchronize()
+    log("pmc pass done")
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """HBM bytes per gate.up SwiGLU launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), scaled by the FETCH_SIZE the reference read of REF_READ_BYTES
+    reports (the counter's unit on this device)."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        sw, ref = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            if re.search(r"qmv_kernel<4, 0, \d+, \d, 1, 0, \d>", r["Kernel_Name"]):
+                sw.append(v)
+            elif "probe_read" in r["Kernel_Name"]:
+                ref.append(v)
+        return sw, ref
+
+    sw_f, ref_f = per_kernel(fetch_csv, "FETCH_SIZE")
+    sw_w, _ = per_kernel(write_csv, "WRITE_SIZE")
+    scale = REF_READ_BYTES / (sum(ref_f) / len(ref_f))
+    fetch = sum(sw_f) / len(sw_f) * scale
+    write = sum(sw_w) / len(sw_w) * scale
+    out = {"kernel": "qswiglu 14336x4096 x2 (gate.up, rmsnorm)", "kernel_hash": kernel_hash(),
+           "counter_scale": round(scale, 4), "fetch_bytes_per_launch": round(fetch),
+           "write_bytes_per_launch": round(write), "bytes_per_launch": round(fetch + write),
+           "launches": len(sw_f)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out))
+
+
+def summarize_trace(path):
+    """Average duration of each of the four matvec launches of a decode layer
+    (qkv, o, gate.up, down: the launch order inside a token) from a rocprofv3
+    kernel-trace CSV."""
+    import csv
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    q = [r for r in rows if "qmv_kernel" in r["Kernel_Name"]]
+    names = ["qkv: rmsnorm + 6144x4096", "o: 4096x4096 + residual",
+             "gate.up: swiglu 2 x 14336x4096", "down: 4096x14336 + residual"]
+    nbytes = [6144 * 4096 * 9 // 16, 4096 * 4096 * 9 // 16, 2 * 14336 * 4096 * 9 // 16,
+              4096 * 14336 * 9 // 16]
+    dur = [[] for _ in names]
+    i = 0
+    while i + 3 < len(q):
+        # template arguments: bits, fmt, lanes per row, rows, epilogue (1 = SwiGLU), ...
+        swi = [q[i + k]["Kernel_Name"].split("<", 1)[1].split(",")[4].strip() == "1"
+               for k in range(4)]
+        if swi != [False, False, True, False]:
+            i += 1
+            continue
+        for k in range(4):
+            dur[k].append(int(q[i + k]["End_Timestamp"]) - int(q[i + k]["Start_Timestamp"]))
+        i += 4
+    print("| launch | calls | avg us | min us | weight bytes | GB/s at avg |")
+    print("|---|---|---|---|---|---|")
+    for k, name in enumerate(names):
+        v = dur[k]
+        avg = sum(v) / len(v) / 1e3
+        print(f"| {name} | {len(v)} | {avg:.2f} | {min(v) / 1e3:.2f} | {nbytes[k]} | "
+              f"{nbytes[k] / avg / 1e3:.0f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -59,7 +145,20 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run only 8 gate.up SwiGLU launches and 2 reference reads of 64 MiB "
+                         "(for rocprofv3 --pmc counter passes)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter CSVs of two --pmc-pass runs into the traffic file")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="per-matvec kernel durations of the decode tokens in a rocprofv3 trace")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -102,6 +201,10 @@ def main():
     act_bytes = model["layers"] * 4 * (
         (H + model["qkv"]) + (QD + H + H) + (H + FF) + (FF + H + H)) + model["layers"] * 2 * H * 2
     step_bytes = weight_bytes + act_bytes
+
+    if args.pmc_pass:
+        pmc_pass(qg, layers, model, dev)
+        return
 
     # ---- buffers ---------------------------------------------------------------
     x0 = torch.from_numpy(synth.activations(args.seed, "x0", H, np.float32)).to(dev)
@@ -158,23 +261,39 @@ def main():
     gbs = step_bytes / (ms * 1e-3) / 1e9
     log(f"{args.steps} tokens: {ms * 1e3:.1f} us/token, {gbs:.0f} GB/s, {1e3 / ms:.0f} tok/s")
 
-    # ---- dominant kernel: gate.up SwiGLU, per-launch HIP events ----------------
+    # ---- dominant kernel: gate.up SwiGLU ----------------------------------------
+    # 32 back-to-back launches (one per layer, distinct weights) captured in a
+    # graph and replayed, timed with HIP events on the capturing stream.
     sw_bytes = (layers[0]["gate"].nbytes() + layers[0]["up"].nbytes() + H * 4 + H * 2 + FF * 4)
-    n_rep = 2
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(len(layers) * n_rep)]
-    for i in range(len(evs)):
-        d = layers[i % len(layers)]
-        qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)  # warm the launch path
+
+    def swiglu_all():
+        for d in layers:
+            qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
+
+    swiglu_all()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    for i, (a, b) in enumerate(evs):
-        d = layers[i % len(layers)]
-        a.record(stream)
-        qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws, stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    sw_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    sw_us = None
+    if graph is not None:
+        sg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sg):
+            swiglu_all()
+        sg.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        a.record()
+        for _ in range(reps):
+            sg.replay()
+        b.record()
+        torch.cuda.synchronize()
+        sw_us = a.elapsed_time(b) * 1e3 / (reps * len(layers))
+    else:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        swiglu_all()
+        b.record()
+        torch.cuda.synchronize()
+        sw_us = a.elapsed_time(b) * 1e3 / len(layers)
     sw_gbs = sw_bytes / (sw_us * 1e-6) / 1e9
 
     # traffic: HBM bytes per launch from the committed counter profile, if it

@@ -29,7 +29,8 @@ QG_OP_GEMV, QG_OP_GEMV_RMSNORM, QG_OP_SWIGLU, QG_OP_MOE, QG_OP_LOGITS_TOPK = 0, 
 QG_MAX_TOPK = 1024
 
 EXPORTED = ("qg_status_str", "qg_workspace_bytes", "qg_workspace_init", "qg_tune", "qgemv",
-            "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk")
+            "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk", "qg_probe_read",
+            "qg_probe_copy")
 
 
 class QgError(RuntimeError):
@@ -65,6 +66,8 @@ def lib():
         L.qswiglu.argtypes = [Q, Q, I, I, I, I, I, I, P, I, P, F, P, P, S, P]
         L.qmoe_experts.argtypes = [Q, Q, Q, I, I, I, I, I, I, Q, P, I, P, F, P, P, P, P, P, S, P]
         L.qlogits_topk.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P, S, P]
+        L.qg_probe_read.argtypes = [P, S, P, I, I, P]
+        L.qg_probe_copy.argtypes = [P, P, S, I, P]
         for name in EXPORTED:
             if name != "qg_status_str":
                 getattr(L, name).restype = I
@@ -162,6 +165,18 @@ def workspace(op: int, N: int, K: int, M: int = 1, bits: int = 4, fmt: int = QG_
 
 def qg_tune(knob: int, value: int):
     _check(lib().qg_tune(knob, value), "qg_tune")
+
+
+def qg_probe_read(src, out, blocks: int, cached: bool = False, stream=None):
+    """Streams src once (read-only bandwidth probe); out: int32 [blocks*256]."""
+    _check(lib().qg_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(out), blocks,
+                               1 if cached else 0, _stream(stream)), "qg_probe_read")
+
+
+def qg_probe_copy(dst, src, blocks: int, stream=None):
+    """Copies src to dst (copy bandwidth probe)."""
+    _check(lib().qg_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), blocks,
+                               _stream(stream)), "qg_probe_copy")
 
 
 def _ws_args(ws):

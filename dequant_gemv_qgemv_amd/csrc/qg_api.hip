@@ -101,7 +101,9 @@ constexpr int kMaxSplits = 16;
 constexpr size_t kLdsBudget = 64 * 1024;
 
 int codes_per_chunk(int bits) { return 128 / bits; }
-int pieces_per_chunk(int bits) { return 128 / bits / 4; }
+// 16-byte pieces of staged x per chunk: fp16 pairs for the affine formats,
+// fp32 for the LUT format.
+int pieces_per_chunk(int bits, int fmt) { return fmt == QG_LUT ? 8 : (bits == 4 ? 4 : 8); }
 
 // Lanes per row: the widest of 64/32/16 that leaves no lane idle in any pass,
 // else the one that idles the fewest.
@@ -142,7 +144,7 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
   const int rpb = (64 / pl.lpr) * pl.rows;
   const int nbands = (s.N + rpb - 1) / rpb;
   const int tiles = (nbands + kWaves - 1) / kWaves;
-  const size_t per_chunk = (size_t)pieces_per_chunk(s.bits) * 16 + 4;
+  const size_t per_chunk = (size_t)pieces_per_chunk(s.bits, s.fmt) * 16 + 16;  // + ChunkInfo
   const size_t lut_bytes = (s.fmt == QG_LUT) ? (size_t)kWaves * rpb * 2 * 16 * 4 : 0;
   int max_chunks = (int)((kLdsBudget - lut_bytes) / per_chunk);
   max_chunks = (max_chunks / pl.lpr) * pl.lpr;
@@ -175,6 +177,7 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
   if (gx > cap) gx = cap;
   gx = ((gx + 7) / 8) * 8;  // slices of one tile share an XCD (workgroups go round-robin over 8)
   pl.grid_x = gx;
+  pl.depth = g_knob[4].load() ? g_knob[4].load() : 2;
   return pl;
 }
 
@@ -306,9 +309,11 @@ int qg_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
 }
 
 // Tuning override for tests and benchmarks: knob 0 = split count, 1 = rows per
-// lane, 2 = lanes per row, 3 = workgroups per CU; value 0 restores automatic.
+// lane, 2 = lanes per row, 3 = workgroups per CU, 4 = pipeline depth; value 0
+// restores automatic.
 int qg_tune(int knob, int value) {
-  if (knob < 0 || knob > 3 || value < 0) return QG_EINVAL;
+  if (knob < 0 || knob > 4 || value < 0) return QG_EINVAL;
+  if (knob == 4 && value != 0 && value != 2 && value != 4) return QG_EINVAL;
   if (knob == 1 && value != 0 && value != 1 && value != 2) return QG_EINVAL;
   if (knob == 2 && value != 0 && value != 16 && value != 32 && value != 64) return QG_EINVAL;
   if (knob == 0 && value > kMaxSplits) return QG_EINVAL;

@@ -76,6 +76,7 @@ struct MvPlan {
   int splits;
   int slice_chunks;
   int grid_x;
+  int depth;          // (band, pass) items in flight per wave: 2 or 4
   size_t lds_bytes;
 };
 

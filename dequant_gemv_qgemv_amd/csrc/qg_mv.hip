@@ -9,30 +9,35 @@
 //
 // The pages' rewrite fma(code, scale*x, bias*x) is applied at group level:
 //   sum_{k in g} (c_k s + b) x_k = s * sum_{k in g} c_k x_k + b * sum_{k in g} x_k,
-// so the per-weight work is one fused multiply-add of the code with x, and the
-// scale and bias enter once per 16-byte chunk of codes.
+// so the per-weight work is a multiply-add of the code with x, and the scale
+// and bias enter once per 16-byte chunk of codes, in fp32.
 //
 // Work mapping (one workgroup = 8 wave64s):
-//  * x (the slice of it this workgroup needs) is staged once in LDS as fp32,
-//    permuted and pre-scaled by powers of two so that the codes can be used
-//    straight out of the packed words (see below), plus one sum of x per chunk
-//    for the bias term. Conflict-free layout: the float4 a lane reads for chunk
-//    j of pass i, piece p sits at [i][p][j].
-//  * Each wave owns a band of rows: 64/LPR sub-waves of LPR lanes, each lane
+//  * x (the slice of it this workgroup needs) is staged once in LDS, permuted
+//    to match the code extraction below, plus one fp32 sum of x per chunk for
+//    the bias term. Conflict-free layout: the 16-byte piece a lane reads for
+//    chunk j of pass i, piece p sits at [i][p][j].
+//  * Each wave owns bands of rows: 64/LPR sub-waves of LPR lanes, each lane
 //    accumulating R rows. Lanes stride along K in 16-byte chunks (coalesced
-//    dwordx4 loads of the row-major codes), two passes in flight at a time.
-//  * Row sums are reduced across the LPR lanes with cross-lane shuffles.
+//    dwordx4 buffer loads of the row-major codes).
+//  * The (band, pass) items of a wave form one software pipeline: loads for
+//    the next items are in flight while the current one is computed, across
+//    band boundaries, and the first ones are issued before x is staged.
+//  * Row sums are reduced across the LPR lanes with DPP.
 //  * Optional split-K: workgroup (tile t, slice s) writes fp32 partials; the
 //    last workgroup of tile t to finish (integer ticket, no float atomics)
 //    adds the slices in fixed order and applies the epilogue, so results do
 //    not depend on timing.
 //
-// Code extraction: masking a packed word with 0x000F000F leaves two fp16 bit
-// patterns that are the subnormal numbers code*2^-24 exactly. v_fma_mix_f32
-// multiplies such an fp16 operand with an fp32 x, so 8 codes of a word cost
-// 1 shift + 4 masks + 8 mixed FMAs. Codes at odd nibble positions come out
-// multiplied by 16 (mask 0x00F000F0); their x is pre-divided by 16 in LDS.
-// 2-bit fields come out multiplied by 4^j; their x is pre-divided by 4^j.
+// Code extraction (affine formats): masking a packed word with 0x000F000F
+// leaves two fp16 bit patterns that are exactly the subnormal numbers
+// code*2^-24. v_dot2_f32_f16 multiplies such a pair with a pair of fp16 x
+// values and adds both products to an fp32 accumulator, so 8 codes of a word
+// cost 1 shift + 4 masks + 4 dot2. Codes at odd nibble positions come out
+// multiplied by 16 (mask 0x00F000F0) and 2-bit fields by 4^j; their x is
+// pre-divided by that power of two when staged. x is staged in fp16 after an
+// exact power-of-two range scale 2^-e chosen from max|x| over the slice; the
+// chunk result is multiplied back by 2^(24+e). The LUT format keeps x in fp32.
 #include "qg_internal.h"
 
 namespace qg {
@@ -42,107 +47,91 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t v) {
   return (float)__builtin_bit_cast(_Float16, v);
 }
 
-constexpr float kTwo24 = 16777216.0f;   // 2^24: undoes the subnormal code scale
 constexpr int kMaxLdsBytes = 64 * 1024;
 
-template <int BITS>
-struct Codes;
+// Per-format staging geometry: codes per 16-byte chunk, 16-byte pieces of
+// staged x per chunk, chunks per group of 64.
+template <int BITS, int FMT>
+struct Geo;
 template <>
-struct Codes<4> {
-  static constexpr int kPerChunk = 32;       // codes in one 16-byte chunk
-  static constexpr int kPieces = 8;          // float4 of staged x per chunk
-  static constexpr int kChunksPerGroup = 2;  // a group of 64 spans two chunks
+struct Geo<4, 0> {  // 32 codes; x as 16 fp16 pairs = 4 pieces
+  static constexpr int kPerChunk = 32, kPieces = 4, kChunksPerGroup = 2;
 };
 template <>
-struct Codes<2> {
-  static constexpr int kPerChunk = 64;
-  static constexpr int kPieces = 16;
-  static constexpr int kChunksPerGroup = 1;
+struct Geo<2, 0> {  // 64 codes; x as 32 fp16 pairs = 8 pieces
+  static constexpr int kPerChunk = 64, kPieces = 8, kChunksPerGroup = 1;
 };
+template <>
+struct Geo<4, 1> {  // LUT: 32 codes; x as 32 fp32 = 8 pieces
+  static constexpr int kPerChunk = 32, kPieces = 8, kChunksPerGroup = 2;
+};
+
+__device__ __forceinline__ float dot2(uint32_t codes, uint32_t xpair, float acc) {
+  return __builtin_amdgcn_fdot2(as_f16x2(codes), as_f16x2(xpair), acc, false);
+}
 
 // ---------------------------------------------------------------------------
 // Inner products of one 16-byte chunk of codes with its staged x.
 
-// 4-bit: returns 2^-24 * sum_k code_k x_k over the chunk's 32 codes.
-__device__ __forceinline__ float dot_q4(const u32x4 q, const float4* xr) {
+// 4-bit: 2^-24 * sum_k code_k x_k over 32 codes; xr[i] holds word i's pairs
+// (x0,x4) (x1/16,x5/16) (x2,x6) (x3/16,x7/16) as fp16.
+__device__ __forceinline__ float dot_q4(const u32x4 q, const u32x4* xr) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t t = w[i] >> 8;
-    const f16x2 h0 = as_f16x2(w[i] & 0x000F000Fu);  // fields 0, 4
-    const f16x2 h1 = as_f16x2(w[i] & 0x00F000F0u);  // fields 1, 5 (times 16)
-    const f16x2 h2 = as_f16x2(t & 0x000F000Fu);     // fields 2, 6
-    const f16x2 h3 = as_f16x2(t & 0x00F000F0u);     // fields 3, 7 (times 16)
-    const float4 u = xr[2 * i], v = xr[2 * i + 1];
-    a0 = fmaf((float)h0.x, u.x, a0);
-    a1 = fmaf((float)h0.y, u.y, a1);
-    a0 = fmaf((float)h1.x, u.z, a0);
-    a1 = fmaf((float)h1.y, u.w, a1);
-    a0 = fmaf((float)h2.x, v.x, a0);
-    a1 = fmaf((float)h2.y, v.y, a1);
-    a0 = fmaf((float)h3.x, v.z, a0);
-    a1 = fmaf((float)h3.y, v.w, a1);
+    a0 = dot2(w[i] & 0x000F000Fu, xr[i].x, a0);  // fields 0, 4
+    a1 = dot2(w[i] & 0x00F000F0u, xr[i].y, a1);  // fields 1, 5 (x16)
+    a0 = dot2(t & 0x000F000Fu, xr[i].z, a0);     // fields 2, 6
+    a1 = dot2(t & 0x00F000F0u, xr[i].w, a1);     // fields 3, 7 (x16)
   }
   return a0 + a1;
 }
 
-// 2-bit: returns 2^-24 * sum_k code_k x_k over the chunk's 64 codes.
-__device__ __forceinline__ float dot_q2(const u32x4 q, const float4* xr) {
+// 2-bit: 2^-24 * sum_k code_k x_k over 64 codes; word i uses xr[2i], xr[2i+1]
+// holding the pairs (f0,f8) (f1,f9)/4 (f2,f10)/16 (f3,f11)/64 (f4,f12)/256
+// (f5,f13) (f6,f14)/4 (f7,f15)/16.
+__device__ __forceinline__ float dot_q2(const u32x4 q, const u32x4* xr) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t t = w[i] >> 10;
-    const f16x2 h0 = as_f16x2(w[i] & 0x00030003u);  // fields 0, 8
-    const f16x2 h1 = as_f16x2(w[i] & 0x000C000Cu);  // fields 1, 9   (x4)
-    const f16x2 h2 = as_f16x2(w[i] & 0x00300030u);  // fields 2, 10  (x16)
-    const f16x2 h3 = as_f16x2(w[i] & 0x00C000C0u);  // fields 3, 11  (x64)
-    const f16x2 h4 = as_f16x2(w[i] & 0x03000300u);  // fields 4, 12  (x256)
-    const f16x2 h5 = as_f16x2(t & 0x00030003u);     // fields 5, 13
-    const f16x2 h6 = as_f16x2(t & 0x000C000Cu);     // fields 6, 14  (x4)
-    const f16x2 h7 = as_f16x2(t & 0x00300030u);     // fields 7, 15  (x16)
-    const float4 p0 = xr[4 * i], p1 = xr[4 * i + 1], p2 = xr[4 * i + 2], p3 = xr[4 * i + 3];
-    a0 = fmaf((float)h0.x, p0.x, a0);
-    a1 = fmaf((float)h0.y, p0.y, a1);
-    a0 = fmaf((float)h1.x, p0.z, a0);
-    a1 = fmaf((float)h1.y, p0.w, a1);
-    a0 = fmaf((float)h2.x, p1.x, a0);
-    a1 = fmaf((float)h2.y, p1.y, a1);
-    a0 = fmaf((float)h3.x, p1.z, a0);
-    a1 = fmaf((float)h3.y, p1.w, a1);
-    a0 = fmaf((float)h4.x, p2.x, a0);
-    a1 = fmaf((float)h4.y, p2.y, a1);
-    a0 = fmaf((float)h5.x, p2.z, a0);
-    a1 = fmaf((float)h5.y, p2.w, a1);
-    a0 = fmaf((float)h6.x, p3.x, a0);
-    a1 = fmaf((float)h6.y, p3.y, a1);
-    a0 = fmaf((float)h7.x, p3.z, a0);
-    a1 = fmaf((float)h7.y, p3.w, a1);
+    const u32x4 u = xr[2 * i], v = xr[2 * i + 1];
+    a0 = dot2(w[i] & 0x00030003u, u.x, a0);
+    a1 = dot2(w[i] & 0x000C000Cu, u.y, a1);
+    a0 = dot2(w[i] & 0x00300030u, u.z, a0);
+    a1 = dot2(w[i] & 0x00C000C0u, u.w, a1);
+    a0 = dot2(w[i] & 0x03000300u, v.x, a0);
+    a1 = dot2(t & 0x00030003u, v.y, a1);
+    a0 = dot2(t & 0x000C000Cu, v.z, a0);
+    a1 = dot2(t & 0x00300030u, v.w, a1);
   }
   return a0 + a1;
 }
 
 // LUT (4-bit codes, 16-entry table per row, held in this wave's LDS slot):
-// returns sum_k lut[code_k] x_k over the chunk's 32 codes (x in natural order).
-__device__ __forceinline__ float dot_lut(const u32x4 q, const float4* xr, const float* tab) {
+// sum_k lut[code_k] x_k over the chunk's 32 codes (x in natural order, fp32).
+__device__ __forceinline__ float dot_lut(const u32x4 q, const u32x4* xr, const float* tab) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float4 u = xr[2 * i], v = xr[2 * i + 1];
-    a0 = fmaf(tab[(w[i] >> 0) & 15u], u.x, a0);
-    a1 = fmaf(tab[(w[i] >> 4) & 15u], u.y, a1);
-    a0 = fmaf(tab[(w[i] >> 8) & 15u], u.z, a0);
-    a1 = fmaf(tab[(w[i] >> 12) & 15u], u.w, a1);
-    a0 = fmaf(tab[(w[i] >> 16) & 15u], v.x, a0);
-    a1 = fmaf(tab[(w[i] >> 20) & 15u], v.y, a1);
-    a0 = fmaf(tab[(w[i] >> 24) & 15u], v.z, a0);
-    a1 = fmaf(tab[(w[i] >> 28) & 15u], v.w, a1);
+    const u32x4 u = xr[2 * i], v = xr[2 * i + 1];
+    a0 = fmaf(tab[(w[i] >> 0) & 15u], __uint_as_float(u.x), a0);
+    a1 = fmaf(tab[(w[i] >> 4) & 15u], __uint_as_float(u.y), a1);
+    a0 = fmaf(tab[(w[i] >> 8) & 15u], __uint_as_float(u.z), a0);
+    a1 = fmaf(tab[(w[i] >> 12) & 15u], __uint_as_float(u.w), a1);
+    a0 = fmaf(tab[(w[i] >> 16) & 15u], __uint_as_float(v.x), a0);
+    a1 = fmaf(tab[(w[i] >> 20) & 15u], __uint_as_float(v.y), a1);
+    a0 = fmaf(tab[(w[i] >> 24) & 15u], __uint_as_float(v.z), a0);
+    a1 = fmaf(tab[(w[i] >> 28) & 15u], __uint_as_float(v.w), a1);
   }
   return a0 + a1;
 }
@@ -150,31 +139,40 @@ __device__ __forceinline__ float dot_lut(const u32x4 q, const float4* xr, const 
 // ---------------------------------------------------------------------------
 // Staging of x into LDS.
 
-// Writes the staged pieces of one chunk (codes-order permutation + power-of-two
-// pre-scales matching the masks in dot_q4 / dot_q2; natural order for LUT).
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const uint32_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
+  const uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
+  return a | (b << 16);
+}
+
+// Writes the staged pieces of one chunk: v holds the chunk's x already
+// multiplied by the range scale (affine) or as is (LUT).
 template <int BITS, int FMT>
-__device__ __forceinline__ void write_pieces(const float* v, float4* dst, int stride) {
+__device__ __forceinline__ void write_pieces(const float* v, u32x4* dst, int stride) {
   if constexpr (FMT == 1) {
 #pragma unroll
     for (int p = 0; p < 8; ++p)
-      dst[p * stride] = make_float4(v[4 * p], v[4 * p + 1], v[4 * p + 2], v[4 * p + 3]);
+      dst[p * stride] = u32x4{__float_as_uint(v[4 * p]), __float_as_uint(v[4 * p + 1]),
+                              __float_as_uint(v[4 * p + 2]), __float_as_uint(v[4 * p + 3])};
   } else if constexpr (BITS == 4) {
     constexpr float r16 = 1.0f / 16.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float* w = v + 8 * i;
-      dst[(2 * i) * stride] = make_float4(w[0], w[4], w[1] * r16, w[5] * r16);
-      dst[(2 * i + 1) * stride] = make_float4(w[2], w[6], w[3] * r16, w[7] * r16);
+      dst[i * stride] = u32x4{pack_f16(w[0], w[4]), pack_f16(w[1] * r16, w[5] * r16),
+                              pack_f16(w[2], w[6]), pack_f16(w[3] * r16, w[7] * r16)};
     }
   } else {
     constexpr float r4 = 0.25f, r16 = 1.0f / 16.0f, r64 = 1.0f / 64.0f, r256 = 1.0f / 256.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float* w = v + 16 * i;
-      dst[(4 * i) * stride] = make_float4(w[0], w[8], w[1] * r4, w[9] * r4);
-      dst[(4 * i + 1) * stride] = make_float4(w[2] * r16, w[10] * r16, w[3] * r64, w[11] * r64);
-      dst[(4 * i + 2) * stride] = make_float4(w[4] * r256, w[12] * r256, w[5], w[13]);
-      dst[(4 * i + 3) * stride] = make_float4(w[6] * r4, w[14] * r4, w[7] * r16, w[15] * r16);
+      dst[(2 * i) * stride] = u32x4{pack_f16(w[0], w[8]), pack_f16(w[1] * r4, w[9] * r4),
+                                    pack_f16(w[2] * r16, w[10] * r16),
+                                    pack_f16(w[3] * r64, w[11] * r64)};
+      dst[(2 * i + 1) * stride] = u32x4{pack_f16(w[4] * r256, w[12] * r256), pack_f16(w[5], w[13]),
+                                        pack_f16(w[6] * r4, w[14] * r4),
+                                        pack_f16(w[7] * r16, w[15] * r16)};
     }
   }
 }
@@ -224,23 +222,27 @@ __device__ __forceinline__ void load_f16(const uint16_t* src16, int k0, float* v
   }
 }
 
-// Block-wide sum (all threads receive it). `red` holds kWaves floats.
-__device__ __forceinline__ float block_sum(float v, float* red) {
+// Block-wide sum / max (all threads receive it). `red` holds kWaves floats.
+// Fixed combination order: every workgroup gets the same bits.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float* red) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = MAX ? fmaxf(v, o) : v + o;
+  }
   const int wave = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  float s = 0.f;
+  float s = red[0];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += red[w];  // fixed order: same value in every block
+  for (int w = 1; w < kWaves; ++w) s = MAX ? fmaxf(s, red[w]) : s + red[w];
   return s;
 }
 
-// 1/sqrt(mean(x^2) + eps) over all K activations (each workgroup computes it
-// itself, in the same order, so every workgroup gets the same value).
-__device__ float rms_scale(const MvParams& p, float* red) {
+// This thread's share of sum(x^2) over all K (strided groups of 8).
+__device__ float sumsq_all(const MvParams& p) {
   float ss = 0.f;
   const int K8 = p.K / 8;
   for (int i = threadIdx.x; i < K8; i += kThreads) {
@@ -249,54 +251,141 @@ __device__ float rms_scale(const MvParams& p, float* red) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
   }
-  const float tot = block_sum(ss, red);
-  return 1.0f / sqrtf(tot / (float)p.K + p.eps);
+  return ss;
 }
 
-// Stages chunks [c0, c0 + nch) of x (padded with zeros up to npass*LPR chunks).
-// For K segments with routing weights, chunk c of segment j is scaled by w_j.
-template <int BITS, int FMT, int LPR>
-__device__ void stage_x(const MvParams& p, int c0, int nch, int npass, float4* xl, float* xsum,
-                        float* red) {
-  constexpr int CPC = Codes<BITS>::kPerChunk;
-  constexpr int PIECES = Codes<BITS>::kPieces;
-  const float rs = p.norm_w ? rms_scale(p, red) : 1.0f;
-  const int total = npass * LPR;
-  for (int c = threadIdx.x; c < total; c += kThreads) {
-    float v[CPC];
-    float s = 0.f;
-    if (c < nch) {
-      const int cg = c0 + c;
-      load_x<CPC>(p.x, p.x_f32, cg * CPC, v);
-      if (p.norm_w) {
-        float g[CPC];
-        load_f16<CPC>(p.norm_w, cg * CPC, g);
+// Power-of-two range scale for the fp16 staging of one chunk: with m = max|x|
+// over the chunk, x * 2^-e stays below 2^14; returns 2^-e and sets
+// *back = 2^(24+e), which also undoes the 2^-24 of the subnormal codes.
+__device__ __forceinline__ float range_scale(float m, float* back) {
+  int E = 0;
+  if (m > 0.f && m < INFINITY) frexpf(m, &E);
+  const int e = (m > 0.f && m < INFINITY) ? E - 14 : 0;
+  *back = ldexpf(1.0f, 24 + e);
+  return ldexpf(1.0f, -e);
+}
+
+// Per-chunk staging record next to the staged x: the chunk's sum of x (for
+// the bias term), the factor 2^(24+e) that undoes the chunk's range scale and
+// the subnormal code scale, and the chunk's sum of squares of the raw x (for
+// the RMSNorm).
+struct ChunkInfo {
+  float xsum, back, ss, pad;
+};
+
+// One thread's chunk of x (and of the norm weights), loaded into registers
+// before the weight prefetch is issued: vector loads return in order, so x
+// must be requested first for its staging not to wait behind the weights.
+template <int CPC>
+struct XChunk {
+  float v[CPC];
+  u32x4 g[CPC / 8];  // norm weights as raw fp16 pairs
+};
+
+template <int CPC>
+__device__ __forceinline__ void stage_load(const MvParams& p, int cg, bool have, XChunk<CPC>& xc) {
+  if (have) {
+    load_x<CPC>(p.x, p.x_f32, cg * CPC, xc.v);
+    if (p.norm_w) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(p.norm_w + cg * CPC);
 #pragma unroll
-        for (int i = 0; i < CPC; ++i) v[i] = v[i] * g[i] * rs;
-      }
-      if (p.seg_mode == kSegCols && p.route.weights) {
-        const int seg = cg / p.seg_len;
-        const float wseg = seg < p.route.n_routed ? p.route.weights[seg] : 1.0f;
-#pragma unroll
-        for (int i = 0; i < CPC; ++i) v[i] *= wseg;
-      }
-#pragma unroll
-      for (int i = 0; i < CPC; ++i) s += v[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < CPC; ++i) v[i] = 0.f;
+      for (int i = 0; i < CPC / 8; ++i) xc.g[i] = src[i];
     }
-    const int pass = c / LPR, j = c % LPR;
-    write_pieces<BITS, FMT>(v, xl + pass * PIECES * LPR + j, LPR);
-    xsum[c] = s;
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPC; ++i) xc.v[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPC / 8; ++i) xc.g[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
+// Stages one chunk (v: its x values in natural order; cg: its logical index,
+// valid = inside the slice): x*g (RMSNorm weight; the 1/rms scalar is applied
+// to the row sums instead), times the K-segment routing weight, then the
+// chunk's own power-of-two range scale (affine formats) and the LDS write.
+// No block-wide reduction is involved.
+template <int BITS, int FMT, int LPR>
+__device__ __forceinline__ void stage_chunk(const MvParams& p, float* v, const u32x4* g, int c,
+                                            int cg, bool valid, u32x4* xl, ChunkInfo* info) {
+  constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
+  constexpr int PIECES = Geo<BITS, FMT>::kPieces;
+  float ss = 0.f;
+  if (p.norm_w) {
+#pragma unroll
+    for (int i = 0; i < CPC / 8; ++i) {
+      const uint32_t w[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f16x2 h = as_f16x2(w[q]);
+        const float a = v[8 * i + 2 * q], b = v[8 * i + 2 * q + 1];
+        ss = fmaf(a, a, fmaf(b, b, ss));
+        v[8 * i + 2 * q] = a * (float)h.x;
+        v[8 * i + 2 * q + 1] = b * (float)h.y;
+      }
+    }
+  }
+  float wseg = 1.0f;
+  if (valid && p.seg_mode == kSegCols && p.route.weights) {
+    const int seg = cg / p.seg_len;
+    wseg = seg < p.route.n_routed ? p.route.weights[seg] : 1.0f;
+  }
+  float s = 0.f, m = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPC; ++i) {
+    v[i] *= wseg;
+    s += v[i];
+    m = fmaxf(m, fabsf(v[i]));
+  }
+  float back = 1.0f;
+  if constexpr (FMT == 0) {
+    const float inv = range_scale(m, &back);
+#pragma unroll
+    for (int i = 0; i < CPC; ++i) v[i] *= inv;
+  }
+  write_pieces<BITS, FMT>(v, xl + (c / LPR) * PIECES * LPR + (c % LPR), LPR);
+  ChunkInfo ci;
+  ci.xsum = valid ? s : 0.f;
+  ci.back = back;
+  ci.ss = valid ? ss : 0.f;
+  ci.pad = 0.f;
+  info[c] = ci;
+}
+
+// Stages chunks [c0, c0 + nch) (zero padded to npass*LPR) when the chunks
+// outnumber the threads: each thread loops over its chunks, reading x again.
+template <int BITS, int FMT, int LPR>
+__device__ void stage_loop(const MvParams& p, int c0, int nch, int npass, u32x4* xl,
+                           ChunkInfo* info) {
+  constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
+  for (int c = threadIdx.x; c < npass * LPR; c += kThreads) {
+    XChunk<CPC> xc;
+    stage_load<CPC>(p, c0 + c, c < nch, xc);
+    stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
+  }
+}
+
+// 1/sqrt(mean(x^2) + eps), summed in fixed order from the per-chunk sums of
+// squares (staged slice = all of K), by each wave on its own: no barrier, and
+// every wave and workgroup gets the same bits.
+__device__ __forceinline__ float rms_from_chunks(const MvParams& p, const ChunkInfo* info, int C) {
+  float ss = 0.f;
+  for (int c = (threadIdx.x & 63); c < C; c += 64) ss += info[c].ss;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  return 1.0f / sqrtf(ss / (float)p.K + p.eps);
+}
+
+// 1/sqrt(mean(x^2) + eps) over all of K read from memory (used when this
+// workgroup stages only a slice of K). Every thread of the block calls it.
+__device__ float rms_all(const MvParams& p, float* red) {
+  return 1.0f / sqrtf(block_reduce<false>(sumsq_all(p), red) / (float)p.K + p.eps);
+}
+
 // ---------------------------------------------------------------------------
-// Per-pass loads through buffer descriptors. A descriptor covers one matrix
-// (or one expert's rows); loads at offsets past its end return zero without
-// touching memory, which handles the last band's missing rows, padding chunks
-// and the prefetch past the last pass without branches.
+// Loads through buffer descriptors. A descriptor covers one matrix (or one
+// expert's rows); loads at offsets past its end return zero without touching
+// memory, which handles the last band's missing rows, padding chunks and the
+// prefetch past the last item without branches.
 
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every descriptor's end
 
@@ -325,21 +414,42 @@ __device__ __forceinline__ MatRsrc mat_rsrc(const QMat& M, int rows, int wpr, in
   return r;
 }
 
-template <int R, bool TWO>
+// Matrix of segment `seg` (routed experts are looked up from the device ids).
+__device__ __forceinline__ QMat seg_mat(const MvParams& p, int seg, bool second) {
+  if (p.route.ids && seg < p.route.n_routed) {
+    const size_t r0 = (size_t)p.route.ids[seg] * (size_t)p.route.expert_rows;
+    const QMat all = second ? p.route.all_B : p.route.all_A;
+    QMat m;
+    m.q = all.q ? all.q + r0 * p.wpr : nullptr;
+    m.s = all.s ? all.s + r0 * p.gpr : nullptr;
+    m.b = all.b ? all.b + r0 * p.gpr : nullptr;
+    m.lut = all.lut ? all.lut + r0 * 16 : nullptr;
+    return m;
+  }
+  return second ? p.B[seg] : p.A[seg];
+}
+
+__device__ __forceinline__ int seg_rows(const MvParams& p, int seg) {
+  if (p.route.ids && seg < p.route.n_routed) return p.route.expert_rows;
+  return p.seg_mode == kSegRows ? p.seg_len : p.N;
+}
+
+template <int R, bool TWO, int LUTN>
 struct PassData {
   u32x4 qa[R];
   uint16_t sa[R], ba[R];
   u32x4 qb[TWO ? R : 1];
   uint16_t sb[TWO ? R : 1], bb[TWO ? R : 1];
+  uint16_t lut[LUTN > 0 ? LUTN : 1];  // LUT entries of the band, carried by its pass 0
 };
 
-// Loads one pass for the lane's R rows. qoff/soff are the byte offsets of the
-// lane's chunk (codes) and group (scales/biases) in each row for this pass;
-// ok = false turns the pass into zero loads that touch no memory.
-template <int FMT, int R, bool TWO>
+// One pass for the lane's R rows. qoff/soff are the byte offsets of the
+// lane's chunk (codes) and group (scales/biases) in each row for pass 0;
+// dq/ds move them to this pass. ok = false gives zero loads.
+template <int FMT, int R, bool TWO, int LUTN>
 __device__ __forceinline__ void load_pass(const MatRsrc& ra, const MatRsrc& rb, const uint32_t* qoff,
                                           const uint32_t* soff, uint32_t dq, uint32_t ds, bool ok,
-                                          PassData<R, TWO>& d) {
+                                          PassData<R, TWO, LUTN>& d) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t oq = ok ? qoff[r] + dq : kOOB;
@@ -357,18 +467,15 @@ __device__ __forceinline__ void load_pass(const MatRsrc& ra, const MatRsrc& rb, 
       }
     }
   }
-  // Keep the prefetch where it is: without this the compiler sinks the loads
-  // next to their first use and the next pass no longer overlaps this one.
-  asm volatile("" ::: "memory");
 }
 
-template <int BITS, int FMT, int LPR, int R, bool TWO>
-__device__ __forceinline__ void compute_pass(const PassData<R, TWO>& d, const float4* xl,
-                                             const float* xsum, int pass, int j,
+template <int BITS, int FMT, int LPR, int R, bool TWO, int LUTN>
+__device__ __forceinline__ void compute_pass(const PassData<R, TWO, LUTN>& d, const u32x4* xl,
+                                             const ChunkInfo* info, int pass, int j,
                                              const float* tabs, float* acc_a, float* acc_b) {
-  constexpr int PIECES = Codes<BITS>::kPieces;
-  float4 xr[PIECES];
-  const float4* src = xl + pass * PIECES * LPR + j;
+  constexpr int PIECES = Geo<BITS, FMT>::kPieces;
+  u32x4 xr[PIECES];
+  const u32x4* src = xl + pass * PIECES * LPR + j;
 #pragma unroll
   for (int i = 0; i < PIECES; ++i) xr[i] = src[i * LPR];
   if constexpr (FMT == 1) {
@@ -378,25 +485,34 @@ __device__ __forceinline__ void compute_pass(const PassData<R, TWO>& d, const fl
       if constexpr (TWO) acc_b[r] += dot_lut(d.qb[r], xr, tabs + (2 * r + 1) * 16);
     }
   } else {
-    const float xs = xsum[pass * LPR + j];
+    const float2 sb = *reinterpret_cast<const float2*>(&info[pass * LPR + j]);  // (xsum, back)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float da = (BITS == 4 ? dot_q4(d.qa[r], xr) : dot_q2(d.qa[r], xr)) * kTwo24;
+      const float da = (BITS == 4 ? dot_q4(d.qa[r], xr) : dot_q2(d.qa[r], xr)) * sb.y;
       acc_a[r] = fmaf(f16_bits_to_f32(d.sa[r]), da, acc_a[r]);
-      acc_a[r] = fmaf(f16_bits_to_f32(d.ba[r]), xs, acc_a[r]);
+      acc_a[r] = fmaf(f16_bits_to_f32(d.ba[r]), sb.x, acc_a[r]);
       if constexpr (TWO) {
-        const float db = (BITS == 4 ? dot_q4(d.qb[r], xr) : dot_q2(d.qb[r], xr)) * kTwo24;
+        const float db = (BITS == 4 ? dot_q4(d.qb[r], xr) : dot_q2(d.qb[r], xr)) * sb.y;
         acc_b[r] = fmaf(f16_bits_to_f32(d.sb[r]), db, acc_b[r]);
-        acc_b[r] = fmaf(f16_bits_to_f32(d.bb[r]), xs, acc_b[r]);
+        acc_b[r] = fmaf(f16_bits_to_f32(d.bb[r]), sb.x, acc_b[r]);
       }
     }
   }
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
 template <int LPR>
 __device__ __forceinline__ float lanes_sum(float v) {
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v += dpp_f32<0xb1, 0xf>(v);   // quad_perm 1,0,3,2
+  v += dpp_f32<0x4e, 0xf>(v);   // quad_perm 2,3,0,1
+  v += dpp_f32<0x141, 0xf>(v);  // row_half_mirror
+  v += dpp_f32<0x140, 0xf>(v);  // row_mirror: every lane of a row of 16 holds the row sum
+  if constexpr (LPR >= 32) v += dpp_f32<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  if constexpr (LPR >= 64) v += dpp_f32<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
@@ -408,26 +524,27 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Segment tables resolved at kernel start (routing ids are device data).
-struct SegTable {
-  QMat A[kMaxSeg];
-  QMat B[kMaxSeg];
-  int rows[kMaxSeg];  // rows of each segment's matrix
-};
-
 // ---------------------------------------------------------------------------
-template <int BITS, int FMT, int LPR, int R, int EPI, int SEG>
+// One workgroup = 8 waves; workgroup (tile t, slice s). Each wave walks its
+// bands t*8 + w, + grid_x*8, ... and within a band the passes over its K
+// slice. That (band, pass) sequence is one software pipeline DEPTH items
+// deep: the first DEPTH items are requested before x is staged, and a slot is
+// refilled with the item DEPTH ahead as soon as it has been consumed, across
+// band boundaries, so the memory queue never drains inside a wave.
+template <int BITS, int FMT, int LPR, int R, int EPI, int SEG, int DEPTH>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
-  constexpr int PIECES = Codes<BITS>::kPieces;
-  constexpr int CPC = Codes<BITS>::kPerChunk;
+  constexpr int PIECES = Geo<BITS, FMT>::kPieces;
+  constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
+  constexpr int CPG = Geo<BITS, FMT>::kChunksPerGroup;
   constexpr int SUB = 64 / LPR;
   constexpr int RPB = SUB * R;  // rows per band
   constexpr bool TWO = (EPI == kEpiSwiglu);
   constexpr int NACC = TWO ? 2 : 1;
+  constexpr int LUTN = (FMT == 1) ? (R * NACC * 16 + LPR - 1) / LPR : 0;
+  typedef PassData<R, TWO, LUTN> PD;
 
-  extern __shared__ float4 smem[];
-  __shared__ float red[kWaves];
-  __shared__ SegTable st;
+  extern __shared__ u32x4 smem[];
+  __shared__ float red[2 * kWaves];
   __shared__ int last_flag;
 
   const int slice = blockIdx.x / p.grid_x;
@@ -437,114 +554,74 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   const int nch = min(p.slice_chunks, C - c0);
   const int npass = (nch + LPR - 1) / LPR;
   const int nbands = (p.N + RPB - 1) / RPB;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPR;
   const int j = lane % LPR;
-  const int first_band = tile * kWaves;
-  if (first_band >= nbands) return;  // same for every slice of this tile: no ticket needed
-
-  if constexpr (SEG != kSegNone) {
-    if (threadIdx.x < p.nseg) {
-      const int i = threadIdx.x;
-      QMat a = p.A[i], b = p.B[i];
-      int rows = (SEG == kSegRows) ? p.seg_len : p.N;
-      if (p.route.ids && i < p.route.n_routed) {
-        const size_t e = (size_t)p.route.ids[i];
-        const size_t r0 = e * (size_t)p.route.expert_rows;
-        a.q = p.route.all_A.q + r0 * p.wpr;
-        a.s = p.route.all_A.s ? p.route.all_A.s + r0 * p.gpr : nullptr;
-        a.b = p.route.all_A.b ? p.route.all_A.b + r0 * p.gpr : nullptr;
-        a.lut = p.route.all_A.lut ? p.route.all_A.lut + r0 * 16 : nullptr;
-        b.q = p.route.all_B.q ? p.route.all_B.q + r0 * p.wpr : nullptr;
-        b.s = p.route.all_B.s ? p.route.all_B.s + r0 * p.gpr : nullptr;
-        b.b = p.route.all_B.b ? p.route.all_B.b + r0 * p.gpr : nullptr;
-        b.lut = p.route.all_B.lut ? p.route.all_B.lut + r0 * 16 : nullptr;
-        rows = p.route.expert_rows;
-      }
-      st.A[i] = a;
-      st.B[i] = b;
-      st.rows[i] = rows;
-    }
-  }
-
-  float4* xl = smem;
-  float* xsum = reinterpret_cast<float*>(smem + (size_t)npass * LPR * PIECES);
-  float* tabs_all = xsum + npass * LPR;  // LUT: [kWaves][SUB][R][2][16]
-  stage_x<BITS, FMT, LPR>(p, c0, nch, npass, xl, xsum, red);
-  __syncthreads();
-
-  float* tabs = tabs_all + (wave * SUB + sub) * R * 2 * 16;
+  if (tile * kWaves >= nbands) return;  // same for every slice of this tile: no ticket needed
   const int band_stride = p.grid_x * kWaves;
 
-  MatRsrc ra{}, rb{};
-  if constexpr (SEG == kSegNone) {
-    ra = mat_rsrc(p.A[0], p.N, p.wpr, p.gpr);
+  // ---- loader: requests (band, pass) items ahead of the compute ----------
+  int ld_band = tile * kWaves + wave, ld_pass = 0, ld_seg = 0;
+  uint32_t qoff[R], soff[R];
+  int ld_row[R];
+  MatRsrc ra, rb;
+  if constexpr (SEG != kSegRows) {
+    if constexpr (SEG == kSegNone) ra = mat_rsrc(p.A[0], p.N, p.wpr, p.gpr);
     if constexpr (TWO) rb = mat_rsrc(p.B[0], p.N, p.wpr, p.gpr);
   }
 
-  for (int band = first_band + wave; band < nbands; band += band_stride) {
-    // rows of this lane (logical) and their offsets inside their matrix
-    int seg_band = 0;
+  auto band_setup = [&](int band) {
     if constexpr (SEG == kSegRows) {
-      seg_band = (band * RPB) / p.seg_len;  // a band never straddles two segments
-      ra = mat_rsrc(st.A[seg_band], st.rows[seg_band], p.wpr, p.gpr);
-      if constexpr (TWO) rb = mat_rsrc(st.B[seg_band], st.rows[seg_band], p.wpr, p.gpr);
+      ld_seg = (band * RPB) / p.seg_len;  // a band never straddles two row segments
+      const int rows = seg_rows(p, ld_seg);
+      ra = mat_rsrc(seg_mat(p, ld_seg, false), rows, p.wpr, p.gpr);
+      if constexpr (TWO) rb = mat_rsrc(seg_mat(p, ld_seg, true), rows, p.wpr, p.gpr);
     }
-    // byte offsets of this lane's first chunk / group in each of its rows
-    constexpr int CPG = Codes<BITS>::kChunksPerGroup;
-    uint32_t qoff[R], soff[R];
-    int local_row[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = band * RPB + sub * R + r;
-      const int lr = (SEG == kSegRows) ? n - seg_band * p.seg_len : n;
-      local_row[r] = lr;
+      const int lr = (SEG == kSegRows) ? n - ld_seg * p.seg_len : n;
       const bool ok = n < p.N;
+      ld_row[r] = ok ? lr : -1;
       // chunk of pass 0; K segments add their (segment-local) chunk per pass
       const uint32_t cfirst = (SEG == kSegCols) ? 0u : (uint32_t)(c0 + j);
       qoff[r] = ok ? (uint32_t)lr * (uint32_t)p.wpr * 4u + cfirst * 16u : kOOB;
       soff[r] = ok ? (uint32_t)lr * (uint32_t)p.gpr * 2u + (cfirst / CPG) * 2u : kOOB;
     }
+  };
 
-    if constexpr (FMT == 1) {
-      // this sub-wave's row tables: [R][2][16] floats
-      wave_sync_lds();
-      for (int e = j; e < R * NACC * 16; e += LPR) {
-        const int r = e / (NACC * 16), m = (e / 16) % NACC, t = e % 16;
-        const int n = band * RPB + sub * R + r;
-        float val = 0.f;
-        if (n < p.N) {
-          const QMat M = (SEG == kSegRows) ? (m ? st.B[seg_band] : st.A[seg_band])
-                                           : (m ? p.B[0] : p.A[0]);
-          val = f16_bits_to_f32(M.lut[(size_t)local_row[r] * 16 + t]);
-        }
-        tabs[(2 * r + m) * 16 + t] = val;
-      }
-      wave_sync_lds();
-    }
-
-    float acc_a[R], acc_b[R];
+  auto issue = [&](PD& d) {
+    if (ld_band < nbands) {
+      if (ld_pass == 0) {
+        band_setup(ld_band);
+        if constexpr (FMT == 1) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc_a[r] = acc_b[r] = 0.f;
-
-    // Issues the loads of pass i into d. For K segments, the descriptors of
-    // the pass's segment are (re)built here; when a pass straddles segments
-    // (segments shorter than LPR chunks) each segment gets its own load with
-    // the other lanes pointed past the end, and the zero-filled results merge.
-    auto issue = [&](int i, PassData<R, TWO>& d) {
-      const bool ok = i < npass && i * LPR + j < nch;
+          for (int q = 0; q < LUTN; ++q) {
+            const int e = j + q * LPR;  // entry e of [R][NACC][16]
+            const int r = e / (NACC * 16), m = (e / 16) % NACC, t = e % 16;
+            uint16_t v = 0;
+            if (e < R * NACC * 16 && ld_row[r] >= 0) {
+              const QMat M = (SEG == kSegRows) ? seg_mat(p, ld_seg, m == 1) : (m ? p.B[0] : p.A[0]);
+              v = M.lut[(size_t)ld_row[r] * 16 + t];
+            }
+            d.lut[q] = v;
+          }
+        }
+      }
+      const bool ok = ld_pass * LPR + j < nch;
       if constexpr (SEG == kSegCols) {
-        const int cpass = c0 + i * LPR;
+        const int cpass = c0 + ld_pass * LPR;
         const int s_lo = min(cpass / p.seg_len, p.nseg - 1);
         const int s_hi = min((cpass + LPR - 1) / p.seg_len, p.nseg - 1);
         const int cg = cpass + j;
         if (s_lo == s_hi) {
-          ra = mat_rsrc(st.A[s_lo], st.rows[s_lo], p.wpr, p.gpr);
+          ra = mat_rsrc(seg_mat(p, s_lo, false), seg_rows(p, s_lo), p.wpr, p.gpr);
           const int cl = cg - s_lo * p.seg_len;
-          load_pass<FMT, R, TWO>(ra, rb, qoff, soff, (uint32_t)cl * 16u,
-                                 (uint32_t)(cl / CPG) * 2u, ok, d);
+          load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u,
+                                       (uint32_t)(cl / CPG) * 2u, ok, d);
         } else {
+          // several segments in one pass: one masked load per segment, merged
           const int mine = cg / p.seg_len;
 #pragma unroll
           for (int r = 0; r < R; ++r) {
@@ -552,11 +629,11 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
             d.sa[r] = d.ba[r] = 0;
           }
           for (int sg = s_lo; sg <= s_hi; ++sg) {
-            PassData<R, TWO> t;
-            ra = mat_rsrc(st.A[sg], st.rows[sg], p.wpr, p.gpr);
+            PD t;
+            ra = mat_rsrc(seg_mat(p, sg, false), seg_rows(p, sg), p.wpr, p.gpr);
             const int cl = cg - sg * p.seg_len;
-            load_pass<FMT, R, TWO>(ra, rb, qoff, soff, (uint32_t)cl * 16u,
-                                   (uint32_t)(cl / CPG) * 2u, ok && mine == sg, t);
+            load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u,
+                                         (uint32_t)(cl / CPG) * 2u, ok && mine == sg, t);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
               d.qa[r] |= t.qa[r];
@@ -566,54 +643,122 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
           }
         }
       } else {
-        load_pass<FMT, R, TWO>(ra, rb, qoff, soff, (uint32_t)(i * LPR) * 16u,
-                               (uint32_t)(i * LPR / CPG) * 2u, ok, d);
+        load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)(ld_pass * LPR) * 16u,
+                                     (uint32_t)(ld_pass * LPR / CPG) * 2u, ok, d);
       }
-    };
-
-    PassData<R, TWO> d0, d1;
-    issue(0, d0);
-    for (int i = 0; i < npass; i += 2) {
-      issue(i + 1, d1);
-      compute_pass<BITS, FMT, LPR, R, TWO>(d0, xl, xsum, i, j, tabs, acc_a, acc_b);
-      issue(i + 2, d0);
-      if (i + 1 < npass) compute_pass<BITS, FMT, LPR, R, TWO>(d1, xl, xsum, i + 1, j, tabs, acc_a, acc_b);
+      if (++ld_pass == npass) {
+        ld_pass = 0;
+        ld_band += band_stride;
+      }
+    } else {
+      load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, 0u, 0u, false, d);
     }
+    // Keep each request where it is issued: otherwise the compiler sinks the
+    // loads next to their first use and the pipeline collapses.
+    asm volatile("" ::: "memory");
+  };
 
+  u32x4* xl = smem;
+  ChunkInfo* info = reinterpret_cast<ChunkInfo*>(smem + (size_t)npass * LPR * PIECES);
+  float* tabs_all = reinterpret_cast<float*>(info + npass * LPR);  // LUT: [kWaves][SUB][R][2][16]
+  float* tabs = tabs_all + (wave * SUB + sub) * R * 2 * 16;
+
+  // x first, then the weight prefetch, then the staging arithmetic: the
+  // staging then waits for x only while the weights are in flight.
+  PD d[DEPTH];
+  const bool whole_k = (c0 == 0 && nch == C);
+  if (npass * LPR <= kThreads) {
+    XChunk<CPC> xc;
+    const int c = threadIdx.x;
+    stage_load<CPC>(p, c0 + c, c < nch, xc);
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) issue(d[k]);
+    if (c < npass * LPR) stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
+  } else {
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) issue(d[k]);
+    stage_loop<BITS, FMT, LPR>(p, c0, nch, npass, xl, info);
+  }
+  // RMSNorm scalar: applied to the row sums (W (g*x) / rms = W (g*x/rms))
+  float rs = 1.0f;
+  if (p.norm_w && !whole_k) rs = rms_all(p, red);  // contains barriers: every thread
+  __syncthreads();
+  if (p.norm_w && whole_k) rs = rms_from_chunks(p, info, C);
+
+  float acc_a[R], acc_b[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc_a[r] = acc_b[r] = 0.f;
+  int cur_band = tile * kWaves + wave, cur_pass = 0;
+
+  auto finish_band = [&](int band) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      acc_a[r] = lanes_sum<LPR>(acc_a[r]);
-      if constexpr (TWO) acc_b[r] = lanes_sum<LPR>(acc_b[r]);
+      acc_a[r] = lanes_sum<LPR>(acc_a[r]) * rs;
+      if constexpr (TWO) acc_b[r] = lanes_sum<LPR>(acc_b[r]) * rs;
     }
-    if (j == 0) {
+    if (j == LPR - 1) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int n = band * RPB + sub * R + r;
-        if (n >= p.N) continue;
-        if (p.splits > 1) {
-          p.partials[((size_t)slice * NACC) * p.N + n] = acc_a[r];
-          if constexpr (TWO) p.partials[((size_t)slice * NACC + 1) * p.N + n] = acc_b[r];
-        } else if constexpr (TWO) {
-          p.y[n] = silu(acc_a[r]) * acc_b[r];
-        } else {
-          p.y[n] = p.residual ? p.residual[n] + acc_a[r] : acc_a[r];
+        if (n < p.N) {
+          if (p.splits > 1) {
+            p.partials[((size_t)slice * NACC) * p.N + n] = acc_a[r];
+            if constexpr (TWO) p.partials[((size_t)slice * NACC + 1) * p.N + n] = acc_b[r];
+          } else if constexpr (TWO) {
+            p.y[n] = silu(acc_a[r]) * acc_b[r];
+          } else {
+            p.y[n] = p.residual ? p.residual[n] + acc_a[r] : acc_a[r];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc_a[r] = acc_b[r] = 0.f;
+  };
+
+  while (cur_band < nbands) {
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+      if (cur_band < nbands) {
+        if constexpr (FMT == 1) {
+          if (cur_pass == 0) {  // this band's row tables into the sub-wave's LDS slot
+            wave_sync_lds();
+#pragma unroll
+            for (int q = 0; q < LUTN; ++q) {
+              const int e = j + q * LPR;
+              if (e < R * NACC * 16) {
+                const int r = e / (NACC * 16), m = (e / 16) % NACC, t = e % 16;
+                tabs[(2 * r + m) * 16 + t] = f16_bits_to_f32(d[k].lut[q]);
+              }
+            }
+            wave_sync_lds();
+          }
+        }
+        compute_pass<BITS, FMT, LPR, R, TWO, LUTN>(d[k], xl, info, cur_pass, j, tabs, acc_a, acc_b);
+        issue(d[k]);
+        if (++cur_pass == npass) {
+          finish_band(cur_band);
+          cur_pass = 0;
+          cur_band += band_stride;
         }
       }
     }
   }
 
   if (p.splits > 1) {
-    // Last workgroup of this tile adds the slices in fixed order.
-    __threadfence();
+    // Last workgroup of this tile adds the slices in fixed order. Every
+    // thread's partial stores complete before the barrier; one thread then
+    // publishes them device-wide and takes the ticket.
     __syncthreads();
     if (threadIdx.x == 0) {
+      __threadfence();
       const uint32_t prev = atomicAdd(&p.tickets[tile], 1u);
       last_flag = (prev == (uint32_t)(p.splits - 1));
+      if (last_flag) __threadfence();
     }
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
-    for (int band = first_band + wave; band < nbands; band += band_stride) {
+    for (int band = tile * kWaves + wave; band < nbands; band += band_stride) {
       if (lane < RPB) {
         const int n = band * RPB + lane;
         if (n < p.N) {
@@ -642,24 +787,37 @@ __global__ void fill_u32_kernel(uint32_t* dst, size_t n, uint32_t v) {
 
 typedef void (*KernelFn)(const MvParams);
 
+template <int BITS, int FMT, int EPI, int SEG, int LPR>
+KernelFn pick_rd(int rows, int depth) {
+  if (rows == 2) return qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 2>;  // two rows: depth 2 only
+  return depth == 4 ? qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 4> : qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 2>;
+}
+
 template <int BITS, int FMT, int EPI, int SEG>
-KernelFn pick_kernel(int lpr, int rows) {
-  if (lpr == 64) return rows == 2 ? qmv_kernel<BITS, FMT, 64, 2, EPI, SEG> : qmv_kernel<BITS, FMT, 64, 1, EPI, SEG>;
-  if (lpr == 32) return rows == 2 ? qmv_kernel<BITS, FMT, 32, 2, EPI, SEG> : qmv_kernel<BITS, FMT, 32, 1, EPI, SEG>;
-  if (lpr == 16) return rows == 2 ? qmv_kernel<BITS, FMT, 16, 2, EPI, SEG> : qmv_kernel<BITS, FMT, 16, 1, EPI, SEG>;
+KernelFn pick_kernel(int lpr, int rows, int depth) {
+  if (lpr == 64) return pick_rd<BITS, FMT, EPI, SEG, 64>(rows, depth);
+  if (lpr == 32) return pick_rd<BITS, FMT, EPI, SEG, 32>(rows, depth);
+  if (lpr == 16) return pick_rd<BITS, FMT, EPI, SEG, 16>(rows, depth);
   return nullptr;
 }
 
 template <int BITS, int FMT>
-KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows) {
-  if (epi == kEpiStore) {
-    if (seg == kSegNone) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows);
-    if (seg == kSegCols) return pick_kernel<BITS, FMT, kEpiStore, kSegCols>(lpr, rows);
-  } else if (epi == kEpiSwiglu) {
-    if (seg == kSegNone) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegNone>(lpr, rows);
-    if (seg == kSegRows) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegRows>(lpr, rows);
+KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows, int depth) {
+  if constexpr (FMT == 1) {  // the LUT format is not gathered by experts
+    if (seg != kSegNone) return nullptr;
+    if (epi == kEpiStore) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows, depth);
+    if (epi == kEpiSwiglu) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegNone>(lpr, rows, depth);
+    return nullptr;
+  } else {
+    if (epi == kEpiStore) {
+      if (seg == kSegNone) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows, depth);
+      if (seg == kSegCols) return pick_kernel<BITS, FMT, kEpiStore, kSegCols>(lpr, rows, depth);
+    } else if (epi == kEpiSwiglu) {
+      if (seg == kSegNone) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegNone>(lpr, rows, depth);
+      if (seg == kSegRows) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegRows>(lpr, rows, depth);
+    }
+    return nullptr;
   }
-  return nullptr;
 }
 
 }  // namespace
@@ -667,9 +825,9 @@ KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows) {
 hipError_t launch_mv(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
                      hipStream_t stream) {
   KernelFn fn = nullptr;
-  if (bits == 4 && fmt == 0) fn = pick_kernel_epi<4, 0>(epi, p.seg_mode, plan.lpr, plan.rows);
-  else if (bits == 2 && fmt == 0) fn = pick_kernel_epi<2, 0>(epi, p.seg_mode, plan.lpr, plan.rows);
-  else if (bits == 4 && fmt == 1) fn = pick_kernel_epi<4, 1>(epi, p.seg_mode, plan.lpr, plan.rows);
+  if (bits == 4 && fmt == 0) fn = pick_kernel_epi<4, 0>(epi, p.seg_mode, plan.lpr, plan.rows, plan.depth);
+  else if (bits == 2 && fmt == 0) fn = pick_kernel_epi<2, 0>(epi, p.seg_mode, plan.lpr, plan.rows, plan.depth);
+  else if (bits == 4 && fmt == 1 && p.seg_mode == kSegNone) fn = pick_kernel_epi<4, 1>(epi, p.seg_mode, plan.lpr, plan.rows, plan.depth);
   if (!fn) return hipErrorInvalidValue;
   if (plan.lds_bytes > (size_t)kMaxLdsBytes) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(plan.grid_x * plan.splits));

@@ -191,6 +191,19 @@ int qlogits_topk(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
                  float *logits, int k, int32_t *idx, float *vals,
                  void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- bandwidth probes (measurement only) ---------------------------------
+ * The decode matvec is bound by HBM bandwidth ([F] TL;DR: time per token is
+ * about the bytes read divided by the bandwidth); these give the achievable
+ * figures to compare against. Both stream `bytes` (a multiple of 16, 16-byte
+ * aligned) with 16-byte non-temporal accesses over `blocks` workgroups of 256
+ * threads. qg_probe_read reads src once and writes one uint32 per thread to
+ * out (out must hold blocks*256 entries); flags bit 0 = ordinary (cached)
+ * loads instead of non-temporal ones. qg_probe_copy copies src to dst (no
+ * overlap). QG_EINVAL on bad arguments. */
+int qg_probe_read(const void *src, size_t bytes, uint32_t *out, int blocks, int flags,
+                  hipStream_t stream);
+int qg_probe_copy(void *dst, const void *src, size_t bytes, int blocks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
