@@ -35,7 +35,7 @@ METRIC = "achieved HBM GB/s (% of roofline) for 4-bit group-64 GEMV; equiv decod
 HBM_PEAK_GBS = 8000.0
 EPS = 1e-5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qswiglu_llama3_8b.json")
-KERNEL_SOURCES = ["qg_mv.hip", "qg_internal.h"]
+KERNEL_SOURCES = ["qg_mv.hip", "qg_common.h", "qg_internal.h"]
 
 
 def log(msg):

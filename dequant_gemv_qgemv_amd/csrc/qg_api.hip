@@ -187,6 +187,70 @@ size_t mv_ws_bytes(int N, int M, int epi) {
   return tickets_al + (size_t)kMaxSplits * (epi == kEpiSwiglu ? 2 : 1) * M * N * 4;
 }
 
+// Extra requirements of the M = 2..8 kernels: each wave loads whole
+// 512-code ranges of a row's scales/biases (or its table) with 16-byte loads.
+int check_mm(const qg_qmat* A, const qg_qmat* B, int K, int fmt) {
+  if (K % 512) return QG_EUNSUPPORTED;
+  const qg_qmat* mats[2] = {A, B};
+  for (const qg_qmat* W : mats) {
+    if (!W) continue;
+    if (fmt == QG_AFFINE && (!aligned(W->scales, 16) || !aligned(W->biases, 16)))
+      return QG_EUNSUPPORTED;
+    if (fmt == QG_LUT && !aligned(W->lut, 16)) return QG_EUNSUPPORTED;
+  }
+  return QG_OK;
+}
+
+// M = 2..8: matrix-core kernels. K is cut into slices of mm_slice_codes()
+// codes (one workgroup each per band set); more than one slice needs the
+// workspace for the fp32 partials.
+int run_mm(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int bits, int fmt, int epi,
+           const void* x, int x_dtype, const uint16_t* norm_w, float eps, const float* residual,
+           float* y, void* ws, bool have_ws, int cus, hipStream_t stream) {
+  const int slice = mm_slice_codes();
+  const int splits = (K + slice - 1) / slice;
+  if (splits > 1 && !have_ws) return QG_EWORKSPACE;
+  const int nbands = (N + 15) / 16;
+  // one 8-wave workgroup per compute unit: the waves hold their activations
+  // and two to four bands of codes in registers
+  const int wg_per_cu = g_knob[3].load() ? g_knob[3].load() : 1;
+  int gx = nbands;
+  const int cap = (cus * wg_per_cu + splits - 1) / splits;
+  if (gx > cap) gx = cap;
+  gx = ((gx + 7) / 8) * 8;  // slices of one tile share an XCD
+  MvPlan pl{};
+  pl.splits = splits;
+  pl.grid_x = gx;
+  MvParams p;
+  memset(&p, 0, sizeof(p));
+  p.A[0] = to_dev(A);
+  p.B[0] = to_dev(B);
+  p.nseg = 1;
+  p.seg_mode = kSegNone;
+  p.N = N;
+  p.K = K;
+  p.M = M;
+  p.wpr = K * bits / 32;
+  p.gpr = K / 64;
+  p.x = x;
+  p.x_f32 = x_dtype == QG_F32;
+  p.norm_w = norm_w;
+  p.eps = eps;
+  p.residual = residual;
+  p.y = y;
+  p.splits = splits;
+  p.slice_chunks = slice / (128 / bits);
+  p.grid_x = gx;
+  if (splits > 1) {
+    const size_t tickets = ((size_t)(N + 7) / 8 + 64) * 4;
+    const size_t tickets_al = (tickets + 255) / 256 * 256;
+    p.tickets = static_cast<uint32_t*>(ws);
+    p.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + tickets_al);
+  }
+  const hipError_t e = launch_mm(bits, fmt, epi, pl, p, stream);
+  return e == hipSuccess ? QG_OK : QG_ELAUNCH;
+}
+
 int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, int bits, int fmt,
            int epi, const void* x, int x_dtype, const uint16_t* norm_w, float eps,
            const float* residual, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -201,11 +265,14 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   const size_t ybytes = (size_t)M * N * 4;
   if (overlaps(x, xbytes, y, ybytes)) return QG_EINVAL;
   if (residual && residual != y && overlaps(residual, ybytes, y, ybytes)) return QG_EINVAL;
-  if (M != 1) return QG_EUNSUPPORTED;
+  if (M > 1 && (rc = check_mm(A, epi == kEpiSwiglu ? B : nullptr, K, fmt))) return rc;
   if (N == 0) return QG_OK;
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;
   const bool have_ws = ws && ws_bytes >= mv_ws_bytes(N, M, epi) && aligned(ws, 256);
+  if (M > 1)
+    return run_mm(A, B, N, K, M, bits, fmt, epi, x, x_dtype, norm_w, eps, residual, y, ws,
+                  have_ws, dev.cus, stream);
   const MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0}, dev.cus, have_ws);
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;  // K too long for one slice: needs ws
   MvParams p;
@@ -219,6 +286,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   p.K = K;
   p.wpr = K * bits / 32;
   p.gpr = K / 64;
+  p.M = 1;
   p.x = x;
   p.x_f32 = x_dtype == QG_F32;
   p.norm_w = norm_w;

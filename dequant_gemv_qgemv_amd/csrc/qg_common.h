@@ -1,0 +1,185 @@
+// qg_common.h -- device helpers shared by the matvec (M = 1) and the small-M
+// MFMA kernels: fp16 bit helpers, the staging geometry and permuted fp16
+// staging of x, activation loads, the per-chunk power-of-two range scale,
+// buffer descriptors over one matrix, and small wave utilities.
+#pragma once
+
+#include "qg_internal.h"
+
+namespace qg {
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t v) {
+  return (float)__builtin_bit_cast(_Float16, v);
+}
+
+constexpr int kMaxLdsBytes = 64 * 1024;
+
+// Per-format staging geometry: codes per 16-byte chunk, 16-byte pieces of
+// staged x per chunk, chunks per group of 64.
+template <int BITS, int FMT>
+struct Geo;
+template <>
+struct Geo<4, 0> {  // 32 codes; x as 16 fp16 pairs = 4 pieces
+  static constexpr int kPerChunk = 32, kPieces = 4, kChunksPerGroup = 2;
+};
+template <>
+struct Geo<2, 0> {  // 64 codes; x as 32 fp16 pairs = 8 pieces
+  static constexpr int kPerChunk = 64, kPieces = 8, kChunksPerGroup = 1;
+};
+template <>
+struct Geo<4, 1> {  // LUT: 32 codes; x as 32 fp32 = 8 pieces
+  static constexpr int kPerChunk = 32, kPieces = 8, kChunksPerGroup = 2;
+};
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const uint32_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
+  const uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
+  return a | (b << 16);
+}
+
+// Writes the staged pieces of one chunk: v holds the chunk's x already
+// multiplied by the range scale (affine) or as is (LUT).
+template <int BITS, int FMT>
+__device__ __forceinline__ void write_pieces(const float* v, u32x4* dst, int stride) {
+  if constexpr (FMT == 1) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      dst[p * stride] = u32x4{__float_as_uint(v[4 * p]), __float_as_uint(v[4 * p + 1]),
+                              __float_as_uint(v[4 * p + 2]), __float_as_uint(v[4 * p + 3])};
+  } else if constexpr (BITS == 4) {
+    constexpr float r16 = 1.0f / 16.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* w = v + 8 * i;
+      dst[i * stride] = u32x4{pack_f16(w[0], w[4]), pack_f16(w[1] * r16, w[5] * r16),
+                              pack_f16(w[2], w[6]), pack_f16(w[3] * r16, w[7] * r16)};
+    }
+  } else {
+    constexpr float r4 = 0.25f, r16 = 1.0f / 16.0f, r64 = 1.0f / 64.0f, r256 = 1.0f / 256.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* w = v + 16 * i;
+      dst[(2 * i) * stride] = u32x4{pack_f16(w[0], w[8]), pack_f16(w[1] * r4, w[9] * r4),
+                                    pack_f16(w[2] * r16, w[10] * r16),
+                                    pack_f16(w[3] * r64, w[11] * r64)};
+      dst[(2 * i + 1) * stride] = u32x4{pack_f16(w[4] * r256, w[12] * r256), pack_f16(w[5], w[13]),
+                                        pack_f16(w[6] * r4, w[14] * r4),
+                                        pack_f16(w[7] * r16, w[15] * r16)};
+    }
+  }
+}
+
+// Loads n consecutive activations starting at element k0 as fp32.
+template <int n>
+__device__ __forceinline__ void load_x(const void* x, int x_f32, int k0, float* v) {
+  if (x_f32) {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(x) + k0);
+#pragma unroll
+    for (int i = 0; i < n / 4; ++i) {
+      const float4 t = src[i];
+      v[4 * i] = t.x;
+      v[4 * i + 1] = t.y;
+      v[4 * i + 2] = t.z;
+      v[4 * i + 3] = t.w;
+    }
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + k0);
+#pragma unroll
+    for (int i = 0; i < n / 8; ++i) {
+      const uint4 t = src[i];
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x2 h = as_f16x2(w[j]);
+        v[8 * i + 2 * j] = (float)h.x;
+        v[8 * i + 2 * j + 1] = (float)h.y;
+      }
+    }
+  }
+}
+
+template <int n>
+__device__ __forceinline__ void load_f16(const uint16_t* src16, int k0, float* v) {
+  const uint4* src = reinterpret_cast<const uint4*>(src16 + k0);
+#pragma unroll
+  for (int i = 0; i < n / 8; ++i) {
+    const uint4 t = src[i];
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x2 h = as_f16x2(w[j]);
+      v[8 * i + 2 * j] = (float)h.x;
+      v[8 * i + 2 * j + 1] = (float)h.y;
+    }
+  }
+}
+
+// Power-of-two range scale for the fp16 staging of one chunk: with m = max|x|
+// over the chunk, x * 2^-e stays below 2^14; returns 2^-e and sets
+// *back = 2^(24+e), which also undoes the 2^-24 of the subnormal codes.
+__device__ __forceinline__ float range_scale(float m, float* back) {
+  int E = 0;
+  if (m > 0.f && m < INFINITY) frexpf(m, &E);
+  const int e = (m > 0.f && m < INFINITY) ? E - 14 : 0;
+  *back = ldexpf(1.0f, 24 + e);
+  return ldexpf(1.0f, -e);
+}
+
+// Per-chunk staging record next to the staged x: the chunk's sum of x (for
+// the bias term), the factor 2^(24+e) that undoes the chunk's range scale and
+// the subnormal code scale, and the chunk's sum of squares of the raw x (for
+// the RMSNorm).
+struct ChunkInfo {
+  float xsum, back, ss, pad;
+};
+
+// ---------------------------------------------------------------------------
+// Loads through buffer descriptors. A descriptor covers one matrix (or one
+// expert's rows); loads at offsets past its end return zero without touching
+// memory, which handles the last band's missing rows, padding chunks and the
+// prefetch past the last item without branches.
+
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every descriptor's end
+
+struct MatRsrc {
+  __amdgpu_buffer_rsrc_t q, s, b;
+};
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(p)), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Descriptors for `rows` rows of matrix M (codes, scales, biases).
+__device__ __forceinline__ MatRsrc mat_rsrc(const QMat& M, int rows, int wpr, int gpr) {
+  MatRsrc r;
+  r.q = make_rsrc(M.q, (uint32_t)rows * (uint32_t)wpr * 4u);
+  r.s = make_rsrc(M.s ? (const void*)M.s : (const void*)M.q, M.s ? (uint32_t)rows * (uint32_t)gpr * 2u : 0u);
+  r.b = make_rsrc(M.b ? (const void*)M.b : (const void*)M.q, M.b ? (uint32_t)rows * (uint32_t)gpr * 2u : 0u);
+  return r;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+
+}  // namespace
+}  // namespace qg

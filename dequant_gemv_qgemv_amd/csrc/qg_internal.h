@@ -52,6 +52,7 @@ struct MvParams {
   int seg_len;        // rows (kSegRows) or chunks (kSegCols) per segment
   int N;              // logical rows
   int K;              // logical columns (sum over K segments)
+  int M;              // activation vectors (x is [M][K], y is [M][N])
   int wpr;            // uint32 words per row of each underlying matrix
   int gpr;            // groups of 64 per row of each underlying matrix
   const void* x;      // [K] activations (fp16 or fp32)
@@ -82,6 +83,12 @@ struct MvPlan {
 
 hipError_t launch_mv(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
                      hipStream_t stream);
+
+// Small-M (2..8) matrix-core kernels: plain / normed store, SwiGLU; one
+// matrix (seg_mode kSegNone). K slices of mm_slice_codes() codes.
+hipError_t launch_mm(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
+                     hipStream_t stream);
+int mm_slice_codes();
 
 // Fill kernel (graph-safe replacement for hipMemsetAsync).
 hipError_t launch_fill_u32(uint32_t* dst, size_t n, uint32_t value, hipStream_t stream);

@@ -97,6 +97,7 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
   // 2. gate.up SwiGLU over the chosen experts' rows (+ shared)
   MvParams p;
   memset(&p, 0, sizeof(p));
+  p.M = 1;
   p.nseg = nseg;
   p.seg_mode = kSegRows;
   p.seg_len = F;

@@ -54,6 +54,11 @@
  *    same inputs gives bitwise the same outputs (no floating-point atomics).
  *  - Alignment: q and x must be 16-byte aligned; fp16 arrays 2-byte aligned;
  *    fp32 arrays 4-byte aligned. Otherwise QG_EINVAL.
+ *  - Several activation vectors (M = 2..8; qgemv, qgemv_rmsnorm, qswiglu)
+ *    run on the matrix cores ([F] section 1: the dispatcher's choice by M).
+ *    They additionally need K % 512 == 0 and 16-byte aligned scales/biases
+ *    (affine) or lut (LUT format); otherwise QG_EUNSUPPORTED. With
+ *    K > 4096 they need the workspace (QG_EWORKSPACE without it).
  *  - Workspace: calls that need scratch device memory take (ws, ws_bytes);
  *    qg_workspace_bytes() sizes it. The caller allocates it once, clears it
  *    once with qg_workspace_init(), and may then reuse it for every call on
@@ -76,7 +81,9 @@ extern "C" {
 #define QG_OK 0
 #define QG_EINVAL (-1)        /* NULL required pointer, bad size, misalignment, bad aliasing */
 #define QG_EUNSUPPORTED (-2)  /* valid but not provided: group != 64, bits not 2/4, LUT with
-                                 bits != 4, M outside [1,8], K or k beyond the limits below */
+                                 bits != 4, M outside [1,8], K or k beyond the limits below,
+                                 M > 1 with K % 512 != 0 or scales/biases/lut not 16-byte
+                                 aligned */
 #define QG_EWORKSPACE (-3)    /* ws NULL or smaller than qg_workspace_bytes() */
 #define QG_ELAUNCH (-4)       /* the HIP runtime reported an error while enqueueing */
 #define QG_EDEVICE (-5)       /* no usable gfx950 device for the current HIP device */

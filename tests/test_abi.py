@@ -86,6 +86,10 @@ def call_gemv(L, W=None, N=64, K=128, M=1, group=64, bits=4, fmt=0, x=X, xdt=1, 
     (dict(y=ctypes.c_void_p(0x10000 + 64)), qg.QG_EINVAL),      # y overlaps x
     (dict(res=ctypes.c_void_p(0x80000000 + 4)), qg.QG_EINVAL),  # residual partly overlaps y
     (dict(N=1 << 20, K=8192), qg.QG_EUNSUPPORTED),              # matrix over 2^31 bytes
+    (dict(M=2, K=576), qg.QG_EUNSUPPORTED),                     # M > 1 needs K % 512 == 0
+    (dict(M=2, K=512, W=_mat(s=0x2002)), qg.QG_EUNSUPPORTED),   # ... and 16-byte aligned scales
+    (dict(M=2, K=512, W=_mat(b=0x3008)), qg.QG_EUNSUPPORTED),   # ... and biases
+    (dict(M=2, K=512, fmt=1, W=_mat(s=0, b=0, lut=0x4008)), qg.QG_EUNSUPPORTED),  # ... and lut
 ])
 def test_qgemv_rejects_before_launch(L, kw, status):
     assert call_gemv(L, **kw) == status
