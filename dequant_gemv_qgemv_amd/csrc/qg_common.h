@@ -172,6 +172,20 @@ __device__ __forceinline__ MatRsrc mat_rsrc(const QMat& M, int rows, int wpr, in
   return r;
 }
 
+// Makes every workgroup fetch the launch parameters it needs first in one
+// round of scalar loads. Without it the compiler sinks part of them below the
+// first data-dependent branch, and a second dependent round trip to the
+// argument buffer (a scalar-cache miss, ~0.6 us) precedes the first weight load.
+__device__ __forceinline__ void params_now(const MvParams& p) {
+  asm volatile("" ::"s"(p.N), "s"(p.K), "s"(p.M), "s"(p.wpr), "s"(p.gpr), "s"(p.grid_x),
+               "s"(p.splits), "s"(p.slice_chunks), "s"(p.x_f32), "s"(p.nseg), "s"(p.seg_mode),
+               "s"(p.seg_len), "s"(p.eps), "s"((uint64_t)p.x), "s"((uint64_t)p.norm_w),
+               "s"((uint64_t)p.y), "s"((uint64_t)p.residual), "s"((uint64_t)p.A[0].q),
+               "s"((uint64_t)p.A[0].s), "s"((uint64_t)p.A[0].b), "s"((uint64_t)p.A[0].lut),
+               "s"((uint64_t)p.B[0].q), "s"((uint64_t)p.B[0].s), "s"((uint64_t)p.B[0].b),
+               "s"((uint64_t)p.B[0].lut), "s"((uint64_t)p.partials), "s"((uint64_t)p.tickets));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ void wave_sync_lds() {

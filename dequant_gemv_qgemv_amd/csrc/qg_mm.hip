@@ -11,12 +11,14 @@
 //
 // Work split. A workgroup (8 waves) owns a K slice of 8 x 512 codes and a set
 // of 16-row bands; wave w owns 512 consecutive codes of the slice. Its share
-// of X (M x 512 values, as fp16 MFMA operands) is staged once into registers,
-// so the inner loop reads no activations at all. For each band the wave
-// streams its 16 x 512 codes (one 16-byte load per lane per item of four
-// chunks), turns the loads into B operands with a 4 x 4 exchange across the
-// four 16-lane rows (v_permlane32_swap / v_permlane16_swap, no LDS), and
-// issues one MFMA per 32 codes. The eight waves' results for a band are summed
+// of X (M x 512 values) is converted once, spread evenly over the wave's 64
+// lanes, and handed through LDS into registers as fp16 MFMA operands, so the
+// inner loop reads no activations at all. For each band the wave
+// streams its 16 x 512 codes in loads of 8 rows x 128 bytes (whole cache
+// lines), regroups them with a DPP half-row rotation and a 4 x 4 exchange
+// across the four 16-lane rows (v_permlane32_swap / v_permlane16_swap, no
+// LDS) so that each lane holds one row's words, and issues one MFMA per 32
+// codes. The eight waves' results for a band are summed
 // in LDS in a fixed order. K longer than one slice is split across
 // workgroups, combined by the last one to finish (integer ticket).
 //
@@ -85,6 +87,11 @@ __device__ __forceinline__ void cross_rows_4x4(uint32_t& w0, uint32_t& w1, uint3
   w3 = d[1];
 }
 
+// The value of lane (i + 8) % 16 of the same 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ uint32_t row_ror8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+}
+
 // B operand of step h for one code word (affine formats): eight fp16 code
 // values code*2^-24 (times 16^j / 4^j where the mask leaves them shifted), in
 // the order the activation operand is staged.
@@ -113,49 +120,80 @@ __device__ __forceinline__ f16x8 lut_operand(uint32_t w, const uint16_t* t) {
   return f16x8_of(d[0], d[1], d[2], d[3]);
 }
 
-// Activation operand(s) of one 64-code group, from 16 values v (this lane's
-// share, already multiplied by 2^-e_g): 4-bit and table format hold elements
-// 8q..8q+7 of two chunks; 2-bit holds elements 16q..16q+15 of one chunk.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 4 lanes of a quad (every lane gets the same bits).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+  return v + dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+}
+// Max over the 32 lanes of each wave half (rows 0-1, rows 2-3).
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v));  // row_mirror
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+// Sum over the 32 lanes of each wave half; exact in lane 0 / 32 of the half.
+__device__ __forceinline__ float half_sum(float v) {
+  v = quad_sum(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// The two operand pieces of one conversion job (16 activations of one group,
+// already scaled): 4-bit and table format: elements 8q'..8q'+7 of one chunk for
+// two consecutive q'; 2-bit: steps 0 and 1 of one q.
 template <int BITS, int FMT>
-__device__ __forceinline__ void group_operands(const float* v, f16x8* dst) {
+__device__ __forceinline__ void job_pieces(const float* v, u32x4* out) {
   if constexpr (FMT == 1) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const float* u = v + 8 * c;
-      dst[c] = f16x8_of(pack_f16(u[0], u[1]), pack_f16(u[2], u[3]), pack_f16(u[4], u[5]),
-                        pack_f16(u[6], u[7]));
+      out[c] = u32x4{pack_f16(u[0], u[1]), pack_f16(u[2], u[3]), pack_f16(u[4], u[5]),
+                     pack_f16(u[6], u[7])};
     }
   } else if constexpr (BITS == 4) {
     constexpr float r16 = 1.0f / 16.0f;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const float* u = v + 8 * c;
-      dst[c] = f16x8_of(pack_f16(u[0], u[4]), pack_f16(u[1] * r16, u[5] * r16),
-                        pack_f16(u[2], u[6]), pack_f16(u[3] * r16, u[7] * r16));
+      out[c] = u32x4{pack_f16(u[0], u[4]), pack_f16(u[1] * r16, u[5] * r16),
+                     pack_f16(u[2], u[6]), pack_f16(u[3] * r16, u[7] * r16)};
     }
   } else {
     constexpr float r4 = 0.25f, r16 = 1.0f / 16.0f, r64 = 1.0f / 64.0f, r256 = 1.0f / 256.0f;
-    dst[0] = f16x8_of(pack_f16(v[0], v[8]), pack_f16(v[1] * r4, v[9] * r4),
-                      pack_f16(v[2] * r16, v[10] * r16), pack_f16(v[3] * r64, v[11] * r64));
-    dst[1] = f16x8_of(pack_f16(v[4] * r256, v[12] * r256), pack_f16(v[5], v[13]),
-                      pack_f16(v[6] * r4, v[14] * r4), pack_f16(v[7] * r16, v[15] * r16));
+    out[0] = u32x4{pack_f16(v[0], v[8]), pack_f16(v[1] * r4, v[9] * r4),
+                   pack_f16(v[2] * r16, v[10] * r16), pack_f16(v[3] * r64, v[11] * r64)};
+    out[1] = u32x4{pack_f16(v[4] * r256, v[12] * r256), pack_f16(v[5], v[13]),
+                   pack_f16(v[6] * r4, v[14] * r4), pack_f16(v[7] * r16, v[15] * r16)};
   }
 }
-
-// Materializes a value in registers at this point (keeps the compiler from
-// carrying the fp32 inputs of a packed operand further down).
-__device__ __forceinline__ void pin(f16x8& v) {
-  u32x4 u = __builtin_bit_cast(u32x4, v);
-  asm volatile("" : "+v"(u));
-  v = __builtin_bit_cast(f16x8, u);
-}
-
-__device__ __forceinline__ float xor_lanes(float v, int mask) { return __shfl_xor(v, mask, 64); }
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+// Operand index within the half range (P) and lane row (q) of a job's two
+// pieces, for group gl (0..3 within the half) and quarter r.
+template <int BITS, int FMT>
+__device__ __forceinline__ void job_slots(int gl, int r, int* P0, int* q0, int* P1, int* q1) {
+  if constexpr (BITS == 2 && FMT == 0) {  // chunk = group; steps 0, 1 of row r
+    *P0 = 2 * gl;
+    *P1 = 2 * gl + 1;
+    *q0 = *q1 = r;
+  } else {  // chunk 2gl + r/2; rows 2(r&1), 2(r&1)+1
+    *P0 = *P1 = 2 * gl + (r >> 1);
+    *q0 = 2 * (r & 1);
+    *q1 = *q0 + 1;
+  }
 }
 
 // Exponent e with max|x| * 2^-e in [2^13, 2^14), or kNoExp for an all-zero range.
@@ -180,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
   using G = MmGeo<BITS, FMT>;
   constexpr int CODES = G::kCodes, STEPS = G::kSteps, CPG = G::kCPG;
   constexpr int KW = kGW * CPG;  // chunks per wave range
-  constexpr int IPB = KW / 4;    // items (4 chunks) per band
+  constexpr int NLI = KW / 8;    // line items (8 chunks = one 128-byte line per row) per band
   constexpr int NACC = EPI == kEpiSwiglu ? 2 : 1;
   constexpr bool LUT = FMT == 1;
   constexpr int BACK_BIAS = LUT ? 0 : 24;
@@ -190,9 +228,12 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
   __shared__ float red[2][NACC][kWaves][kTok][kBand];
   __shared__ float ssq[kWaves][kTok];
   __shared__ float bk[kWaves][kTok];
+  __shared__ float xsq[kWaves][kTok][kGW];       // group sums of x per token
+  __shared__ u32x4 xst[kWaves][8 * 4 * kTok];    // staged pieces, half a range
   __shared__ uint16_t luts[LUT ? kWaves : 1][kBand * kLutStride];
   __shared__ int last_flag;
 
+  params_now(p);
   const int slice = blockIdx.x / p.grid_x;
   const int tile = blockIdx.x - slice * p.grid_x;
   const int nbands = (p.N + kBand - 1) / kBand;
@@ -218,18 +259,25 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
 
   // ---- loads ----------------------------------------------------------------
   // DB bands in flight per wave, in a ring of slots indexed at compile time.
-  u32x4 cq[NACC][DB][IPB];   // codes: one 16-byte chunk per lane per item
+  u32x4 cq[NACC][DB][NLI][2];  // codes: two 16-byte chunks per lane per line item
   uint32_t sq[NACC][DB][4];  // scales of groups gw0..gw0+7 of the lane's row (8 halves)
   uint32_t bq[NACC][DB][2];  // biases of groups gw0+4q..gw0+4q+3 (rows q < 2), or
                              // table entries 4q..4q+3 of the row (table format)
   const bool range_ok = gw0 < p.gpr;  // wave-uniform: this wave has codes in this slice
 
+  // Line item it of a band: chunks 8it..8it+7 of the 16 rows, in two loads of
+  // 8 rows x 128 bytes (whole cache lines; 16 rows x 64 bytes per load halves
+  // the achieved bandwidth). In load h, lane (q, col) takes row 8h + col % 8,
+  // chunk 4 * (col / 8) + q of the line.
   auto issue_item = [&](int band, int it, int a, int d) {
-    const int ch = cw0 + 4 * it + q;
+    const int ch = cw0 + 8 * it + 4 * (col >> 3) + q;
     const bool ok = band < nbands && ch < C;
-    const uint32_t n = (uint32_t)(band * kBand + col);
-    const uint32_t off = ok ? n * (uint32_t)p.wpr * 4u + (uint32_t)ch * 16u : kOOB;
-    cq[a][d][it] = __builtin_amdgcn_raw_buffer_load_b128(rs_[a].q, off, 0, 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t n = (uint32_t)(band * kBand + 8 * h + (col & 7));
+      const uint32_t off = ok ? n * (uint32_t)p.wpr * 4u + (uint32_t)ch * 16u : kOOB;
+      cq[a][d][it][h] = __builtin_amdgcn_raw_buffer_load_b128(rs_[a].q, off, 0, 2);
+    }
   };
   auto issue_rowdata = [&](int band, int a, int d) {
     const bool okb = band < nbands;
@@ -252,131 +300,141 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
   };
   auto issue_band = [&](int band, int a, int d) {
 #pragma unroll
-    for (int it = 0; it < IPB; ++it) issue_item(band, it, a, d);
+    for (int it = 0; it < NLI; ++it) issue_item(band, it, a, d);
     issue_rowdata(band, a, d);
   };
 
   int band = tile;
+
+  // ---- stage this wave's share of X (M x 512 activations) ---------------------
+  // Conversion jobs: (token t, group g, quarter r) = 16 activations, elements
+  // 16r..16r+15 of group g of this wave's range. Job 32t + 4g + r runs on lane
+  // (32t + 4g + r) % 64 in round t / 2: a group's quarters sit on one quad and a
+  // token's eight groups on 32 lanes, so the group sums and the token maximum
+  // are DPP / row-swap reductions, and the work grows with M only.
+  const int jt = lane >> 5, jg = (lane >> 2) & 7, jr = lane & 3;
+  u32x4 pc[kTok / 2][2];  // converted pieces of each round's job
+  const int k0 = (gw0 + jg) * 64 + 16 * jr;  // the job's first column (same in every round)
+  const bool gok = gw0 + jg < p.gpr;
+  // every round's activation loads first: one memory round trip for the range
+  float v[kTok / 2][16];
+  float gv[16];
+  if (norm && gok) {
+    load_f16<8>(p.norm_w, k0, gv);
+    load_f16<8>(p.norm_w, k0 + 8, gv + 8);
+  }
+#pragma unroll
+  for (int rd = 0; rd < kTok / 2; ++rd) {
+    const int t = 2 * rd + jt;
+    if (2 * rd < M && t < M && gok) {
+      const char* xt = static_cast<const char*>(p.x) + (size_t)t * p.K * (p.x_f32 ? 4 : 2);
+      load_x<8>(xt, p.x_f32, k0, v[rd]);
+      load_x<8>(xt, p.x_f32, k0 + 8, v[rd] + 8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[rd][i] = 0.f;
+    }
+  }
+  // then the first bands' codes: they stream in while the activations, which
+  // return first, are converted
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int a = 0; a < NACC; ++a) issue_band(band + d * p.grid_x, a, d);
   asm volatile("" ::: "memory");
-
-  // ---- stage this wave's share of X into registers --------------------------
-  // Lane (q, col) holds token col; for group g its 16 values are elements
-  // 8q..8q+7 of chunks 2g, 2g+1 (4-bit, table) or 16q..16q+15 of chunk g (2-bit).
-  f16x8 xa[KW * STEPS];
-  float gsum[kGW];
-  int ge[kGW];
-  float ssum = 0.f;
-  const bool tok_ok = col < M;
-  const char* xrow = static_cast<const char*>(p.x) + (size_t)(tok_ok ? col : 0) * p.K * (p.x_f32 ? 4 : 2);
 #pragma unroll
-  for (int g = 0; g < kGW; ++g) {
-    float v[16];
-    const bool ok = tok_ok && gw0 + g < p.gpr;
-    int k0[2];
-    if constexpr (BITS == 2 && !LUT) {
-      k0[0] = (gw0 + g) * 64 + 16 * q;
-      k0[1] = k0[0] + 8;
-    } else {
-      k0[0] = (cw0 + 2 * g) * 32 + 8 * q;
-      k0[1] = k0[0] + 32;
-    }
-    if (ok) {
-      load_x<8>(xrow, p.x_f32, k0[0], v);
-      load_x<8>(xrow, p.x_f32, k0[1], v + 8);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0.f;
-    }
+  for (int rd = 0; rd < kTok / 2; ++rd) {
+    pc[rd][0] = pc[rd][1] = u32x4{0u, 0u, 0u, 0u};
+    if (2 * rd >= M) continue;  // wave-uniform
+    const int t = 2 * rd + jt;
     if (norm) {
-      float gv[16];
-      if (ok) {
-        load_f16<8>(p.norm_w, k0[0], gv);
-        load_f16<8>(p.norm_w, k0[1], gv + 8);
-      }
+      float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        ssum = fmaf(v[i], v[i], ssum);
-        if (ok) v[i] *= gv[i];
+        ss = fmaf(v[rd][i], v[rd][i], ss);
+        v[rd][i] *= gok ? gv[i] : 0.f;
       }
+      ss = half_sum(ss);  // over the token's 32 lanes
+      if ((lane & 31) == 0 && t < M) ssq[wave][t] = ss;
     }
-    float s = 0.f, m = 0.f;
+    float sm = 0.f, mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s += v[i];
-      m = fmaxf(m, fabsf(v[i]));
+      sm += v[rd][i];
+      mx = fmaxf(mx, fabsf(v[rd][i]));
     }
-    s += xor_lanes(s, 16);
-    s += xor_lanes(s, 32);
-    m = fmaxf(m, xor_lanes(m, 16));
-    m = fmaxf(m, xor_lanes(m, 32));
-    gsum[g] = s;
-    ge[g] = range_exp(m);
-    const float inv = ldexpf(1.0f, ge[g] == kNoExp ? 0 : -ge[g]);
+    sm = quad_sum(sm);
+    mx = half_max(mx);
+    int E = range_exp(mx);
+    if (E == kNoExp) E = 0;
+    if (jr == 0 && t < M) xsq[wave][t][jg] = sm;
+    if ((lane & 31) == 0 && t < M) bk[wave][t] = ldexpf(1.0f, BACK_BIAS + E);
+    const float inv = ldexpf(1.0f, -E);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] *= inv;
-    group_operands<BITS, FMT>(v, &xa[g * 2]);
-    pin(xa[g * 2]);
-    pin(xa[g * 2 + 1]);
-    if (g & 1) asm volatile("" ::: "memory");  // bound the loads in flight
+    for (int i = 0; i < 16; ++i) v[rd][i] *= inv;
+    job_pieces<BITS, FMT>(v[rd], pc[rd]);
   }
-  // one exponent per token over the range: rescale each group's operands by
-  // 2^(e_g - E) (a power of two <= 1, exact unless it drops into subnormals)
-  int E = kNoExp;
+  // pieces -> LDS -> operands, one half of the range (groups 0-3, then 4-7) at a
+  // time: operand P of lane (q, col) is piece (P, q) of token col
+  f16x8 xa[KW * STEPS];
+  u32x4* xs = xst[wave];
+  const int lane_half = jg >> 2;
 #pragma unroll
-  for (int g = 0; g < kGW; ++g) E = max(E, ge[g]);
-  if (E == kNoExp) E = 0;
+  for (int hf = 0; hf < 2; ++hf) {
+    wave_sync_lds();
 #pragma unroll
-  for (int g = 0; g < kGW; ++g) {
-    const int d = ge[g] == kNoExp ? 0 : ge[g] - E;
-    if (d != 0) {
-      const _Float16 f = (_Float16)ldexpf(1.0f, max(d, -30));
-      xa[2 * g] *= f;
-      xa[2 * g + 1] *= f;
+    for (int rd = 0; rd < kTok / 2; ++rd) {
+      const int t = 2 * rd + jt;
+      if (2 * rd < M && t < M && lane_half == hf) {
+        int P0, q0, P1, q1;
+        job_slots<BITS, FMT>(jg & 3, jr, &P0, &q0, &P1, &q1);
+        xs[(P0 * 4 + q0) * kTok + t] = pc[rd][0];
+        xs[(P1 * 4 + q1) * kTok + t] = pc[rd][1];
+      }
+    }
+    wave_sync_lds();
+#pragma unroll
+    for (int P = 0; P < 8; ++P) {
+      const u32x4 u = col < M ? xs[(P * 4 + q) * kTok + col] : u32x4{0u, 0u, 0u, 0u};
+      xa[hf * 8 + P] = __builtin_bit_cast(f16x8, u);
     }
   }
+  wave_sync_lds();
   // bias operand: lane row q < 2 carries groups 4q..4q+3 as (hi, lo) pairs of
   // sum_x * 2^-(24+E), the units of D
   f16x8 xb = f16x8_of(0u, 0u, 0u, 0u);
   if constexpr (!LUT) {
-    uint32_t d[4];
+    if (q < 2 && col < M) {
+      const float binv = 1.0f / bk[wave][col];  // a power of two: exact
+      uint32_t d[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float t = ldexpf(q == 0 ? gsum[j] : gsum[4 + j], -(BACK_BIAS + E));
-      const _Float16 hi = (_Float16)t;
-      const _Float16 lo = (_Float16)(t - (float)hi);
-      d[j] = q < 2 ? ((uint32_t)__builtin_bit_cast(uint16_t, hi) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16))
-                   : 0u;
-    }
-    xb = f16x8_of(d[0], d[1], d[2], d[3]);
-  }
-  // factor that undoes this wave's scaling of token col (applied in the band sums)
-  if (q == 0 && col < kTok) bk[wave][col] = ldexpf(1.0f, BACK_BIAS + E);
-
-  // sum of squares per token for the norm: this slice's share, or all of K
-  // when the row is split over several workgroups
-  if (norm) {
-    if (p.splits > 1) {
-      for (int j = 0; j < M; ++j) {
-        float part = 0.f;
-        const char* xj = static_cast<const char*>(p.x) + (size_t)j * p.K * (p.x_f32 ? 4 : 2);
-        for (int k = threadIdx.x * 8; k < p.K; k += kThreads * 8) {
-          float v[8];
-          load_x<8>(xj, p.x_f32, k, v);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) part = fmaf(v[i], v[i], part);
-        }
-        part = wave_sum(part);
-        if (lane == 0) ssq[wave][j] = part;
+      for (int j = 0; j < 4; ++j) {
+        const float t = xsq[wave][col][4 * q + j] * binv;
+        const _Float16 hi = (_Float16)t;
+        const _Float16 lo = (_Float16)(t - (float)hi);
+        d[j] = (uint32_t)__builtin_bit_cast(uint16_t, hi) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
       }
-    } else {
-      ssum += xor_lanes(ssum, 16);
-      ssum += xor_lanes(ssum, 32);
-      if (q == 0 && col < M) ssq[wave][col] = ssum;
+      xb = f16x8_of(d[0], d[1], d[2], d[3]);
+    }
+  }
+
+  // sum of squares per token for the norm over all of K when the row is split
+  // over several workgroups (otherwise the eight waves' shares above)
+  if (norm && p.splits > 1) {
+    __syncthreads();  // the per-range shares above are replaced
+    for (int j = 0; j < M; ++j) {
+      float part = 0.f;
+      const char* xj = static_cast<const char*>(p.x) + (size_t)j * p.K * (p.x_f32 ? 4 : 2);
+      for (int k = threadIdx.x * 8; k < p.K; k += kThreads * 8) {
+        float v[8];
+        load_x<8>(xj, p.x_f32, k, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = fmaf(v[i], v[i], part);
+      }
+      part = wave_sum(part);
+      if (lane == 0) ssq[wave][j] = part;
     }
   }
   __syncthreads();
@@ -418,15 +476,28 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
         wave_sync_lds();
       }
 #pragma unroll
-      for (int it = 0; it < IPB; ++it) {
-        uint32_t w[4] = {cq[a][d][it].x, cq[a][d][it].y, cq[a][d][it].z, cq[a][d][it].w};
+      for (int it = 0; it < NLI; ++it) {
+        const u32x4 X = cq[a][d][it][0], Y = cq[a][d][it][1];
         issue_item(ahead, it, a, d);
         asm volatile("" ::: "memory");
+        // back to one row per column: lane (q, col) gets chunk q (w[0..3]) and
+        // chunk 4 + q (w[4..7]) of row col, then the 4 x 4 exchanges give it
+        // word q of chunks 0..3 and of chunks 4..7
+        const bool lo = col < 8;
+        uint32_t w[8];
+        const uint32_t xs4[4] = {X.x, X.y, X.z, X.w}, ys4[4] = {Y.x, Y.y, Y.z, Y.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t xr = row_ror8(xs4[j]), yr = row_ror8(ys4[j]);
+          w[j] = lo ? xs4[j] : yr;
+          w[4 + j] = lo ? xr : ys4[j];
+        }
         cross_rows_4x4(w[0], w[1], w[2], w[3]);
+        cross_rows_4x4(w[4], w[5], w[6], w[7]);
         f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int k = 4 * it + c;  // chunk within the wave range
+        for (int c = 0; c < 8; ++c) {
+          const int k = 8 * it + c;  // chunk within the wave range
           if constexpr (LUT) {
             acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[k], lut_operand(w[c], trow), acc[a], 0, 0, 0);
           } else {

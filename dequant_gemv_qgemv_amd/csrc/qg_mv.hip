@@ -374,6 +374,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   __shared__ float red[2 * kWaves];
   __shared__ int last_flag;
 
+  params_now(p);
   const int slice = blockIdx.x / p.grid_x;
   const int tile = blockIdx.x - slice * p.grid_x;
   const int C = p.K / CPC;
