@@ -1,20 +1,28 @@
 """Decode-throughput benchmark of the quantized matvec path on one MI355X.
 
-One step = one decode token through the Llama-3-8B-shaped stack: 32 layers,
-hidden 4096, each layer = rmsnorm+QKV matvec (4096->6144), O matvec
-(4096->4096, + residual), rmsnorm + gate.up SwiGLU (4096->14336 x2), down
-matvec (14336->4096, + residual); 4-bit codes, group 64, fp16 scale + bias,
-fp32 activations; the attention output is stood in by the q-slice of the QKV
-output. Weights are seeded synthetic data of those shapes (3.93 GB, resident
-in HBM before timing). The 128 launches of a token are captured once in a HIP
-graph and replayed.
+Default (--config stack, 4-bit, M=1): one step = one decode token through
+the Llama-3-8B-shaped stack: 32 layers, hidden 4096, each layer = rmsnorm+QKV
+matvec (4096->6144), O matvec (4096->4096, + residual), rmsnorm + gate.up
+SwiGLU (4096->14336 x2), down matvec (14336->4096, + residual); 4-bit codes,
+group 64, fp16 scale + bias, fp32 activations; the attention output is stood
+in by the q-slice of the QKV output. Weights are seeded synthetic data of
+those shapes (3.93 GB, resident in HBM before timing). The launches of a step
+are captured once in a HIP graph and replayed.
 
-Prints ONE JSON line: value = algorithmic bytes per token / time per token
-(GB/s), plus equivalent tokens/s, the roofline of the dominant kernel (the
-gate.up SwiGLU launch: 32 back-to-back launches over distinct weights in a
-graph, timed with HIP events on the stream that replays it), the
-measured device-to-device copy bandwidth, and the CPU oracle's throughput on a
-bounded sample of the same workload.
+Other workloads (each prints its own line): --config stack with --bits 2 or
+--fmt 1 (16-entry table) and --m 1..8 activation vectors per step; --config
+single (one 2048 x 2048 4-bit matvec, rotating over 256 weight sets);
+--config moe (one 512-expert layer, top-3 + shared expert, 60 chained router
+draws per token over the same weights); --config qwen (28-layer hidden-1024
+stack + final norm + 151936 x 1024 logits + top-40, three model copies
+rotated per token).
+
+Prints ONE JSON line: value = algorithmic bytes per step / time per step
+(GB/s), plus equivalent steps/s, the roofline of the dominant kernel
+(back-to-back launches over distinct weights in a graph, timed with HIP
+events on the stream that replays it), the measured device-to-device copy
+bandwidth, and the CPU oracle's throughput on a bounded sample of the same
+workload.
 """
 
 from __future__ import annotations
@@ -135,11 +143,465 @@ def summarize_trace(path):
               f"{nbytes[k] / avg / 1e3:.0f} |")
 
 
+def graph_step(fn, use_graph, out_tensor):
+    """Captures fn in a HIP graph (after one eager run) and checks that a
+    replay gives bitwise the eager result; returns (step, graph or None)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    eager = out_tensor.clone()
+    if not use_graph:
+        return fn, None
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out_tensor, eager):
+        log("graph replay differs from the eager run; falling back to eager launches")
+        return fn, None
+    return g.replay, g
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_launches(fn, n, use_graph, reps=5):
+    """us per launch of fn (which issues n launches), replayed from a graph."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+    else:
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * n)
+
+
+def copy_peak(dev):
+    """Device-to-device copy bandwidth (read + write bytes), 1 GiB buffers."""
+    import torch
+    nb = 1 << 30
+    src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    return 2 * nb * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+
+def cpu_sample(work, seconds):
+    """Runs work(i) -> bytes for i = 0, 1, ... until `seconds` have passed;
+    returns (bytes done, calls, seconds)."""
+    t_start = time.time()
+    done, n = 0, 0
+    while time.time() - t_start < seconds:
+        b = work(n)
+        if b is None:
+            break
+        done += b
+        n += 1
+    dt = time.time() - t_start
+    return done, n, dt
+
+
+def oracle_threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def emit(args, workload, cfg, step_bytes, ms, dom, copy_gbs, cpu, dtype="f32"):
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": dict({"workload": workload, "bytes_per_step": step_bytes}, **cfg),
+        "steps_per_s": round(1e3 / ms, 2),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "frac_of_copy_peak": round(gbs / copy_gbs, 4),
+        "copy_peak_gbs": round(copy_gbs, 1),
+        "roofline": dom,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def roofline(kernel, nbytes, us, traffic=None):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "bytes_per_launch": nbytes, "us_per_launch": round(us, 3)}
+
+
+def upload_layer(qg, w, dev):
+    import torch
+    d = {k: qg.QMat.from_host(v, dev) for k, v in w.items() if isinstance(v, dict)}
+    for k in ("g_attn", "g_ffn"):
+        d[k] = torch.from_numpy(w[k].view(np.int16)).to(dev)
+    return d
+
+
+def run_stack(args, qg, synth, dev):
+    """Llama-3-8B-shaped decode stack; M activation vectors per step."""
+    import torch
+    bits, fmt, M = args.bits, args.fmt, args.m
+    model = dict(synth.LLAMA3_8B)
+    model["layers"] = args.layers
+    H, FF, QD, NQ = model["hidden"], model["ffn"], model["q_dim"], model["qkv"]
+
+    t0 = time.time()
+    host_layers, layers = [], []
+    for li in range(model["layers"]):
+        w = synth.layer_weights(args.seed, model, li, bits, fmt)
+        host_layers.append(w)
+        layers.append(upload_layer(qg, w, dev))
+    torch.cuda.synchronize()
+    weight_bytes = sum(m.nbytes() for d in layers for m in d.values() if isinstance(m, qg.QMat))
+    log(f"weights: {model['layers']} layers, {weight_bytes / 1e9:.3f} GB in HBM "
+        f"({time.time() - t0:.1f} s)")
+    # activation traffic per step (fp32 reads/writes of x, qkv, h, u; norm weights)
+    act_bytes = model["layers"] * (M * 4 * ((H + NQ) + (QD + H + H) + (H + FF) + (FF + H + H))
+                                   + 2 * H * 2)
+    step_bytes = weight_bytes + act_bytes
+
+    if args.pmc_pass:
+        pmc_pass(qg, layers, model, dev)
+        return
+
+    shp = (lambda n: (n,)) if M == 1 else (lambda n: (M, n))
+    x0 = torch.from_numpy(synth.activations(args.seed, "x0", M * H, np.float32)
+                          .reshape(shp(H))).to(dev)
+    x = torch.empty(shp(H), dtype=torch.float32, device=dev)
+    qkv = torch.empty(shp(NQ), dtype=torch.float32, device=dev)
+    a = torch.empty(shp(QD), dtype=torch.float32, device=dev)
+    h = torch.empty(shp(H), dtype=torch.float32, device=dev)
+    u = torch.empty(shp(FF), dtype=torch.float32, device=dev)
+    ws = qg.workspace(qg.QG_OP_SWIGLU, FF, FF, M, bits, fmt, 1, dev)
+
+    def token():
+        x.copy_(x0)
+        for d in layers:
+            qg.qgemv_rmsnorm(d["qkv"], x, d["g_attn"], EPS, y=qkv, ws=ws)
+            if M == 1:
+                att = qkv[:QD]
+            else:  # stands in for the attention kernel writing its [M][q_dim] output
+                a.copy_(qkv[:, :QD])
+                att = a
+            qg.qgemv(d["o"], att, residual=x, y=h, ws=ws)
+            qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
+            qg.qgemv(d["down"], u, residual=h, y=x, ws=ws)
+
+    step, graph = graph_step(token, not args.no_graph, x)
+    if not bool(torch.isfinite(x).all()):
+        log("non-finite output")
+        sys.exit(1)
+    ms = time_steps(step, args.steps, args.warmup)
+    log(f"{args.steps} steps: {ms * 1e3:.1f} us/step, {step_bytes / (ms * 1e-3) / 1e9:.0f} GB/s, "
+        f"{1e3 / ms:.0f} steps/s")
+
+    # dominant kernel: gate.up SwiGLU, one launch per layer over distinct weights
+    sw_bytes = layers[0]["gate"].nbytes() + layers[0]["up"].nbytes() + M * (H * 4 + FF * 4) + H * 2
+
+    def swiglu_all():
+        for d in layers:
+            qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
+
+    sw_us = time_launches(swiglu_all, len(layers), graph is not None)
+    traffic = None
+    if bits == 4 and fmt == 0 and M == 1 and os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("kernel_hash") == kernel_hash():
+                traffic = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    fmt_name = {0: f"{bits}-bit g64 planar", 1: "4-bit 16-entry table per row"}[fmt]
+    kname = ("qswiglu" if M == 1 else f"qswiglu M={M} (matrix cores)") + \
+        " 14336x4096 x2 (gate.up, rmsnorm)"
+    dom = roofline(kname, sw_bytes, sw_us, traffic)
+    copy_gbs = copy_peak(dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th = oracle_threads()
+        xh = synth.activations(args.seed, "x0", M * H, np.float32).reshape(M, H).astype(np.float64)
+
+        def work(i):
+            nonlocal xh
+            if i >= len(host_layers):
+                return None
+            w = host_layers[i]
+            xh = np.stack([oracle.decoder_layer(w, xh[m], QD, EPS, nthreads=th) for m in range(M)])
+            return sum(int(sum(v.nbytes for k2, v in mm.items() if isinstance(v, np.ndarray)))
+                       for mm in w.values() if isinstance(mm, dict))
+
+        done, nl, dt = cpu_sample(work, args.cpu_seconds)
+        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+               "sample": f"{nl} of {len(host_layers)} decoder layers of one step ({M} vector(s); "
+                         f"{done / 1e9:.3f} GB of weights) in {dt:.1f} s, fp64 scalar C",
+               "steps_per_s": round(nl / len(host_layers) / dt, 6)}
+    workload = f"llama3-8b-shaped decode stack, {fmt_name}, M={M}"
+    cfg = {"layers": model["layers"], "hidden": H, "qkv": NQ, "ffn": FF, "bits": bits, "fmt": fmt,
+           "m": M, "graph": graph is not None}
+    emit(args, workload, cfg, step_bytes, ms, dom, copy_gbs, cpu)
+
+
+def run_single(args, qg, synth, dev):
+    """One 2048 x 2048 4-bit matvec; 256 weight sets rotated (607 MB, more
+    than the 256 MB last-level cache)."""
+    import torch
+    N = K = 2048
+    sets = 256
+    host = [synth.qmat(args.seed, ("cfg0", i), N, K, 4) for i in range(sets)]
+    mats = [qg.QMat.from_host(w, dev) for w in host]
+    x = torch.from_numpy(synth.activations(args.seed, "cfg0x", K, np.float16)).to(dev)
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+    unit_bytes = mats[0].nbytes() + K * 2 + N * 4
+
+    def all_sets():
+        for m in mats:
+            qg.qgemv(m, x, y=y)
+
+    step, graph = graph_step(all_sets, not args.no_graph, y)
+    ms = time_steps(step, args.steps, args.warmup)
+    us = ms * 1e3 / sets
+    dom = roofline("qgemv 2048x2048 4-bit g64 (x fp16)", unit_bytes, us)
+    copy_gbs = copy_peak(dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th = oracle_threads()
+        xh = synth.activations(args.seed, "cfg0x", K, np.float16)
+
+        def work(i):
+            oracle.gemv(host[i % sets], xh, nthreads=th)
+            return unit_bytes
+
+        done, n, dt = cpu_sample(work, args.cpu_seconds)
+        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+               "sample": f"{n} matvecs 2048x2048 in {dt:.1f} s, fp64 scalar C",
+               "us_per_matvec": round(dt / n * 1e6, 1)}
+    cfg = {"n": N, "k": K, "weight_sets": sets, "us_per_matvec": round(us, 3),
+           "graph": graph is not None}
+    emit(args, "single 4-bit g64 matvec 2048x2048, M=1, back-to-back over 256 weight sets",
+         cfg, unit_bytes * sets, ms, dom, copy_gbs, cpu, dtype="f32")
+
+
+def run_moe(args, qg, synth, dev):
+    """One 512-expert layer (gate, up 4096->1024, down 1024->4096, 4-bit),
+    top-3 routed + 1 shared expert; a token runs 60 chained layers over the
+    same weights with fresh router logits each."""
+    import torch
+    mdl = synth.MOE_397B
+    E, F, H, K, L = mdl["experts"], mdl["ffn"], mdl["hidden"], mdl["top_k"], mdl["draws"]
+    t0 = time.time()
+    gate = synth.qmat(args.seed, "moe_gate_all", E * F, H, 4)
+    up = synth.qmat(args.seed, "moe_up_all", E * F, H, 4)
+    down = synth.qmat(args.seed, "moe_down_all", E * H, F, 4)
+    for W in (gate, up, down):
+        W["E"] = E
+    shared = tuple(synth.qmat(args.seed, ("moe_shared", n), *nk, 4)
+                   for n, nk in (("gate", (F, H)), ("up", (F, H)), ("down", (H, F))))
+    g = synth.norm_weight(args.seed, "moe_g", H)
+    Gd, Ud, Dd = (qg.QMat.from_host(W, dev) for W in (gate, up, down))
+    Sd = tuple(qg.QMat.from_host(W, dev) for W in shared)
+    gd = torch.from_numpy(g.view(np.int16)).to(dev)
+    logits = [synth.router_logits(args.seed, ("moe_route", l), E) for l in range(L)]
+    lgd = torch.from_numpy(np.stack(logits)).to(dev)
+    x0 = torch.from_numpy(synth.activations(args.seed, "moe_x0", H, np.float32)).to(dev)
+    x = torch.empty(H, dtype=torch.float32, device=dev)
+    ws = qg.workspace(qg.QG_OP_MOE, H, F, 1, 4, 0, K, dev)
+    torch.cuda.synchronize()
+    log(f"moe weights {(Gd.nbytes() + Ud.nbytes() + Dd.nbytes()) / 1e9:.2f} GB ({time.time() - t0:.1f} s)")
+    expert_bytes = synth.qmat_bytes(F, H) * 2 + synth.qmat_bytes(H, F)
+    layer_bytes = (K + 1) * expert_bytes + E * 4 + H * 4 * 2 + H * 2
+
+    def token():
+        x.copy_(x0)
+        for l in range(L):
+            qg.qmoe_experts(Gd, Ud, Dd, E, Sd, lgd[l], K, x, gd, EPS, y=x, ws=ws)
+
+    step, graph = graph_step(token, not args.no_graph, x)
+    ms = time_steps(step, args.steps, args.warmup)
+    us_layer = ms * 1e3 / L
+    dom = roofline("qmoe_experts (route, gate.up of 4 experts, down + combine)", layer_bytes, us_layer)
+    copy_gbs = copy_peak(dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th = oracle_threads()
+        xh = synth.activations(args.seed, "moe_x0", H, np.float32).astype(np.float64)
+
+        def work(i):
+            nonlocal xh
+            if i >= L:
+                return None
+            xh, _, _ = oracle.moe_layer(gate, up, down, shared, logits[i], K, xh, g, EPS,
+                                        nthreads=th)
+            return layer_bytes
+
+        done, n, dt = cpu_sample(work, args.cpu_seconds)
+        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+               "sample": f"{n} of {L} chained expert layers of one token in {dt:.1f} s, "
+                         f"fp64 scalar C", "tok_per_s": round(n / L / dt, 6)}
+    cfg = {"experts": E, "hidden": H, "ffn": F, "top_k": K, "shared": 1, "layers_per_token": L,
+           "us_per_layer": round(us_layer, 3), "graph": graph is not None}
+    emit(args, "moe expert layer, 512 experts 4-bit g64, top-3 + shared, 60 chained draws per token",
+         cfg, layer_bytes * L, ms, dom, copy_gbs, cpu)
+
+
+def run_qwen(args, qg, synth, dev):
+    """Qwen3-0.6B-shaped stack (28 layers, hidden 1024) + final norm + logits
+    151936 x 1024 + top-40 on the GPU; three model copies rotated per token
+    (about 1 GB, more than the last-level cache)."""
+    import torch
+    model = dict(synth.QWEN3_06B)
+    H, FF, QD, NQ, V = model["hidden"], model["ffn"], model["q_dim"], model["qkv"], model["vocab"]
+    copies, topk = 3, 40
+    t0 = time.time()
+    hosts, devs = [], []
+    for c in range(copies):
+        hl = [synth.layer_weights(args.seed + c, model, li) for li in range(model["layers"])]
+        head = synth.qmat(args.seed + c, ("qwen_head",), V, H, 4)
+        gf = synth.norm_weight(args.seed + c, "qwen_gf", H)
+        hosts.append((hl, head, gf))
+        devs.append(([upload_layer(qg, w, dev) for w in hl], qg.QMat.from_host(head, dev),
+                     torch.from_numpy(gf.view(np.int16)).to(dev)))
+    torch.cuda.synchronize()
+    stack_bytes = sum(m.nbytes() for d in devs[0][0] for m in d.values() if isinstance(m, qg.QMat))
+    head_bytes = devs[0][1].nbytes()
+    act_bytes = model["layers"] * (4 * ((H + NQ) + (QD + H + H) + (H + FF) + (FF + H + H)) + 2 * H * 2) \
+        + H * 4 + H * 2 + V * 4 * 2 + topk * 8
+    step_bytes = stack_bytes + head_bytes + act_bytes
+    log(f"qwen: {copies} copies, {step_bytes / 1e6:.1f} MB per token ({time.time() - t0:.1f} s)")
+    x0 = torch.from_numpy(synth.activations(args.seed, "qwen_x0", H, np.float32)).to(dev)
+    x = torch.empty(H, dtype=torch.float32, device=dev)
+    qkv = torch.empty(NQ, dtype=torch.float32, device=dev)
+    h = torch.empty(H, dtype=torch.float32, device=dev)
+    u = torch.empty(FF, dtype=torch.float32, device=dev)
+    z = torch.empty(V, dtype=torch.float32, device=dev)
+    idx = torch.empty(topk, dtype=torch.int32, device=dev)
+    vals = torch.empty(topk, dtype=torch.float32, device=dev)
+    ws = qg.workspace(qg.QG_OP_LOGITS_TOPK, V, H, 1, 4, 0, topk, dev)
+    ws2 = qg.workspace(qg.QG_OP_SWIGLU, FF, FF, 1, 4, 0, 1, dev)
+
+    def token_of(c):
+        layers, head, gf = devs[c]
+
+        def token():
+            x.copy_(x0)
+            for d in layers:
+                qg.qgemv_rmsnorm(d["qkv"], x, d["g_attn"], EPS, y=qkv, ws=ws2)
+                qg.qgemv(d["o"], qkv[:QD], residual=x, y=h, ws=ws2)
+                qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws2)
+                qg.qgemv(d["down"], u, residual=h, y=x, ws=ws2)
+            qg.qlogits_topk(head, x, topk, gf, EPS, logits=z, idx=idx, vals=vals, ws=ws)
+        return token
+
+    steps_c, graph = [], None
+    for c in range(copies):
+        st, graph = graph_step(token_of(c), not args.no_graph, idx)
+        steps_c.append(st)
+    k = [0]
+
+    def step():
+        steps_c[k[0] % copies]()
+        k[0] += 1
+
+    ms = time_steps(step, args.steps, args.warmup)
+
+    def heads():
+        for c in range(copies):
+            qg.qlogits_topk(devs[c][1], x, topk, devs[c][2], EPS, logits=z, idx=idx, vals=vals,
+                            ws=ws)
+
+    head_us = time_launches(heads, copies, graph is not None)
+    dom = roofline("qlogits_topk 151936x1024 4-bit + final norm + top-40", head_bytes + H * 4 + V * 8,
+                   head_us)
+    copy_gbs = copy_peak(dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th = oracle_threads()
+        hl, head, gf = hosts[0]
+        xh = synth.activations(args.seed, "qwen_x0", H, np.float32).astype(np.float64)
+        per_layer = stack_bytes // model["layers"]
+
+        def work(i):
+            nonlocal xh
+            if i < len(hl):
+                xh = oracle.decoder_layer(hl[i], xh, QD, EPS, nthreads=th)
+                return per_layer
+            if i == len(hl):
+                oracle.logits_topk(head, xh, topk, gf, EPS, nthreads=th)
+                return head_bytes
+            return None
+
+        done, n, dt = cpu_sample(work, args.cpu_seconds)
+        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+               "sample": f"{min(n, len(hl))} of {len(hl)} decoder layers"
+                         f"{' + logits/top-40' if n > len(hl) else ''} of one token in {dt:.1f} s, "
+                         f"fp64 scalar C"}
+    cfg = {"layers": model["layers"], "hidden": H, "vocab": V, "top_k": topk, "copies": copies,
+           "graph": graph is not None}
+    emit(args, "qwen3-0.6b-shaped decode stack + logits + top-40, 4-bit g64, M=1", cfg,
+         step_bytes, ms, dom, copy_gbs, cpu)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="stack", choices=["stack", "single", "moe", "qwen"])
+    ap.add_argument("--bits", type=int, default=4, choices=[2, 4], help="stack: code width")
+    ap.add_argument("--fmt", type=int, default=0, choices=[0, 1],
+                    help="stack: 0 = scale + bias per group, 1 = 16-entry table per row (4-bit)")
+    ap.add_argument("--m", type=int, default=1, help="stack: activation vectors per step (1..8)")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
@@ -165,6 +627,12 @@ def main():
         print("bench.py: this build runs on one GPU only; --gpus above 1 is not supported "
               "(the sharding plan is described in the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.fmt == 1 and args.bits != 4:
+        print("bench.py: the table format has 4-bit codes", file=sys.stderr)
+        sys.exit(2)
+    if not 1 <= args.m <= 8:
+        print("bench.py: --m must be 1..8", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -178,199 +646,8 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    model = dict(synth.LLAMA3_8B)
-    model["layers"] = args.layers
-    H, FF, QD = model["hidden"], model["ffn"], model["q_dim"]
-
-    # ---- weights (host, then HBM) -------------------------------------------
-    t0 = time.time()
-    host_layers, layers = [], []
-    for li in range(model["layers"]):
-        w = synth.layer_weights(args.seed, model, li)
-        host_layers.append(w)
-        d = {k: qg.QMat.from_host(v, dev) for k, v in w.items() if isinstance(v, dict)}
-        d["g_attn"] = torch.from_numpy(w["g_attn"].view(np.int16)).to(dev)
-        d["g_ffn"] = torch.from_numpy(w["g_ffn"].view(np.int16)).to(dev)
-        layers.append(d)
-    torch.cuda.synchronize()
-    weight_bytes = sum(m.nbytes() for d in layers for k, m in d.items() if isinstance(m, qg.QMat))
-    log(f"weights: {model['layers']} layers, {weight_bytes / 1e9:.3f} GB in HBM "
-        f"({time.time() - t0:.1f} s)")
-
-    # activation traffic per token (fp32 reads/writes of x, qkv, h, u + norm weights)
-    act_bytes = model["layers"] * 4 * (
-        (H + model["qkv"]) + (QD + H + H) + (H + FF) + (FF + H + H)) + model["layers"] * 2 * H * 2
-    step_bytes = weight_bytes + act_bytes
-
-    if args.pmc_pass:
-        pmc_pass(qg, layers, model, dev)
-        return
-
-    # ---- buffers ---------------------------------------------------------------
-    x0 = torch.from_numpy(synth.activations(args.seed, "x0", H, np.float32)).to(dev)
-    x = torch.empty(H, dtype=torch.float32, device=dev)
-    qkv = torch.empty(model["qkv"], dtype=torch.float32, device=dev)
-    h = torch.empty(H, dtype=torch.float32, device=dev)
-    u = torch.empty(FF, dtype=torch.float32, device=dev)
-    ws = qg.workspace(qg.QG_OP_SWIGLU, FF, H, 1, 4, 0, 1, dev)
-
-    def token():
-        x.copy_(x0)
-        for d in layers:
-            qg.qgemv_rmsnorm(d["qkv"], x, d["g_attn"], EPS, y=qkv, ws=ws)
-            qg.qgemv(d["o"], qkv[:QD], residual=x, y=h, ws=ws)
-            qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
-            qg.qgemv(d["down"], u, residual=h, y=x, ws=ws)
-
-    token()
-    torch.cuda.synchronize()
-    eager_out = x.clone()
-    step = token
-    graph = None
-    if not args.no_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            token()
-        torch.cuda.current_stream().wait_stream(s)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            token()
-        step = graph.replay
-        step()
-        torch.cuda.synchronize()
-        if not torch.equal(x, eager_out):
-            log("graph replay differs from the eager token; falling back to eager launches")
-            step = token
-            graph = None
-    if not bool(torch.isfinite(x).all()):
-        log("non-finite output")
-        sys.exit(1)
-
-    # ---- timed steps ------------------------------------------------------------
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"{args.steps} tokens: {ms * 1e3:.1f} us/token, {gbs:.0f} GB/s, {1e3 / ms:.0f} tok/s")
-
-    # ---- dominant kernel: gate.up SwiGLU ----------------------------------------
-    # 32 back-to-back launches (one per layer, distinct weights) captured in a
-    # graph and replayed, timed with HIP events on the capturing stream.
-    sw_bytes = (layers[0]["gate"].nbytes() + layers[0]["up"].nbytes() + H * 4 + H * 2 + FF * 4)
-
-    def swiglu_all():
-        for d in layers:
-            qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
-
-    swiglu_all()
-    torch.cuda.synchronize()
-    sw_us = None
-    if graph is not None:
-        sg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(sg):
-            swiglu_all()
-        sg.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 5
-        a.record()
-        for _ in range(reps):
-            sg.replay()
-        b.record()
-        torch.cuda.synchronize()
-        sw_us = a.elapsed_time(b) * 1e3 / (reps * len(layers))
-    else:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        swiglu_all()
-        b.record()
-        torch.cuda.synchronize()
-        sw_us = a.elapsed_time(b) * 1e3 / len(layers)
-    sw_gbs = sw_bytes / (sw_us * 1e-6) / 1e9
-
-    # traffic: HBM bytes per launch from the committed counter profile, if it
-    # was taken on the current kernel source
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tr = json.load(open(TRAFFIC_FILE))
-            if tr.get("kernel_hash") == kernel_hash():
-                traffic = tr.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
-
-    # ---- measured copy bandwidth (read + write bytes) --------------------------
-    nb = 1 << 30
-    src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * nb * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
-
-    # ---- CPU oracle baseline on a bounded sample --------------------------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        threads = max(1, min(16, os.cpu_count() or 1))
-        xh = synth.activations(args.seed, "x0", H, np.float32).astype(np.float64)
-        t_start = time.time()
-        done_bytes = 0
-        nl = 0
-        while nl < len(host_layers) and time.time() - t_start < args.cpu_seconds:
-            w = host_layers[nl]
-            xh = oracle.decoder_layer(w, xh, QD, EPS, nthreads=threads)
-            done_bytes += sum(int(m["q"].nbytes + m["scales"].nbytes + m["biases"].nbytes)
-                              for m in w.values() if isinstance(m, dict))
-            nl += 1
-        dt = time.time() - t_start
-        cpu = {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{nl} of {len(host_layers)} decoder layers of one token "
-                         f"({done_bytes / 1e9:.3f} GB of weights) in {dt:.1f} s, fp64 scalar C",
-               "tok_per_s": round(nl / len(host_layers) / dt, 6)}
-
-    out = {
-        "metric": METRIC,
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": "llama3-8b-shaped decode stack, 4-bit g64 planar, M=1",
-                   "layers": model["layers"], "hidden": H, "qkv": model["qkv"], "ffn": FF,
-                   "bytes_per_token": step_bytes, "graph": graph is not None},
-        "tok_per_s": round(1e3 / ms, 2),
-        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "frac_of_copy_peak": round(gbs / copy_gbs, 4),
-        "copy_peak_gbs": round(copy_gbs, 1),
-        "roofline": {"bound": "hbm", "kernel": "qswiglu 14336x4096 x2 (gate.up, rmsnorm)",
-                     "achieved": round(sw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(sw_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": sw_bytes, "us_per_launch": round(sw_us, 3)},
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+    {"stack": run_stack, "single": run_single, "moe": run_moe, "qwen": run_qwen}[args.config](
+        args, qg, synth, dev)
 
 
 if __name__ == "__main__":
