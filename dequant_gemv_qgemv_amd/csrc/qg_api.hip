@@ -125,6 +125,7 @@ int pick_lpr(int C) {
 struct MvShape {
   int N, K, bits, fmt, epi;
   int col_seg_chunks;  // K-segment length in chunks (0: one matrix along K)
+  int seg;             // SegMode of the launch
 };
 
 // Chooses lanes per row, rows per lane, split-K and grid for one launch.
@@ -141,6 +142,11 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
       }
   }
   pl.rows = g_knob[1].load() ? g_knob[1].load() : 1;
+  pl.depth = g_knob[4].load() ? g_knob[4].load() : 2;
+  // Resident workgroups per CU: two 8-wave groups keep 16 waves in flight
+  // where the kernel's registers allow it (the 2-bit kernels fit one).
+  const int resident = mv_resident_per_cu(s.bits, s.fmt, s.epi, s.seg, pl);
+  const int wg_per_cu = g_knob[3].load() ? g_knob[3].load() : (resident < 2 ? resident : 2);
   const int rpb = (64 / pl.lpr) * pl.rows;
   const int nbands = (s.N + rpb - 1) / rpb;
   const int tiles = (nbands + kWaves - 1) / kWaves;
@@ -154,7 +160,7 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
     splits = g_knob[0].load();
   } else {
     // Small N: more workgroups in flight by splitting K (keep >= 2 passes per slice).
-    const int target = 2 * cus;
+    const int target = wg_per_cu * cus;
     if (tiles < target && passes >= 4) {
       int want = (target + tiles - 1) / tiles;
       if (want > passes / 2) want = passes / 2;
@@ -170,14 +176,11 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
   pl.splits = (C + pl.slice_chunks - 1) / pl.slice_chunks;
   const int slice_npass = slice_passes;
   pl.lds_bytes = (size_t)slice_npass * pl.lpr * per_chunk + lut_bytes;
-  // Resident workgroups per CU: two 8-wave groups keep 16 waves in flight.
-  const int wg_per_cu = g_knob[3].load() ? g_knob[3].load() : 2;
   int gx = tiles;
   const int cap = (cus * wg_per_cu + pl.splits - 1) / pl.splits;
   if (gx > cap) gx = cap;
   gx = ((gx + 7) / 8) * 8;  // slices of one tile share an XCD (workgroups go round-robin over 8)
   pl.grid_x = gx;
-  pl.depth = g_knob[4].load() ? g_knob[4].load() : 2;
   return pl;
 }
 
@@ -273,7 +276,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   if (M > 1)
     return run_mm(A, B, N, K, M, bits, fmt, epi, x, x_dtype, norm_w, eps, residual, y, ws,
                   have_ws, dev.cus, stream);
-  const MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0}, dev.cus, have_ws);
+  const MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0, kSegNone}, dev.cus, have_ws);
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;  // K too long for one slice: needs ws
   MvParams p;
   memset(&p, 0, sizeof(p));
@@ -315,7 +318,8 @@ int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;
   MvParams p = p0;
-  const MvPlan pl = plan_mv({p.N, p.K, bits, fmt, epi, p.seg_mode == kSegCols ? p.seg_len : 0}, dev.cus, have_ws);
+  const MvPlan pl = plan_mv({p.N, p.K, bits, fmt, epi, p.seg_mode == kSegCols ? p.seg_len : 0,
+                             p.seg_mode}, dev.cus, have_ws);
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;
   p.splits = pl.splits;
   p.slice_chunks = pl.slice_chunks;

@@ -83,6 +83,8 @@ struct MvPlan {
 
 hipError_t launch_mv(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
                      hipStream_t stream);
+// Workgroups of the kernel launch_mv would pick that fit on one compute unit.
+int mv_resident_per_cu(int bits, int fmt, int epi, int seg, const MvPlan& plan);
 
 // Small-M (2..8) matrix-core kernels: plain / normed store, SwiGLU; one
 // matrix (seg_mode kSegNone). K slices of mm_slice_codes() codes.

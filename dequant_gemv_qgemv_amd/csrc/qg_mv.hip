@@ -38,6 +38,9 @@
 // pre-divided by that power of two when staged. x is staged in fp16 after an
 // exact power-of-two range scale 2^-e chosen from max|x| over the slice; the
 // chunk result is multiplied back by 2^(24+e). The LUT format keeps x in fp32.
+#include <mutex>
+#include <unordered_map>
+
 #include "qg_common.h"
 
 namespace qg {
@@ -650,12 +653,36 @@ KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows, int depth) {
 
 }  // namespace
 
+namespace {
+KernelFn select_mv(int bits, int fmt, int epi, int seg, const MvPlan& plan) {
+  if (bits == 4 && fmt == 0) return pick_kernel_epi<4, 0>(epi, seg, plan.lpr, plan.rows, plan.depth);
+  if (bits == 2 && fmt == 0) return pick_kernel_epi<2, 0>(epi, seg, plan.lpr, plan.rows, plan.depth);
+  if (bits == 4 && fmt == 1 && seg == kSegNone) return pick_kernel_epi<4, 1>(epi, seg, plan.lpr, plan.rows, plan.depth);
+  return nullptr;
+}
+}  // namespace
+
+int mv_resident_per_cu(int bits, int fmt, int epi, int seg, const MvPlan& plan) {
+  const KernelFn fn = select_mv(bits, fmt, epi, seg, plan);
+  if (!fn) return 1;
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find((const void*)fn);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  // registers decide; the dynamic LDS of one workgroup is at most kMaxLdsBytes
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)fn, kThreads, kMaxLdsBytes) !=
+          hipSuccess ||
+      n < 1)
+    n = 1;
+  cache[(const void*)fn] = n;
+  return n;
+}
+
 hipError_t launch_mv(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
                      hipStream_t stream) {
-  KernelFn fn = nullptr;
-  if (bits == 4 && fmt == 0) fn = pick_kernel_epi<4, 0>(epi, p.seg_mode, plan.lpr, plan.rows, plan.depth);
-  else if (bits == 2 && fmt == 0) fn = pick_kernel_epi<2, 0>(epi, p.seg_mode, plan.lpr, plan.rows, plan.depth);
-  else if (bits == 4 && fmt == 1 && p.seg_mode == kSegNone) fn = pick_kernel_epi<4, 1>(epi, p.seg_mode, plan.lpr, plan.rows, plan.depth);
+  const KernelFn fn = select_mv(bits, fmt, epi, p.seg_mode, plan);
   if (!fn) return hipErrorInvalidValue;
   if (plan.lds_bytes > (size_t)kMaxLdsBytes) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(plan.grid_x * plan.splits));
