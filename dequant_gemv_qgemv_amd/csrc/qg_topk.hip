@@ -10,9 +10,10 @@
 // and the result cannot depend on scheduling.
 //
 // Two phases in one launch: every workgroup finds the k largest keys of its
-// slice (radix select on 8-bit digits with LDS histograms, then a bitonic sort
-// of the k survivors) and writes them to the workspace; the last workgroup to
-// finish (integer ticket) repeats the selection over all candidates.
+// slice (radix select on 8-bit digits with per-wave LDS histograms, stopping
+// once a digit bin holds exactly the keys still wanted) and writes them to the
+// workspace; the last workgroup to finish (integer ticket) repeats the
+// selection over all candidates and sorts the k winners.
 #include "qg_internal.h"
 
 namespace qg {
@@ -39,31 +40,109 @@ __device__ __forceinline__ uint32_t key_index(uint64_t key) {
   return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull);
 }
 
+constexpr int kTkWaves = kTkThreads / 64;
+
 struct SelectShared {
-  uint32_t hist[256];
+  uint32_t hist[kTkWaves][256];  // one histogram per wave (fewer colliding atomics)
+  uint32_t tot[256];             // their sum
   uint64_t list[kTkMaxK];
-  uint32_t digit, rem, count;
+  uint32_t digit, rem, count, done;
   int last;
 };
 
-// The kk-th largest of the keys visited by for_each (kk >= 1, keys unique).
+// Bitwise AND and OR of all nonzero keys of the block (for the common prefix).
+template <class ForEach>
+__device__ void and_or(ForEach for_each, SelectShared& sh, uint64_t* a_out, uint64_t* o_out) {
+  uint64_t a = ~0ull, o = 0ull;
+  for_each([&](uint64_t key) {
+    if (key) {
+      a &= key;
+      o |= key;
+    }
+  });
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a &= __shfl_xor(a, off);
+    o |= __shfl_xor(o, off);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh.list[2 * wave] = a;
+    sh.list[2 * wave + 1] = o;
+  }
+  __syncthreads();
+  a = ~0ull;
+  o = 0ull;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    a &= sh.list[2 * w];
+    o |= sh.list[2 * w + 1];
+  }
+  __syncthreads();
+  *a_out = a;
+  *o_out = o;
+}
+
+// Adds 1 to bin d of this wave's histogram for every active lane: lanes that
+// share the digit of the wave's first active lane are counted with one atomic
+// (two rounds), the rest individually; keeps same-address collisions low when
+// the keys crowd into a few bins.
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t d) {
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const uint64_t act = __ballot(active);
+    if (act == 0ull) return;
+    const int leader = __builtin_ctzll(act);
+    const uint32_t ld = __shfl(d, leader);
+    const bool same = active && d == ld;
+    const uint64_t m = __ballot(same);
+    if ((int)(threadIdx.x & 63) == leader) atomicAdd(&hist[ld], (uint32_t)__builtin_popcountll(m));
+    active = active && !same;
+  }
+  if (active) atomicAdd(&hist[d], 1u);
+}
+
+// The kk-th largest of the nonzero keys visited by for_each (1 <= kk <= their
+// count, keys unique), or a smaller key t such that exactly kk keys are >= t:
+// radix select from the highest bit where the keys differ, in windows of up to
+// 8 bits, stopping as soon as the chosen digit's bin holds exactly the keys
+// still wanted (every key with that prefix is then in). Called by all
+// kTkThreads threads of the block.
 template <class ForEach>
 __device__ uint64_t kth_largest(ForEach for_each, uint32_t kk, SelectShared& sh) {
-  uint64_t prefix = 0, mask = 0;
+  const int wave = threadIdx.x >> 6;
+  uint64_t all_and, all_or;
+  and_or(for_each, sh, &all_and, &all_or);
+  const uint64_t diff = all_and ^ all_or;
+  if (diff == 0ull) return all_and;  // a single key
+  int top = 63 - __builtin_clzll(diff);  // highest bit where keys differ
+  uint64_t mask = top == 63 ? 0ull : ~0ull << (top + 1);
+  uint64_t prefix = all_and & mask;  // the bits every key shares
   uint32_t remaining = kk;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[i] = 0u;
+  while (top >= 0) {
+    const int lo = top >= 7 ? top - 7 : 0;
+    const uint64_t wmask = ((1ull << (top - lo + 1)) - 1ull) << lo;
+#pragma unroll
+    for (int j = 0; j < kTkWaves * 256 / kTkThreads; ++j)
+      (&sh.hist[0][0])[threadIdx.x + j * kTkThreads] = 0u;
     __syncthreads();
     for_each([&](uint64_t key) {
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      hist_add(sh.hist[wave], key != 0ull && (key & mask) == prefix, (uint32_t)((key & wmask) >> lo));
     });
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kTkWaves; ++w) t += sh.hist[w][threadIdx.x];
+      sh.tot[threadIdx.x] = t;
+    }
     __syncthreads();
     if (threadIdx.x < 64) {
       const int l = threadIdx.x;  // lane l owns bins 255-4l .. 252-4l
       uint32_t c[4], tot = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        c[q] = sh.hist[255 - 4 * l - q];
+        c[q] = sh.tot[255 - 4 * l - q];
         tot += c[q];
       }
       uint32_t inc = tot;
@@ -80,6 +159,7 @@ __device__ uint64_t kth_largest(ForEach for_each, uint32_t kk, SelectShared& sh)
           if (cum + c[q] >= remaining) {
             sh.digit = 255 - 4 * l - q;
             sh.rem = remaining - cum;
+            sh.done = (c[q] == remaining - cum);  // the whole bin is wanted
             break;
           }
           cum += c[q];
@@ -87,26 +167,53 @@ __device__ uint64_t kth_largest(ForEach for_each, uint32_t kk, SelectShared& sh)
       }
     }
     __syncthreads();
-    prefix |= (uint64_t)sh.digit << shift;
-    mask |= (uint64_t)255 << shift;
+    prefix |= (uint64_t)sh.digit << lo;
+    mask |= wmask;
     remaining = sh.rem;
+    const bool done = sh.done;
     __syncthreads();
+    if (done) break;
+    top = lo - 1;
   }
   return prefix;
 }
 
-// Collects the keys >= thr (exactly kk of them) into sh.list[0..kk) sorted
-// descending; entries [kk, pow2) are zero.
+// Collects the keys >= thr (exactly kk of them) into sh.list[0..kk), in no
+// particular order.
 template <class ForEach>
-__device__ void gather_sorted(ForEach for_each, uint64_t thr, uint32_t kk, SelectShared& sh) {
-  uint32_t p2 = 1;
-  while (p2 < kk) p2 <<= 1;
-  for (uint32_t i = threadIdx.x; i < p2; i += blockDim.x) sh.list[i] = 0ull;
+__device__ void gather(ForEach for_each, uint64_t thr, SelectShared& sh) {
   if (threadIdx.x == 0) sh.count = 0u;
   __syncthreads();
   for_each([&](uint64_t key) {
     if (key >= thr) sh.list[atomicAdd(&sh.count, 1u)] = key;
   });
+  __syncthreads();
+}
+
+// Sorts sh.list[0..kk) descending (entries kk..pow2 are set to zero first):
+// one wave with shuffles for kk <= 64, else a block bitonic network.
+__device__ void sort_desc(uint32_t kk, SelectShared& sh) {
+  if (kk <= 64) {
+    if (threadIdx.x < 64) {
+      const uint32_t l = threadIdx.x;
+      uint64_t v = l < kk ? sh.list[l] : 0ull;
+      for (uint32_t size = 2; size <= 64; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+          const uint64_t o = __shfl_xor(v, stride);
+          const bool up = (l & stride) == 0;          // lower index of the pair
+          const bool desc = (l & size) == 0 || size == 64;
+          const uint64_t hi = v > o ? v : o, lo = v > o ? o : v;
+          v = (up == desc) ? hi : lo;
+        }
+      }
+      if (l < kk) sh.list[l] = v;
+    }
+    __syncthreads();
+    return;
+  }
+  uint32_t p2 = 1;
+  while (p2 < kk) p2 <<= 1;
+  for (uint32_t i = kk + threadIdx.x; i < p2; i += blockDim.x) sh.list[i] = 0ull;
   __syncthreads();
   for (uint32_t size = 2; size <= p2; size <<= 1) {
     for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
@@ -143,25 +250,44 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
 #pragma unroll
     for (int j = 0; j < kTkPer; ++j) f(keys[j]);
   };
+  // this slice's k largest (fewer if the slice is shorter), unsorted
   const uint32_t kk = (uint32_t)min(k, n);
   const uint64_t thr = kth_largest(regs, kk, sh);
-  gather_sorted(regs, thr, kk, sh);
+  gather(regs, thr, sh);
   for (int r = threadIdx.x; r < k; r += kTkThreads)
     cand[(size_t)b * k + r] = r < (int)kk ? sh.list[r] : 0ull;
 
-  __threadfence();
+  // every thread's candidate stores complete before the barrier; one thread
+  // then publishes them device-wide and takes the ticket (a fence per thread
+  // would write back and invalidate the caches 1024 times)
   __syncthreads();
-  if (threadIdx.x == 0) sh.last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+  if (threadIdx.x == 0) {
+    __threadfence();
+    sh.last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+    if (sh.last) __threadfence();
+  }
   __syncthreads();
   if (!sh.last) return;
-  __threadfence();
 
+  // the last workgroup: the k largest of all candidates (held in registers
+  // when they fit), sorted
   const int total = gridDim.x * k;
-  auto all = [&](auto&& f) {
-    for (int i = threadIdx.x; i < total; i += kTkThreads) f(__builtin_nontemporal_load(&cand[i]));
-  };
-  const uint64_t thr2 = kth_largest(all, (uint32_t)k, sh);
-  gather_sorted(all, thr2, (uint32_t)k, sh);
+  if (total <= kTkSlice) {
+#pragma unroll
+    for (int j = 0; j < kTkPer; ++j) {
+      const int i = threadIdx.x + j * kTkThreads;
+      keys[j] = i < total ? __builtin_nontemporal_load(&cand[i]) : 0ull;
+    }
+    const uint64_t thr2 = kth_largest(regs, (uint32_t)k, sh);
+    gather(regs, thr2, sh);
+  } else {
+    auto all = [&](auto&& f) {
+      for (int i = threadIdx.x; i < total; i += kTkThreads) f(__builtin_nontemporal_load(&cand[i]));
+    };
+    const uint64_t thr2 = kth_largest(all, (uint32_t)k, sh);
+    gather(all, thr2, sh);
+  }
+  sort_desc((uint32_t)k, sh);
   for (int r = threadIdx.x; r < k; r += kTkThreads) {
     const uint32_t i = key_index(sh.list[r]);
     idx[r] = (int32_t)i;
@@ -171,30 +297,55 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
 }
 
 // Router: one wave. ids = top_k of the logits (order above), w = softmax over
-// the chosen logits only.
+// the chosen logits only. Each lane keeps its own top_k keys (sorted, in
+// registers) over batches of loads issued together; the wave then takes the
+// largest head top_k times.
 __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ logits, int E,
                                                    int top_k, int32_t* ids_ws, float* w_ws,
                                                    int32_t* ids_out, float* w_out) {
+  constexpr int B = 8;  // loads per lane per batch
   const int l = threadIdx.x;
+  uint64_t mine[kMaxRoutes];
+#pragma unroll
+  for (int r = 0; r < kMaxRoutes; ++r) mine[r] = 0ull;
+  for (int base = 0; base < E; base += 64 * B) {
+    float v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + l + 64 * j;
+      v[j] = i < E ? logits[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + l + 64 * j;
+      uint64_t key = i < E ? order_key(v[j], (uint32_t)i) : 0ull;
+      // insert into the lane's descending list (entries past top_k stay unused)
+#pragma unroll
+      for (int r = 0; r < kMaxRoutes; ++r) {
+        const uint64_t cur = mine[r];
+        const bool take = key > cur;
+        mine[r] = take ? key : cur;
+        key = take ? cur : key;
+      }
+    }
+  }
   uint64_t chosen[kMaxRoutes];
 #pragma unroll
   for (int r = 0; r < kMaxRoutes; ++r) {
     chosen[r] = 0ull;
     if (r < top_k) {
-      uint64_t best = 0ull;
-      for (int i = l; i < E; i += 64) {
-        const uint64_t key = order_key(logits[i], (uint32_t)i);
-        bool taken = false;
-#pragma unroll
-        for (int q = 0; q < r; ++q) taken |= (chosen[q] == key);
-        if (!taken && key > best) best = key;
-      }
+      uint64_t best = mine[0];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
         const uint64_t o = __shfl_xor(best, off);
         if (o > best) best = o;
       }
       chosen[r] = best;
+      if (mine[0] == best) {  // keys are unique: exactly one lane pops its head
+#pragma unroll
+        for (int q = 0; q + 1 < kMaxRoutes; ++q) mine[q] = mine[q + 1];
+        mine[kMaxRoutes - 1] = 0ull;
+      }
     }
   }
   if (l == 0) {
