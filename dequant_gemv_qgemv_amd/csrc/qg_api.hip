@@ -156,17 +156,11 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
   max_chunks = (max_chunks / pl.lpr) * pl.lpr;
   const int passes = (C + pl.lpr - 1) / pl.lpr;
   int splits = (C + max_chunks - 1) / max_chunks;
-  if (g_knob[0].load()) {
-    splits = g_knob[0].load();
-  } else {
-    // Small N: more workgroups in flight by splitting K (keep >= 2 passes per slice).
-    const int target = wg_per_cu * cus;
-    if (tiles < target && passes >= 4) {
-      int want = (target + tiles - 1) / tiles;
-      if (want > passes / 2) want = passes / 2;
-      if (want > splits) splits = want;
-    }
-  }
+  // K is split only when one slice would not fit in LDS: measured on MI355X,
+  // splitting a launch to put more workgroups in flight made every shape slower
+  // (a tail of the waves runs three times longer), so small-N launches keep
+  // their tiles.
+  if (g_knob[0].load()) splits = g_knob[0].load();
   if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits > passes) splits = passes;
   if (splits < 1) splits = 1;
