@@ -186,6 +186,93 @@ __device__ __forceinline__ void params_now(const MvParams& p) {
                "s"((uint64_t)p.B[0].lut), "s"((uint64_t)p.partials), "s"((uint64_t)p.tickets));
 }
 
+// A unique 64-bit key per (value, index) that sorts as: larger value first,
+// equal values by lower index, -0 equal to +0, NaN below every number.
+__device__ __forceinline__ uint64_t order_key(float v, uint32_t i) {
+  uint32_t u;
+  if (v != v) {
+    u = 0u;  // NaN sorts below every number
+  } else {
+    if (v == 0.0f) v = 0.0f;  // -0 and +0 are the same value
+    u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - i);
+}
+
+__device__ __forceinline__ uint32_t key_index(uint64_t key) {
+  return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull);
+}
+
+// Router, run by one whole wave: ids = the top_k (<= kMaxRoutes) logits in
+// the order above, w = softmax over the chosen logits only. Each lane keeps
+// its own top_k keys (sorted, in registers) over batches of loads issued
+// together; the wave then takes the largest head top_k times. Lane 0 returns
+// the result in ids / w (registers).
+__device__ __forceinline__ void route_wave(const float* __restrict__ logits, int E, int top_k,
+                                           int32_t* ids, float* w) {
+  constexpr int B = 8;  // loads per lane per batch
+  const int l = threadIdx.x & 63;
+  uint64_t mine[kMaxRoutes];
+#pragma unroll
+  for (int r = 0; r < kMaxRoutes; ++r) mine[r] = 0ull;
+  for (int base = 0; base < E; base += 64 * B) {
+    float v[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + l + 64 * j;
+      v[j] = i < E ? logits[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int i = base + l + 64 * j;
+      uint64_t key = i < E ? order_key(v[j], (uint32_t)i) : 0ull;
+#pragma unroll
+      for (int r = 0; r < kMaxRoutes; ++r) {  // insert into the lane's descending list
+        const uint64_t cur = mine[r];
+        const bool take = key > cur;
+        mine[r] = take ? key : cur;
+        key = take ? cur : key;
+      }
+    }
+  }
+  uint64_t chosen[kMaxRoutes];
+#pragma unroll
+  for (int r = 0; r < kMaxRoutes; ++r) {
+    chosen[r] = 0ull;
+    if (r < top_k) {
+      uint64_t best = mine[0];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t o = __shfl_xor(best, off);
+        if (o > best) best = o;
+      }
+      chosen[r] = best;
+      if (mine[0] == best) {  // keys are unique: exactly one lane pops its head
+#pragma unroll
+        for (int q = 0; q + 1 < kMaxRoutes; ++q) mine[q] = mine[q + 1];
+        mine[kMaxRoutes - 1] = 0ull;
+      }
+    }
+  }
+  float lv[kMaxRoutes];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kMaxRoutes; ++r) {
+    lv[r] = r < top_k ? logits[key_index(chosen[r])] : -INFINITY;
+    lmax = fmaxf(lmax, lv[r]);
+  }
+  float den = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxRoutes; ++r)
+    if (r < top_k) den += expf(lv[r] - lmax);
+#pragma unroll
+  for (int r = 0; r < kMaxRoutes; ++r) {
+    ids[r] = r < top_k ? (int32_t)key_index(chosen[r]) : 0;
+    w[r] = r < top_k ? expf(lv[r] - lmax) / den : 0.f;
+  }
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ void wave_sync_lds() {

@@ -36,12 +36,22 @@ enum SegMode : int { kSegNone = 0, kSegRows = 1, kSegCols = 2 };
 // Routing input: when `ids` is set, segments [0, n_routed) are expert ids[i]
 // of a stacked tensor whose expert e starts at row e * expert_rows of
 // `all_A`/`all_B`; segment n_routed (if any) is the fixed A[n_routed].
+// With `logits` set, every workgroup picks the experts itself (top n_routed
+// of n_experts logits, softmax over the chosen) before its first weight load,
+// and workgroup 0 stores the choice in ids_store / w_store (and sel_ids /
+// sel_w when set) for the launches that follow.
 struct Routing {
   const int32_t* ids;     // device [n_routed] or nullptr
   const float* weights;   // device [n_routed] (K-segment input scaling) or nullptr
   int n_routed;
   int expert_rows;
   QMat all_A, all_B;
+  const float* logits;    // device [n_experts] or nullptr
+  int n_experts;
+  int32_t* ids_store;
+  float* w_store;
+  int32_t* sel_ids;
+  float* sel_w;
 };
 
 struct MvParams {

@@ -4,13 +4,14 @@
 // Compute" -- the combine, norm and residual run on the GPU and go straight to
 // the next layer, with no host round trip).
 //
-// Three launches on one stream:
-//  1. route: top_k of the router logits and softmax over the chosen ones,
-//     written to the workspace (and to sel_ids / sel_w when given);
-//  2. gate.up SwiGLU over the chosen experts plus the shared one, as one
-//     matvec over (top_k+1)*F gathered rows; each workgroup reads the chosen
-//     ids and points its row segments at those experts;
-//  3. down + combine + residual, as one matvec over the K-concatenation
+// Two launches on one stream:
+//  1. gate.up SwiGLU over the chosen experts plus the shared one, as one
+//     matvec over (top_k+1)*F gathered rows: every workgroup first picks the
+//     experts itself (top_k of the router logits, softmax over the chosen
+//     ones; 512 logits cost less than a launch) and points its row segments
+//     at them; workgroup 0 stores the choice in the workspace (and in sel_ids /
+//     sel_w when given);
+//  2. down + combine + residual, as one matvec over the K-concatenation
 //     [Down_e0 | Down_e1 | ... | Down_shared] against [w0*u0, w1*u1, ..., u_sh]:
 //     sum_e w_e (Down_e u_e) is that single row-by-row dot product, so the
 //     weighted combine costs no extra pass.
@@ -21,8 +22,6 @@
 
 namespace qg {
 
-hipError_t launch_route(const float* logits, int E, int top_k, int32_t* ids_ws, float* w_ws,
-                        int32_t* ids_out, float* w_out, hipStream_t stream);
 int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have_ws, void* ws,
                        size_t ws_bytes, size_t ws_offset, hipStream_t stream);
 size_t mv_workspace_bytes(int N, int epi);
@@ -89,12 +88,7 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
   float* u = reinterpret_cast<float*>(base + kRouteBytes);
   const size_t mv_off = kRouteBytes + align256((size_t)(top_k + 1) * F * 4);
 
-  // 1. routing
-  if (launch_route(router_logits, n_experts, top_k, ids_ws, w_ws, sel_ids, sel_w, stream) !=
-      hipSuccess)
-    return QG_ELAUNCH;
-
-  // 2. gate.up SwiGLU over the chosen experts' rows (+ shared)
+  // 1. routing + gate.up SwiGLU over the chosen experts' rows (+ shared)
   MvParams p;
   memset(&p, 0, sizeof(p));
   p.M = 1;
@@ -105,10 +99,16 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
     p.A[top_k] = dev(&shared3[0]);
     p.B[top_k] = dev(&shared3[1]);
   }
-  p.route.ids = ids_ws;
+  p.route.ids = nullptr;
   p.route.weights = nullptr;
   p.route.n_routed = top_k;
   p.route.expert_rows = F;
+  p.route.logits = router_logits;
+  p.route.n_experts = n_experts;
+  p.route.ids_store = ids_ws;
+  p.route.w_store = w_ws;
+  p.route.sel_ids = sel_ids;
+  p.route.sel_w = sel_w;
   p.route.all_A = dev(gate_all);
   p.route.all_B = dev(up_all);
   p.N = nseg * F;
@@ -124,9 +124,10 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
   rc = mv_launch_internal(bits, fmt, kEpiSwiglu, p, true, ws, ws_bytes, mv_off, stream);
   if (rc) return rc;
 
-  // 3. down over the K-concatenated experts, weighted, + residual
+  // 2. down over the K-concatenated experts, weighted, + residual
   MvParams d;
   memset(&d, 0, sizeof(d));
+  d.M = 1;
   d.nseg = nseg;
   d.seg_mode = kSegCols;
   d.seg_len = F / (128 / bits);  // chunks per expert segment

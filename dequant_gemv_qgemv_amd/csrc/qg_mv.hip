@@ -252,10 +252,11 @@ __device__ float rms_all(const MvParams& p, float* red) {
   return 1.0f / sqrtf(block_reduce<false>(sumsq_all(p), red) / (float)p.K + p.eps);
 }
 
-// Matrix of segment `seg` (routed experts are looked up from the device ids).
-__device__ __forceinline__ QMat seg_mat(const MvParams& p, int seg, bool second) {
-  if (p.route.ids && seg < p.route.n_routed) {
-    const size_t r0 = (size_t)p.route.ids[seg] * (size_t)p.route.expert_rows;
+// Matrix of segment `seg` (routed experts are looked up from the chosen ids:
+// device memory, or the workgroup's own routing in LDS).
+__device__ __forceinline__ QMat seg_mat(const MvParams& p, const int32_t* ids, int seg, bool second) {
+  if (ids && seg < p.route.n_routed) {
+    const size_t r0 = (size_t)ids[seg] * (size_t)p.route.expert_rows;
     const QMat all = second ? p.route.all_B : p.route.all_A;
     QMat m;
     m.q = all.q ? all.q + r0 * p.wpr : nullptr;
@@ -267,8 +268,8 @@ __device__ __forceinline__ QMat seg_mat(const MvParams& p, int seg, bool second)
   return second ? p.B[seg] : p.A[seg];
 }
 
-__device__ __forceinline__ int seg_rows(const MvParams& p, int seg) {
-  if (p.route.ids && seg < p.route.n_routed) return p.route.expert_rows;
+__device__ __forceinline__ int seg_rows(const MvParams& p, const int32_t* ids, int seg) {
+  if (ids && seg < p.route.n_routed) return p.route.expert_rows;
   return p.seg_mode == kSegRows ? p.seg_len : p.N;
 }
 
@@ -376,6 +377,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   extern __shared__ u32x4 smem[];
   __shared__ float red[2 * kWaves];
   __shared__ int last_flag;
+  __shared__ int32_t rt_ids[kMaxRoutes];
+  __shared__ float rt_w[kMaxRoutes];
 
   params_now(p);
   const int slice = blockIdx.x / p.grid_x;
@@ -392,6 +395,33 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   if (tile * kWaves >= nbands) return;  // same for every slice of this tile: no ticket needed
   const int band_stride = p.grid_x * kWaves;
 
+  // Expert ids of a gathered launch: from device memory, or chosen here
+  // (workgroup 0 stores them for the launches that follow).
+  const int32_t* rids = p.route.ids;
+  if constexpr (SEG == kSegRows) {
+    if (p.route.logits) {
+      if (wave == 0) {
+        int32_t ids[kMaxRoutes];
+        float w[kMaxRoutes];
+        route_wave(p.route.logits, p.route.n_experts, p.route.n_routed, ids, w);
+        if (lane == 0) {
+          for (int r = 0; r < p.route.n_routed; ++r) {
+            rt_ids[r] = ids[r];
+            rt_w[r] = w[r];
+            if (blockIdx.x == 0) {
+              p.route.ids_store[r] = ids[r];
+              p.route.w_store[r] = w[r];
+              if (p.route.sel_ids) p.route.sel_ids[r] = ids[r];
+              if (p.route.sel_w) p.route.sel_w[r] = w[r];
+            }
+          }
+        }
+      }
+      __syncthreads();
+      rids = rt_ids;
+    }
+  }
+
   // ---- loader: requests (band, pass) items ahead of the compute ----------
   int ld_band = tile * kWaves + wave, ld_pass = 0, ld_seg = 0;
   uint32_t qoff[R], soff[R];
@@ -405,9 +435,9 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   auto band_setup = [&](int band) {
     if constexpr (SEG == kSegRows) {
       ld_seg = (band * RPB) / p.seg_len;  // a band never straddles two row segments
-      const int rows = seg_rows(p, ld_seg);
-      ra = mat_rsrc(seg_mat(p, ld_seg, false), rows, p.wpr, p.gpr);
-      if constexpr (TWO) rb = mat_rsrc(seg_mat(p, ld_seg, true), rows, p.wpr, p.gpr);
+      const int rows = seg_rows(p, rids, ld_seg);
+      ra = mat_rsrc(seg_mat(p, rids, ld_seg, false), rows, p.wpr, p.gpr);
+      if constexpr (TWO) rb = mat_rsrc(seg_mat(p, rids, ld_seg, true), rows, p.wpr, p.gpr);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -433,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
             const int r = e / (NACC * 16), m = (e / 16) % NACC, t = e % 16;
             uint16_t v = 0;
             if (e < R * NACC * 16 && ld_row[r] >= 0) {
-              const QMat M = (SEG == kSegRows) ? seg_mat(p, ld_seg, m == 1) : (m ? p.B[0] : p.A[0]);
+              const QMat M = (SEG == kSegRows) ? seg_mat(p, rids, ld_seg, m == 1) : (m ? p.B[0] : p.A[0]);
               v = M.lut[(size_t)ld_row[r] * 16 + t];
             }
             d.lut[q] = v;
@@ -447,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
         const int s_hi = min((cpass + LPR - 1) / p.seg_len, p.nseg - 1);
         const int cg = cpass + j;
         if (s_lo == s_hi) {
-          ra = mat_rsrc(seg_mat(p, s_lo, false), seg_rows(p, s_lo), p.wpr, p.gpr);
+          ra = mat_rsrc(seg_mat(p, rids, s_lo, false), seg_rows(p, rids, s_lo), p.wpr, p.gpr);
           const int cl = cg - s_lo * p.seg_len;
           load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u,
                                        (uint32_t)(cl / CPG) * 2u, ok, d);
@@ -461,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
           }
           for (int sg = s_lo; sg <= s_hi; ++sg) {
             PD t;
-            ra = mat_rsrc(seg_mat(p, sg, false), seg_rows(p, sg), p.wpr, p.gpr);
+            ra = mat_rsrc(seg_mat(p, rids, sg, false), seg_rows(p, rids, sg), p.wpr, p.gpr);
             const int cl = cg - sg * p.seg_len;
             load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u,
                                          (uint32_t)(cl / CPG) * 2u, ok && mine == sg, t);

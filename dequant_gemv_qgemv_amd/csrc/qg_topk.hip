@@ -1,8 +1,7 @@
 // qg_topk.hip -- exact top-k of the logits on the GPU (page "Booster la
 // vitesse d'inference sur Apple Silicon", section 1: logits matvec + top-k on
-// the GPU so that only the chosen entries come back), and the MoE router's
-// top-k + softmax (GeekNews item on the 397B MoE engine, "Architecture du
-// modele": a few experts of 512 per token).
+// the GPU so that only the chosen entries come back). The MoE router's top-k
+// (route_wave, qg_common.h) uses the same key order.
 //
 // Order: larger value first; equal values by lower index; -0 equals +0; NaN is
 // below every number. Each (value, index) becomes one unique 64-bit key that
@@ -14,7 +13,7 @@
 // once a digit bin holds exactly the keys still wanted) and writes them to the
 // workspace; the last workgroup to finish (integer ticket) repeats the
 // selection over all candidates and sorts the k winners.
-#include "qg_internal.h"
+#include "qg_common.h"
 
 namespace qg {
 namespace {
@@ -23,22 +22,6 @@ constexpr int kTkThreads = 1024;
 constexpr int kTkPer = 8;  // keys per thread in the slice phase
 constexpr int kTkSlice = kTkThreads * kTkPer;
 constexpr int kTkMaxK = 1024;
-
-__device__ __forceinline__ uint64_t order_key(float v, uint32_t i) {
-  uint32_t u;
-  if (v != v) {
-    u = 0u;  // NaN sorts below every number
-  } else {
-    if (v == 0.0f) v = 0.0f;  // -0 and +0 are the same value
-    u = __float_as_uint(v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - i);
-}
-
-__device__ __forceinline__ uint32_t key_index(uint64_t key) {
-  return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull);
-}
 
 constexpr int kTkWaves = kTkThreads / 64;
 
@@ -296,84 +279,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   if (threadIdx.x == 0) *ticket = 0u;
 }
 
-// Router: one wave. ids = top_k of the logits (order above), w = softmax over
-// the chosen logits only. Each lane keeps its own top_k keys (sorted, in
-// registers) over batches of loads issued together; the wave then takes the
-// largest head top_k times.
-__global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ logits, int E,
-                                                   int top_k, int32_t* ids_ws, float* w_ws,
-                                                   int32_t* ids_out, float* w_out) {
-  constexpr int B = 8;  // loads per lane per batch
-  const int l = threadIdx.x;
-  uint64_t mine[kMaxRoutes];
-#pragma unroll
-  for (int r = 0; r < kMaxRoutes; ++r) mine[r] = 0ull;
-  for (int base = 0; base < E; base += 64 * B) {
-    float v[B];
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int i = base + l + 64 * j;
-      v[j] = i < E ? logits[i] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int i = base + l + 64 * j;
-      uint64_t key = i < E ? order_key(v[j], (uint32_t)i) : 0ull;
-      // insert into the lane's descending list (entries past top_k stay unused)
-#pragma unroll
-      for (int r = 0; r < kMaxRoutes; ++r) {
-        const uint64_t cur = mine[r];
-        const bool take = key > cur;
-        mine[r] = take ? key : cur;
-        key = take ? cur : key;
-      }
-    }
-  }
-  uint64_t chosen[kMaxRoutes];
-#pragma unroll
-  for (int r = 0; r < kMaxRoutes; ++r) {
-    chosen[r] = 0ull;
-    if (r < top_k) {
-      uint64_t best = mine[0];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint64_t o = __shfl_xor(best, off);
-        if (o > best) best = o;
-      }
-      chosen[r] = best;
-      if (mine[0] == best) {  // keys are unique: exactly one lane pops its head
-#pragma unroll
-        for (int q = 0; q + 1 < kMaxRoutes; ++q) mine[q] = mine[q + 1];
-        mine[kMaxRoutes - 1] = 0ull;
-      }
-    }
-  }
-  if (l == 0) {
-    float lv[kMaxRoutes];
-    float lmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < kMaxRoutes; ++r) {
-      lv[r] = r < top_k ? logits[key_index(chosen[r])] : -INFINITY;
-      lmax = fmaxf(lmax, lv[r]);
-    }
-    float den = 0.f;
-#pragma unroll
-    for (int r = 0; r < kMaxRoutes; ++r)
-      if (r < top_k) den += expf(lv[r] - lmax);
-#pragma unroll
-    for (int r = 0; r < kMaxRoutes; ++r) {
-      if (r < top_k) {
-        const int32_t id = (int32_t)key_index(chosen[r]);
-        const float w = expf(lv[r] - lmax) / den;
-        ids_ws[r] = id;
-        w_ws[r] = w;
-        if (ids_out) ids_out[r] = id;
-        if (w_out) w_out[r] = w;
-      }
-    }
-  }
-}
-
 }  // namespace
 
 size_t topk_workspace_bytes(int V, int k) {
@@ -390,13 +295,6 @@ int plan_and_launch_topk(const float* logits, int V, int k, int32_t* idx, float*
   hipLaunchKernelGGL(topk_kernel, dim3(G), dim3(kTkThreads), 0, stream, logits, V, k, cand,
                      ticket, idx, vals);
   return hipGetLastError() == hipSuccess ? 0 : -4;
-}
-
-hipError_t launch_route(const float* logits, int E, int top_k, int32_t* ids_ws, float* w_ws,
-                        int32_t* ids_out, float* w_out, hipStream_t stream) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(64), 0, stream, logits, E, top_k, ids_ws, w_ws,
-                     ids_out, w_out);
-  return hipGetLastError();
 }
 
 }  // namespace qg
