@@ -174,9 +174,10 @@ __device__ __forceinline__ void stage_load(const MvParams& p, int cg, bool have,
 // valid = inside the slice): x*g (RMSNorm weight; the 1/rms scalar is applied
 // to the row sums instead), times the K-segment routing weight, then the
 // chunk's own power-of-two range scale (affine formats) and the LDS write.
-// No block-wide reduction is involved.
+// No block-wide reduction is involved. Returns the chunk's sum of squares of
+// x (0 without a norm or outside the slice).
 template <int BITS, int FMT, int LPR>
-__device__ __forceinline__ void stage_chunk(const MvParams& p, float* v, const u32x4* g, int c,
+__device__ __forceinline__ float stage_chunk(const MvParams& p, float* v, const u32x4* g, int c,
                                             int cg, bool valid, u32x4* xl, ChunkInfo* info) {
   constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
   constexpr int PIECES = Geo<BITS, FMT>::kPieces;
@@ -220,30 +221,22 @@ __device__ __forceinline__ void stage_chunk(const MvParams& p, float* v, const u
   ci.ss = valid ? ss : 0.f;
   ci.pad = 0.f;
   info[c] = ci;
+  return ci.ss;
 }
 
 // Stages chunks [c0, c0 + nch) (zero padded to npass*LPR) when the chunks
 // outnumber the threads: each thread loops over its chunks, reading x again.
 template <int BITS, int FMT, int LPR>
-__device__ void stage_loop(const MvParams& p, int c0, int nch, int npass, u32x4* xl,
-                           ChunkInfo* info) {
+__device__ float stage_loop(const MvParams& p, int c0, int nch, int npass, u32x4* xl,
+                            ChunkInfo* info) {
   constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
+  float ss = 0.f;
   for (int c = threadIdx.x; c < npass * LPR; c += kThreads) {
     XChunk<CPC> xc;
     stage_load<CPC>(p, c0 + c, c < nch, xc);
-    stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
+    ss += stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
   }
-}
-
-// 1/sqrt(mean(x^2) + eps), summed in fixed order from the per-chunk sums of
-// squares (staged slice = all of K), by each wave on its own: no barrier, and
-// every wave and workgroup gets the same bits.
-__device__ __forceinline__ float rms_from_chunks(const MvParams& p, const ChunkInfo* info, int C) {
-  float ss = 0.f;
-  for (int c = (threadIdx.x & 63); c < C; c += 64) ss += info[c].ss;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  return 1.0f / sqrtf(ss / (float)p.K + p.eps);
+  return ss;
 }
 
 // 1/sqrt(mean(x^2) + eps) over all of K read from memory (used when this
@@ -528,23 +521,35 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   // staging then waits for x only while the weights are in flight.
   PD d[DEPTH];
   const bool whole_k = (c0 == 0 && nch == C);
+  float ss = 0.f;
   if (npass * LPR <= kThreads) {
     XChunk<CPC> xc;
     const int c = threadIdx.x;
     stage_load<CPC>(p, c0 + c, c < nch, xc);
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) issue(d[k]);
-    if (c < npass * LPR) stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
+    if (c < npass * LPR) ss = stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
   } else {
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) issue(d[k]);
-    stage_loop<BITS, FMT, LPR>(p, c0, nch, npass, xl, info);
+    ss = stage_loop<BITS, FMT, LPR>(p, c0, nch, npass, xl, info);
   }
-  // RMSNorm scalar: applied to the row sums (W (g*x) / rms = W (g*x/rms))
+  // RMSNorm scalar: applied to the row sums (W (g*x) / rms = W (g*x/rms)).
+  // Whole K staged here: each wave sums its chunks' squares before the
+  // barrier, the eight partials are added after it in fixed order.
   float rs = 1.0f;
   if (p.norm_w && !whole_k) rs = rms_all(p, red);  // contains barriers: every thread
+  if (p.norm_w && whole_k) {
+    const float w_ss = lanes_sum<64>(ss);
+    if (lane == 63) red[wave] = w_ss;
+  }
   __syncthreads();
-  if (p.norm_w && whole_k) rs = rms_from_chunks(p, info, C);
+  if (p.norm_w && whole_k) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += red[w];
+    rs = 1.0f / sqrtf(t / (float)p.K + p.eps);
+  }
 
   float acc_a[R], acc_b[R];
 #pragma unroll
