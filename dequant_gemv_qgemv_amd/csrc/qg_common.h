@@ -148,7 +148,7 @@ struct ChunkInfo {
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every descriptor's end
 
 struct MatRsrc {
-  __amdgpu_buffer_rsrc_t q, s, b;
+  __amdgpu_buffer_rsrc_t q, s, b, l;  // codes, scales, biases, tables
 };
 
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
@@ -163,12 +163,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-// Descriptors for `rows` rows of matrix M (codes, scales, biases).
+// Descriptors for `rows` rows of matrix M (codes, scales, biases, tables;
+// an absent array gets an empty descriptor).
 __device__ __forceinline__ MatRsrc mat_rsrc(const QMat& M, int rows, int wpr, int gpr) {
   MatRsrc r;
   r.q = make_rsrc(M.q, (uint32_t)rows * (uint32_t)wpr * 4u);
   r.s = make_rsrc(M.s ? (const void*)M.s : (const void*)M.q, M.s ? (uint32_t)rows * (uint32_t)gpr * 2u : 0u);
   r.b = make_rsrc(M.b ? (const void*)M.b : (const void*)M.q, M.b ? (uint32_t)rows * (uint32_t)gpr * 2u : 0u);
+  r.l = make_rsrc(M.lut ? (const void*)M.lut : (const void*)M.q, M.lut ? (uint32_t)rows * 32u : 0u);
+  return r;
+}
+
+// Descriptors over nothing: every access reads zero.
+__device__ __forceinline__ MatRsrc empty_rsrc(const MvParams& p) {
+  MatRsrc r;
+  r.q = r.s = r.b = r.l = make_rsrc(p.y, 0u);
   return r;
 }
 

@@ -224,6 +224,171 @@ __device__ __forceinline__ float stage_chunk(const MvParams& p, float* v, const 
   return ci.ss;
 }
 
+// ---------------------------------------------------------------------------
+// Staging in quarters (slices of at most 128 chunks). Each chunk's x is cut
+// into four quarters of CPC/4 consecutive values held by four adjacent lanes;
+// quarter unit u (chunk u/4, quarter u%4) belongs to thread u. Every wave of
+// the workgroup then carries a few x loads at the head of its memory queue,
+// ahead of its weight prefetch, instead of two waves carrying all of them
+// behind the weight requests of the others. The chunk's sum and maximum are
+// combined over the quad with DPP.
+
+// Makes a value pass through an empty instruction at this point: the compiler
+// must have it here and cannot hoist its uses above, so a load issued earlier
+// is waited for here and not before the loads issued in between.
+__device__ __forceinline__ void hold(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void hold(float& v) { asm volatile("" : "+v"(v)); }
+
+struct XRsrc {
+  __amdgpu_buffer_rsrc_t x, g;
+};
+
+__device__ __forceinline__ XRsrc x_rsrc(const MvParams& p) {
+  XRsrc r;
+  r.x = make_rsrc(p.x, (uint32_t)p.K * (p.x_f32 ? 4u : 2u));
+  r.g = make_rsrc(p.norm_w ? (const void*)p.norm_w : p.x, p.norm_w ? (uint32_t)p.K * 2u : 0u);
+  return r;
+}
+
+// Requests quarter unit u of the slice starting at chunk c0 (nch chunks;
+// units of padding chunks and past nunits load nothing and hold zeros). The
+// words stay raw until staging so that nothing waits for them here, and the
+// instruction count is the same on every path (fp16 x and a missing norm read
+// past their descriptors and get zeros) so that the later wait for them counts
+// exactly the loads issued after.
+template <int CPC>
+__device__ __forceinline__ void quarter_load(const MvParams& p, const XRsrc& r, int c0, int nch, int u,
+                                             int nunits, u32x4* x, u32x4* g) {
+  constexpr int QV = CPC / 4;
+  const int c = u >> 2, q = u & 3;
+  const bool ok = u < nunits && c < nch;
+  const uint32_t k0 = (uint32_t)((c0 + c) * CPC + q * QV);
+  const uint32_t es = p.x_f32 ? 4u : 2u;
+#pragma unroll
+  for (int i = 0; i < QV / 4; ++i) {
+    const bool in = ok && (p.x_f32 || i < QV / 8);
+    x[i] = __builtin_amdgcn_raw_buffer_load_b128(r.x, in ? (k0 + (p.x_f32 ? 4 : 8) * i) * es : kOOB, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < QV / 8; ++i)
+    g[i] = __builtin_amdgcn_raw_buffer_load_b128(r.g, ok && p.norm_w ? (k0 + 8 * i) * 2u : kOOB, 0, 0);
+}
+
+// Writes quarter q of a chunk's staged x (w already range scaled for the
+// affine formats): the same pieces write_pieces produces for those values.
+template <int BITS, int FMT>
+__device__ __forceinline__ void write_quarter(const float* w, u32x4* dst, int stride, int q) {
+  if constexpr (FMT == 1) {
+    dst[(2 * q) * stride] = u32x4{__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]),
+                                  __float_as_uint(w[3])};
+    dst[(2 * q + 1) * stride] = u32x4{__float_as_uint(w[4]), __float_as_uint(w[5]), __float_as_uint(w[6]),
+                                      __float_as_uint(w[7])};
+  } else if constexpr (BITS == 4) {
+    constexpr float r16 = 1.0f / 16.0f;
+    dst[q * stride] = u32x4{pack_f16(w[0], w[4]), pack_f16(w[1] * r16, w[5] * r16), pack_f16(w[2], w[6]),
+                            pack_f16(w[3] * r16, w[7] * r16)};
+  } else {
+    constexpr float r4 = 0.25f, r16 = 1.0f / 16.0f, r64 = 1.0f / 64.0f, r256 = 1.0f / 256.0f;
+    dst[(2 * q) * stride] = u32x4{pack_f16(w[0], w[8]), pack_f16(w[1] * r4, w[9] * r4),
+                                  pack_f16(w[2] * r16, w[10] * r16), pack_f16(w[3] * r64, w[11] * r64)};
+    dst[(2 * q + 1) * stride] = u32x4{pack_f16(w[4] * r256, w[12] * r256), pack_f16(w[5], w[13]),
+                                      pack_f16(w[6] * r4, w[14] * r4), pack_f16(w[7] * r16, w[15] * r16)};
+  }
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+}
+
+// Stages quarter unit u (as stage_chunk does for a whole chunk). The four
+// lanes of a quad always hold the four quarters of one chunk, all inside or
+// all past nunits, so the quad reductions see only their own chunk. Returns
+// this lane's sum of squares of its raw x (0 without a norm or outside the
+// slice).
+template <int BITS, int FMT, int LPR>
+__device__ __forceinline__ float stage_quarter(const MvParams& p, const u32x4* x, const u32x4* g, int u,
+                                               int nunits, int c0, int nch, u32x4* xl, ChunkInfo* info) {
+  constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
+  constexpr int QV = CPC / 4;
+  constexpr int PIECES = Geo<BITS, FMT>::kPieces;
+  const int c = u >> 2, q = u & 3;
+  const bool valid = u < nunits && c < nch;
+  float v[QV];
+  if (p.x_f32) {
+#pragma unroll
+    for (int i = 0; i < QV / 4; ++i) {
+      v[4 * i] = __uint_as_float(x[i].x);
+      v[4 * i + 1] = __uint_as_float(x[i].y);
+      v[4 * i + 2] = __uint_as_float(x[i].z);
+      v[4 * i + 3] = __uint_as_float(x[i].w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < QV / 8; ++i) {
+      const uint32_t w[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x2 h = as_f16x2(w[j]);
+        v[8 * i + 2 * j] = (float)h.x;
+        v[8 * i + 2 * j + 1] = (float)h.y;
+      }
+    }
+  }
+  float ss = 0.f;
+  if (p.norm_w) {
+#pragma unroll
+    for (int i = 0; i < QV / 8; ++i) {
+      const uint32_t w[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f16x2 h = as_f16x2(w[t]);
+        const float a = v[8 * i + 2 * t], b = v[8 * i + 2 * t + 1];
+        ss = fmaf(a, a, fmaf(b, b, ss));
+        v[8 * i + 2 * t] = a * (float)h.x;
+        v[8 * i + 2 * t + 1] = b * (float)h.y;
+      }
+    }
+  }
+  float wseg = 1.0f;
+  if (valid && p.seg_mode == kSegCols && p.route.weights) {
+    const int seg = (c0 + c) / p.seg_len;
+    wseg = seg < p.route.n_routed ? p.route.weights[seg] : 1.0f;
+  }
+  float s = 0.f, m = 0.f;
+#pragma unroll
+  for (int i = 0; i < QV; ++i) {
+    v[i] *= wseg;
+    s += v[i];
+    m = fmaxf(m, fabsf(v[i]));
+  }
+  s = quad_sum(s);
+  m = quad_max(m);
+  float back = 1.0f;
+  if constexpr (FMT == 0) {
+    const float inv = range_scale(m, &back);
+#pragma unroll
+    for (int i = 0; i < QV; ++i) v[i] *= inv;
+  }
+  const float css = quad_sum(ss);
+  if (u < nunits) {
+    write_quarter<BITS, FMT>(v, xl + (c / LPR) * PIECES * LPR + (c % LPR), LPR, q);
+    if (q == 0) {
+      ChunkInfo ci;
+      ci.xsum = valid ? s : 0.f;
+      ci.back = back;
+      ci.ss = valid ? css : 0.f;
+      ci.pad = 0.f;
+      info[c] = ci;
+    }
+  }
+  return valid ? ss : 0.f;
+}
+
 // Stages chunks [c0, c0 + nch) (zero padded to npass*LPR) when the chunks
 // outnumber the threads: each thread loops over its chunks, reading x again.
 template <int BITS, int FMT, int LPR>
@@ -419,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   int ld_band = tile * kWaves + wave, ld_pass = 0, ld_seg = 0;
   uint32_t qoff[R], soff[R];
   int ld_row[R];
-  MatRsrc ra, rb;
+  MatRsrc ra = empty_rsrc(p), rb = empty_rsrc(p);
   if constexpr (SEG != kSegRows) {
     if constexpr (SEG == kSegNone) ra = mat_rsrc(p.A[0], p.N, p.wpr, p.gpr);
     if constexpr (TWO) rb = mat_rsrc(p.B[0], p.N, p.wpr, p.gpr);
@@ -445,67 +610,69 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
     }
   };
 
+  // One request of the pipeline: item (ld_band, ld_pass), or loads that
+  // return zeros past the last band. Every call issues the same instructions
+  // on one straight path (offsets past a descriptor's end where there is
+  // nothing to load): with a branch around the loads the compiler reuses the
+  // destinations of loads still in flight as temporaries on the other path,
+  // and the wait this forces drains the whole pipeline at every request.
   auto issue = [&](PD& d) {
-    if (ld_band < nbands) {
-      if (ld_pass == 0) {
-        band_setup(ld_band);
-        if constexpr (FMT == 1) {
+    const bool have = ld_band < nbands;  // uniform
+    if (have && ld_pass == 0) band_setup(ld_band);
+    if constexpr (FMT == 1) {
+      // a band's tables ride along with its first pass
+      const bool first = have && ld_pass == 0;
 #pragma unroll
-          for (int q = 0; q < LUTN; ++q) {
-            const int e = j + q * LPR;  // entry e of [R][NACC][16]
-            const int r = e / (NACC * 16), m = (e / 16) % NACC, t = e % 16;
-            uint16_t v = 0;
-            if (e < R * NACC * 16 && ld_row[r] >= 0) {
-              const QMat M = (SEG == kSegRows) ? seg_mat(p, rids, ld_seg, m == 1) : (m ? p.B[0] : p.A[0]);
-              v = M.lut[(size_t)ld_row[r] * 16 + t];
-            }
-            d.lut[q] = v;
-          }
-        }
+      for (int q = 0; q < LUTN; ++q) {
+        const int e = j + q * LPR;  // entry e of [R][NACC][16]
+        const int r = min(e / (NACC * 16), R - 1), m = (e / 16) % NACC, t = e % 16;
+        const bool ok = first && e < R * NACC * 16 && ld_row[r] >= 0;
+        const uint32_t off = ((uint32_t)ld_row[r] * 16u + (uint32_t)t) * 2u;
+        uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(ra.l, ok && m == 0 ? off : kOOB, 0, 0);
+        if constexpr (TWO) v |= __builtin_amdgcn_raw_buffer_load_b16(rb.l, ok && m == 1 ? off : kOOB, 0, 0);
+        d.lut[q] = v;
       }
-      const bool ok = ld_pass * LPR + j < nch;
-      if constexpr (SEG == kSegCols) {
-        const int cpass = c0 + ld_pass * LPR;
-        const int s_lo = min(cpass / p.seg_len, p.nseg - 1);
-        const int s_hi = min((cpass + LPR - 1) / p.seg_len, p.nseg - 1);
-        const int cg = cpass + j;
-        if (s_lo == s_hi) {
-          ra = mat_rsrc(seg_mat(p, rids, s_lo, false), seg_rows(p, rids, s_lo), p.wpr, p.gpr);
-          const int cl = cg - s_lo * p.seg_len;
-          load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u,
-                                       (uint32_t)(cl / CPG) * 2u, ok, d);
-        } else {
-          // several segments in one pass: one masked load per segment, merged
-          const int mine = cg / p.seg_len;
+    }
+    const bool ok = have && ld_pass * LPR + j < nch;
+    if constexpr (SEG == kSegCols) {
+      const int cpass = c0 + ld_pass * LPR;
+      const int s_lo = min(cpass / p.seg_len, p.nseg - 1);
+      const int s_hi = min((cpass + LPR - 1) / p.seg_len, p.nseg - 1);
+      const int cg = cpass + j;
+      if (s_lo == s_hi) {
+        ra = mat_rsrc(seg_mat(p, rids, s_lo, false), seg_rows(p, rids, s_lo), p.wpr, p.gpr);
+        const int cl = cg - s_lo * p.seg_len;
+        load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u, (uint32_t)(cl / CPG) * 2u, ok,
+                                     d);
+      } else {
+        // several segments in one pass: one masked load per segment, merged
+        const int mine = cg / p.seg_len;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          d.qa[r] = u32x4{0u, 0u, 0u, 0u};
+          d.sa[r] = d.ba[r] = 0;
+        }
+        for (int sg = s_lo; sg <= s_hi; ++sg) {
+          PD t;
+          ra = mat_rsrc(seg_mat(p, rids, sg, false), seg_rows(p, rids, sg), p.wpr, p.gpr);
+          const int cl = cg - sg * p.seg_len;
+          load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u, (uint32_t)(cl / CPG) * 2u,
+                                       ok && mine == sg, t);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            d.qa[r] = u32x4{0u, 0u, 0u, 0u};
-            d.sa[r] = d.ba[r] = 0;
-          }
-          for (int sg = s_lo; sg <= s_hi; ++sg) {
-            PD t;
-            ra = mat_rsrc(seg_mat(p, rids, sg, false), seg_rows(p, rids, sg), p.wpr, p.gpr);
-            const int cl = cg - sg * p.seg_len;
-            load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u,
-                                         (uint32_t)(cl / CPG) * 2u, ok && mine == sg, t);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-              d.qa[r] |= t.qa[r];
-              d.sa[r] |= t.sa[r];
-              d.ba[r] |= t.ba[r];
-            }
+            d.qa[r] |= t.qa[r];
+            d.sa[r] |= t.sa[r];
+            d.ba[r] |= t.ba[r];
           }
         }
-      } else {
-        load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)(ld_pass * LPR) * 16u,
-                                     (uint32_t)(ld_pass * LPR / CPG) * 2u, ok, d);
-      }
-      if (++ld_pass == npass) {
-        ld_pass = 0;
-        ld_band += band_stride;
       }
     } else {
-      load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, 0u, 0u, false, d);
+      load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)(ld_pass * LPR) * 16u,
+                                   (uint32_t)(ld_pass * LPR / CPG) * 2u, ok, d);
+    }
+    if (have && ++ld_pass == npass) {
+      ld_pass = 0;
+      ld_band += band_stride;
     }
     // Keep each request where it is issued: otherwise the compiler sinks the
     // loads next to their first use and the pipeline collapses.
@@ -522,12 +689,34 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   PD d[DEPTH];
   const bool whole_k = (c0 == 0 && nch == C);
   float ss = 0.f;
-  if (npass * LPR <= kThreads) {
+  if (4 * npass * LPR <= kThreads) {
+    // One quarter unit per thread, x requested first; x is waited for only
+    // after the weight requests are out.
+    const int nunits = 4 * npass * LPR;
+    const XRsrc xr = x_rsrc(p);
+    u32x4 qx[CPC / 16], qg[(CPC / 4 + 7) / 8];
+#pragma unroll
+    for (int i = 0; i < CPC / 16; ++i) qx[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) qg[i] = u32x4{0u, 0u, 0u, 0u};
+    quarter_load<CPC>(p, xr, c0, nch, threadIdx.x, nunits, qx, qg);
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) issue(d[k]);
+#pragma unroll
+    for (int i = 0; i < CPC / 16; ++i) hold(qx[i]);
+#pragma unroll
+    for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) hold(qg[i]);
+    ss = stage_quarter<BITS, FMT, LPR>(p, qx, qg, threadIdx.x, nunits, c0, nch, xl, info);
+  } else if (npass * LPR <= kThreads) {
     XChunk<CPC> xc;
     const int c = threadIdx.x;
     stage_load<CPC>(p, c0 + c, c < nch, xc);
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) issue(d[k]);
+#pragma unroll
+    for (int i = 0; i < CPC; ++i) hold(xc.v[i]);
+#pragma unroll
+    for (int i = 0; i < CPC / 8; ++i) hold(xc.g[i]);
     if (c < npass * LPR) ss = stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
   } else {
 #pragma unroll
@@ -582,31 +771,31 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
     for (int r = 0; r < R; ++r) acc_a[r] = acc_b[r] = 0.f;
   };
 
+  // Every slot runs on every round, also past the last band (zeros in, no
+  // stores out), so that the loads of the loop stay on one straight path.
   while (cur_band < nbands) {
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) {
-      if (cur_band < nbands) {
-        if constexpr (FMT == 1) {
-          if (cur_pass == 0) {  // this band's row tables into the sub-wave's LDS slot
-            wave_sync_lds();
+      if constexpr (FMT == 1) {
+        if (cur_pass == 0) {  // this band's row tables into the sub-wave's LDS slot
+          wave_sync_lds();
 #pragma unroll
-            for (int q = 0; q < LUTN; ++q) {
-              const int e = j + q * LPR;
-              if (e < R * NACC * 16) {
-                const int r = e / (NACC * 16), m = (e / 16) % NACC, t = e % 16;
-                tabs[(2 * r + m) * 16 + t] = f16_bits_to_f32(d[k].lut[q]);
-              }
+          for (int q = 0; q < LUTN; ++q) {
+            const int e = j + q * LPR;
+            if (e < R * NACC * 16) {
+              const int r = e / (NACC * 16), m = (e / 16) % NACC, t = e % 16;
+              tabs[(2 * r + m) * 16 + t] = f16_bits_to_f32(d[k].lut[q]);
             }
-            wave_sync_lds();
           }
+          wave_sync_lds();
         }
-        compute_pass<BITS, FMT, LPR, R, TWO, LUTN>(d[k], xl, info, cur_pass, j, tabs, acc_a, acc_b);
-        issue(d[k]);
-        if (++cur_pass == npass) {
-          finish_band(cur_band);
-          cur_pass = 0;
-          cur_band += band_stride;
-        }
+      }
+      compute_pass<BITS, FMT, LPR, R, TWO, LUTN>(d[k], xl, info, cur_pass, j, tabs, acc_a, acc_b);
+      issue(d[k]);
+      if (++cur_pass == npass) {
+        finish_band(cur_band);
+        cur_pass = 0;
+        cur_band += band_stride;
       }
     }
   }
