@@ -163,6 +163,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// ---------------------------------------------------------------------------
+// Hand-off between workgroups of one launch (split-K partials, top-k
+// candidates) without cache-wide maintenance. A device-scope fence on gfx950
+// writes back and invalidates the whole L2 of the issuing XCD, so every other
+// workgroup there fetches its activations again; a split launch slowed down
+// about threefold that way. Instead the data goes through agent-coherent
+// (sc1) stores and loads, every wave waits for its own stores to complete
+// before the workgroup barrier, and one thread then takes the ticket with a
+// relaxed device-scope atomic.
+template <typename T>
+__device__ __forceinline__ void handoff_store(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T handoff_load(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* t) {
+  return __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Descriptors for `rows` rows of matrix M (codes, scales, biases, tables;
 // an absent array gets an empty descriptor).
 __device__ __forceinline__ MatRsrc mat_rsrc(const QMat& M, int rows, int wpr, int gpr) {

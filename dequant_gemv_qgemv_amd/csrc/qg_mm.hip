@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
         if (p.splits > 1) {
 #pragma unroll
           for (int a = 0; a < NACC; ++a)
-            p.partials[(((size_t)slice * NACC + a) * M + ot) * p.N + n] = v[a];
+            handoff_store(&p.partials[(((size_t)slice * NACC + a) * M + ot) * p.N + n], v[a]);
         } else {
           finish(n, v);
         }
@@ -560,13 +560,11 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
   }
 
   if (p.splits > 1) {
+    // the partial stores are complete before the barrier, then one thread
+    // takes the ticket; the last workgroup of the tile adds the slices
+    stores_done();
     __syncthreads();
-    if (threadIdx.x == 0) {
-      __threadfence();
-      const uint32_t prev = atomicAdd(&p.tickets[tile], 1u);
-      last_flag = (prev == (uint32_t)(p.splits - 1));
-      if (last_flag) __threadfence();
-    }
+    if (threadIdx.x == 0) last_flag = take_ticket(&p.tickets[tile]) == (uint32_t)(p.splits - 1);
     __syncthreads();
     if (!last_flag) return;
     if (out_thread) {
@@ -578,13 +576,13 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
         for (int a = 0; a < NACC; ++a) {
           float t = 0.f;
           for (int s = 0; s < p.splits; ++s)
-            t += __builtin_nontemporal_load(&p.partials[(((size_t)s * NACC + a) * M + ot) * p.N + n]);
+            t += handoff_load(&p.partials[(((size_t)s * NACC + a) * M + ot) * p.N + n]);
           v[a] = t;
         }
         finish(n, v);
       }
     }
-    if (threadIdx.x == 0) p.tickets[tile] = 0u;
+    if (threadIdx.x == 0) handoff_store(&p.tickets[tile], 0u);
   }
 }
 

@@ -757,8 +757,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
         const int n = band * RPB + sub * R + r;
         if (n < p.N) {
           if (p.splits > 1) {
-            p.partials[((size_t)slice * NACC) * p.N + n] = acc_a[r];
-            if constexpr (TWO) p.partials[((size_t)slice * NACC + 1) * p.N + n] = acc_b[r];
+            handoff_store(&p.partials[((size_t)slice * NACC) * p.N + n], acc_a[r]);
+            if constexpr (TWO) handoff_store(&p.partials[((size_t)slice * NACC + 1) * p.N + n], acc_b[r]);
           } else if constexpr (TWO) {
             p.y[n] = silu(acc_a[r]) * acc_b[r];
           } else {
@@ -801,16 +801,11 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   }
 
   if (p.splits > 1) {
-    // Last workgroup of this tile adds the slices in fixed order. Every
-    // thread's partial stores complete before the barrier; one thread then
-    // publishes them device-wide and takes the ticket.
+    // Last workgroup of this tile adds the slices in fixed order: the partial
+    // stores are complete before the barrier, then one thread takes the ticket.
+    stores_done();
     __syncthreads();
-    if (threadIdx.x == 0) {
-      __threadfence();
-      const uint32_t prev = atomicAdd(&p.tickets[tile], 1u);
-      last_flag = (prev == (uint32_t)(p.splits - 1));
-      if (last_flag) __threadfence();
-    }
+    if (threadIdx.x == 0) last_flag = take_ticket(&p.tickets[tile]) == (uint32_t)(p.splits - 1);
     __syncthreads();
     if (!last_flag) return;
     for (int band = tile * kWaves + wave; band < nbands; band += band_stride) {
@@ -819,8 +814,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
         if (n < p.N) {
           float a = 0.f, b = 0.f;
           for (int s = 0; s < p.splits; ++s) {
-            a += __builtin_nontemporal_load(&p.partials[((size_t)s * NACC) * p.N + n]);
-            if constexpr (TWO) b += __builtin_nontemporal_load(&p.partials[((size_t)s * NACC + 1) * p.N + n]);
+            a += handoff_load(&p.partials[((size_t)s * NACC) * p.N + n]);
+            if constexpr (TWO) b += handoff_load(&p.partials[((size_t)s * NACC + 1) * p.N + n]);
           }
           if constexpr (TWO) {
             p.y[n] = silu(a) * b;
@@ -830,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
         }
       }
     }
-    if (threadIdx.x == 0) p.tickets[tile] = 0u;  // ready for the next call on this stream
+    if (threadIdx.x == 0) handoff_store(&p.tickets[tile], 0u);  // ready for the next call on this stream
   }
 }
 

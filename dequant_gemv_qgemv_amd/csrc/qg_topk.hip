@@ -238,17 +238,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   const uint64_t thr = kth_largest(regs, kk, sh);
   gather(regs, thr, sh);
   for (int r = threadIdx.x; r < k; r += kTkThreads)
-    cand[(size_t)b * k + r] = r < (int)kk ? sh.list[r] : 0ull;
+    handoff_store(&cand[(size_t)b * k + r], r < (int)kk ? sh.list[r] : (uint64_t)0);
 
-  // every thread's candidate stores complete before the barrier; one thread
-  // then publishes them device-wide and takes the ticket (a fence per thread
-  // would write back and invalidate the caches 1024 times)
+  // every thread's candidate stores are complete before the barrier; one
+  // thread then takes the ticket
+  stores_done();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    sh.last = atomicAdd(ticket, 1u) == gridDim.x - 1;
-    if (sh.last) __threadfence();
-  }
+  if (threadIdx.x == 0) sh.last = take_ticket(ticket) == gridDim.x - 1;
   __syncthreads();
   if (!sh.last) return;
 
@@ -259,13 +255,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
 #pragma unroll
     for (int j = 0; j < kTkPer; ++j) {
       const int i = threadIdx.x + j * kTkThreads;
-      keys[j] = i < total ? __builtin_nontemporal_load(&cand[i]) : 0ull;
+      keys[j] = i < total ? handoff_load(&cand[i]) : 0ull;
     }
     const uint64_t thr2 = kth_largest(regs, (uint32_t)k, sh);
     gather(regs, thr2, sh);
   } else {
     auto all = [&](auto&& f) {
-      for (int i = threadIdx.x; i < total; i += kTkThreads) f(__builtin_nontemporal_load(&cand[i]));
+      for (int i = threadIdx.x; i < total; i += kTkThreads) f(handoff_load(&cand[i]));
     };
     const uint64_t thr2 = kth_largest(all, (uint32_t)k, sh);
     gather(all, thr2, sh);
@@ -276,7 +272,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
     idx[r] = (int32_t)i;
     vals[r] = z[i];
   }
-  if (threadIdx.x == 0) *ticket = 0u;
+  if (threadIdx.x == 0) handoff_store(ticket, 0u);
 }
 
 }  // namespace
