@@ -18,7 +18,9 @@ primitives in the pages' order:
   with the routing weights, add the always-on shared expert with weight 1
   and the residual. (GeekNews item on the 397B MoE engine: "Architecture du
   modele", "Deferred GPU Expert Compute".)
-* logits head: z = Wlm . rmsnorm(x; g_final), then the top-k of z.
+* logits head: z = Wlm . rmsnorm(x; g_final), then the top-k of z, and
+  optionally one token drawn from the top-k (temperature, top-p, a uniform
+  number from the counter-based SplitMix64 generator).
 
 Parity status of each function: see the ``PINS`` table at the bottom.
 """
@@ -83,8 +85,15 @@ def lib():
             L.og_swiglu.argtypes = [ctypes.POINTER(_QMat), ctypes.POINTER(_QMat), I, P, P, I]
             L.og_topk.argtypes = [P, I, I, P, P]
             L.og_route.argtypes = [P, I, I, P, P]
+            D = ctypes.c_double
+            U64 = ctypes.c_uint64
+            L.og_sample.argtypes = [P, P, I, D, D, D, P]
+            L.og_splitmix64.argtypes = [U64, U64]
+            L.og_splitmix64.restype = U64
+            L.og_uniform.argtypes = [U64, U64]
+            L.og_uniform.restype = D
             for f in ("og_unpack", "og_dequant", "og_gemv", "og_rmsnorm", "og_swiglu",
-                      "og_topk", "og_route"):
+                      "og_topk", "og_route", "og_sample"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -199,6 +208,26 @@ def route(logits, k: int):
     return ids, w
 
 
+def sample(vals, idx, temperature: float, top_p: float, u: float) -> int:
+    """One token from a top-k list (vals larger first) for the uniform draw u."""
+    V = _c(vals, np.float64)
+    Ix = _c(idx, np.int32)
+    tok = np.empty(1, np.int32)
+    _check(lib().og_sample(V.ctypes.data, Ix.ctypes.data, V.size, float(temperature),
+                           float(top_p), float(u), tok.ctypes.data), "sample")
+    return int(tok[0])
+
+
+def splitmix64(seed: int, counter: int) -> int:
+    """Output number `counter` of the SplitMix64 generator started at `seed`."""
+    return int(lib().og_splitmix64(seed & (2**64 - 1), counter & (2**64 - 1)))
+
+
+def uniform(seed: int, counter: int) -> float:
+    """The draw in [0, 1) for (seed, counter): top 53 bits of splitmix64."""
+    return float(lib().og_uniform(seed & (2**64 - 1), counter & (2**64 - 1)))
+
+
 # ---------------------------------------------------------------------------
 # composed steps
 
@@ -280,4 +309,10 @@ PINS = {
     "moe_layer": "zero experts give y = x; single-expert closed form; K-concatenation identity",
     "decoder_layer": "composition of pinned primitives; zero weights give identity",
     "logits_topk": "composition of pinned gemv, rmsnorm and topk",
+    "splitmix64": "published first output for state 0 (0xE220A8397B1DCDAF); Python big-int "
+                  "arithmetic of the published mixing steps over random seeds",
+    "uniform": "range [0, 1); mean and variance of 200000 draws; top-53-bit mapping",
+    "sample": "greedy at temperature 0; two- and three-candidate closed forms of the inverse "
+              "CDF at chosen u; temperature scaling invariance; top-p prefix cut; empirical "
+              "frequencies of 40000 counter draws against softmax probabilities",
 }

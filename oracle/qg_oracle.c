@@ -29,7 +29,9 @@
  *  - SwiGLU: silu(gate) * up, silu(z) = z / (1 + exp(-z));
  *  - top-k order: larger value first, equal values by lower index; NaN is
  *    below every number;
- *  - routing weights: softmax over the selected logits only.
+ *  - routing weights: softmax over the selected logits only;
+ *  - sampling after top-k: temperature and top-p over the k candidates, one
+ *    uniform draw from the counter-based SplitMix64 generator (see og_sample).
  *
  * Everything is computed in double. Dequantized weights q*s+b are exact in
  * double (q has 4 bits, s and b are fp16). Dot products run in k order.
@@ -295,4 +297,73 @@ int og_route(const double *logits, int E, int k, int32_t *ids, double *w)
     for (int i = 0; i < k; ++i)
         w[i] = exp(logits[ids[i]] - lmax) / den;
     return 0;
+}
+
+/* ---- Sampling from the top-k ([F] section 1: logits matvec + top-k
+ * sampling on the GPU, only the token comes back) ---------------------------
+ * The page names the step, not its rule; the plainest reading, used here:
+ *   temperature == 0: the token is idx[0] (greedy);
+ *   otherwise w_i = exp((vals_i - vals_0) / temperature) for the k candidates
+ *   in their order (vals_0 is the largest); top_p keeps the shortest prefix
+ *   0..m-1 whose weight sum reaches top_p times the total (m >= 1); with S the
+ *   prefix sum, the token is idx[i] for the first i whose running sum
+ *   w_0 + ... + w_i exceeds u * S (the last prefix entry if none does).
+ * Sums run in index order. u is a uniform draw in [0, 1). */
+int og_sample(const double *vals, const int32_t *idx, int k, double temperature, double top_p,
+              double u, int32_t *token)
+{
+    if (!vals || !idx || !token || k < 1 || !(temperature >= 0.0) || !(top_p > 0.0) ||
+        !(top_p <= 1.0) || !(u >= 0.0) || !(u < 1.0))
+        return -1;
+    if (temperature == 0.0) {
+        *token = idx[0];
+        return 0;
+    }
+    double *w = (double *)malloc((size_t)k * sizeof(double));
+    if (!w)
+        return -1;
+    double total = 0.0;
+    for (int i = 0; i < k; ++i) {
+        w[i] = exp((vals[i] - vals[0]) / temperature);
+        total += w[i];
+    }
+    int m = 0;
+    double prefix = 0.0;
+    while (m < k) {
+        prefix += w[m];
+        ++m;
+        if (prefix >= top_p * total)
+            break;
+    }
+    const double target = u * prefix;
+    double run = 0.0;
+    int pick = m - 1;
+    for (int i = 0; i < m; ++i) {
+        run += w[i];
+        if (run > target) {
+            pick = i;
+            break;
+        }
+    }
+    free(w);
+    *token = idx[pick];
+    return 0;
+}
+
+/* Counter-based SplitMix64 (G. Steele, D. Lea, C. Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014): output number `counter`
+ * (0, 1, 2, ...) of the generator started from state `seed` is the mixing
+ * function applied to seed + (counter + 1) * 0x9E3779B97F4A7C15. */
+uint64_t og_splitmix64(uint64_t seed, uint64_t counter)
+{
+    uint64_t z = seed + (counter + 1u) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+/* The top 53 bits of the output as a double in [0, 1). */
+double og_uniform(uint64_t seed, uint64_t counter)
+{
+    return (double)(og_splitmix64(seed, counter) >> 11) * 0x1.0p-53;
 }

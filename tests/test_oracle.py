@@ -342,3 +342,105 @@ def test_expert_bytes_match_page():
     nbytes = sum(m["q"].nbytes + m["scales"].nbytes + m["biases"].nbytes for m in mats)
     assert nbytes == c["bytes"]
     assert nbytes / 2 ** 20 == c["mib"]
+
+
+# ---------------------------------------------------------------------------
+# sampling after top-k: the counter-based generator and the draw
+
+# Outputs 0..3 of SplitMix64 started from state 0 (the reference
+# implementation accompanying Steele, Lea and Flood, OOPSLA 2014; the first
+# two are also java.util.SplittableRandom(0).nextLong() = -2152535657050944081
+# and 7960286522194355700).
+SPLITMIX64_STATE0 = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC]
+
+
+def test_splitmix64_published_outputs():
+    assert [oracle.splitmix64(0, c) for c in range(4)] == SPLITMIX64_STATE0
+    assert oracle.splitmix64(0, 0) - 2**64 == -2152535657050944081
+    assert oracle.splitmix64(0, 1) == 7960286522194355700
+
+
+def test_splitmix64_seed_is_a_state_offset():
+    # starting from state s = 0 + j*gamma gives the generator's outputs from
+    # position j on: the counter form is the sequential generator
+    gamma = 0x9E3779B97F4A7C15
+    for j in range(3):
+        for c in range(3):
+            assert oracle.splitmix64((j * gamma) % 2**64, c) == oracle.splitmix64(0, j + c)
+
+
+def test_uniform_range_and_moments():
+    n = 200000
+    u = np.array([oracle.uniform(1234, c) for c in range(n)])
+    assert u.min() >= 0.0 and u.max() < 1.0
+    assert abs(u.mean() - 0.5) < 4 * np.sqrt(1 / 12 / n)
+    assert abs(u.var() - 1 / 12) < 0.002
+    for c in (0, 1, 77):
+        assert oracle.uniform(99, c) == (oracle.splitmix64(99, c) >> 11) / 2.0**53
+
+
+def test_sample_greedy_at_zero_temperature():
+    idx = np.array([7, 3, 9], np.int32)
+    for u in (0.0, 0.5, 0.999999):
+        assert oracle.sample([2.0, 1.0, 0.5], idx, 0.0, 1.0, u) == 7
+
+
+def test_sample_inverse_cdf_closed_forms():
+    # two candidates with weights 1 and 1/3: probabilities 3/4 and 1/4
+    v2, i2 = [0.0, -np.log(3.0)], np.array([11, 22], np.int32)
+    assert oracle.sample(v2, i2, 1.0, 1.0, 0.0) == 11
+    assert oracle.sample(v2, i2, 1.0, 1.0, 0.7499) == 11
+    assert oracle.sample(v2, i2, 1.0, 1.0, 0.7501) == 22
+    assert oracle.sample(v2, i2, 1.0, 1.0, 0.999) == 22
+    # three candidates with weights 4:2:1: cumulative 4/7, 6/7, 1
+    v3, i3 = np.log([4.0, 2.0, 1.0]), np.array([5, 6, 7], np.int32)
+    assert oracle.sample(v3, i3, 1.0, 1.0, 0.5) == 5
+    assert oracle.sample(v3, i3, 1.0, 1.0, 0.6) == 6
+    assert oracle.sample(v3, i3, 1.0, 1.0, 0.85) == 6
+    assert oracle.sample(v3, i3, 1.0, 1.0, 0.86) == 7
+
+
+def test_sample_temperature_scales_the_logits():
+    rng = np.random.default_rng(5)
+    v = np.sort(rng.normal(size=8))[::-1]
+    idx = np.arange(8, dtype=np.int32)
+    for u in np.linspace(0.0, 0.99, 34):
+        assert oracle.sample(2.0 * v, idx, 2.0, 1.0, u) == oracle.sample(v, idx, 1.0, 1.0, u)
+        assert oracle.sample(v, idx, 0.5, 1.0, u) == oracle.sample(2.0 * v, idx, 1.0, 1.0, u)
+    # a very low temperature is greedy
+    assert oracle.sample(v, idx, 1e-3, 1.0, 0.999) == 0
+
+
+def test_sample_top_p_prefix():
+    v3, i3 = np.log([4.0, 2.0, 1.0]), np.array([5, 6, 7], np.int32)
+    for u in (0.0, 0.5, 0.99):  # 4/7 >= 0.5: only the first candidate is kept
+        assert oracle.sample(v3, i3, 1.0, 0.5, u) == 5
+    # top_p 0.8 keeps the first two (6/7 >= 0.8 > 4/7), renormalized 2/3, 1/3
+    assert oracle.sample(v3, i3, 1.0, 0.8, 0.66) == 5
+    assert oracle.sample(v3, i3, 1.0, 0.8, 0.67) == 6
+    assert oracle.sample(v3, i3, 1.0, 0.8, 0.99) == 6
+
+
+@pytest.mark.parametrize("top_p", [1.0, 0.9])
+def test_sample_frequencies_match_softmax(top_p):
+    rng = np.random.default_rng(11)
+    v = np.sort(rng.normal(scale=0.8, size=5))[::-1]
+    idx = np.arange(5, dtype=np.int32)
+    T = 0.7
+    p = scipy.special.softmax(v / T)
+    keep = int(np.searchsorted(np.cumsum(p), top_p * (1 - 1e-12)) + 1)
+    q = np.zeros(5)
+    q[:keep] = p[:keep] / p[:keep].sum()
+    n = 40000
+    counts = np.bincount([oracle.sample(v, idx, T, top_p, oracle.uniform(2024, c)) for c in range(n)],
+                         minlength=5)
+    sigma = np.sqrt(n * q * (1 - q)) + 1e-9
+    assert np.all(np.abs(counts - n * q) < 5 * sigma + 1), (counts, n * q)
+
+
+def test_sample_rejects_bad_arguments():
+    v, i = [1.0, 0.0], np.array([0, 1], np.int32)
+    for T, tp, u in ((-1.0, 1.0, 0.5), (1.0, 0.0, 0.5), (1.0, 1.5, 0.5), (1.0, 1.0, 1.0),
+                     (1.0, 1.0, -0.1), (float("nan"), 1.0, 0.5)):
+        with pytest.raises(Exception):
+            oracle.sample(v, i, T, tp, u)

@@ -37,6 +37,17 @@ MUTANTS = [
      "    if (va != vb)\n        return va > vb;\n    return ia > ib;"),
     ("route_bad_norm", "w[i] = exp(logits[ids[i]] - lmax) / den;",
      "w[i] = exp(logits[ids[i]] - lmax) / (den + 1.0);"),
+    ("splitmix_counter_from_zero", "uint64_t z = seed + (counter + 1u) * 0x9E3779B97F4A7C15ull;",
+     "uint64_t z = seed + counter * 0x9E3779B97F4A7C15ull;"),
+    ("splitmix_shift", "z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;",
+     "z = (z ^ (z >> 28)) * 0x94D049BB133111EBull;"),
+    ("uniform_52_bits", "return (double)(og_splitmix64(seed, counter) >> 11) * 0x1.0p-53;",
+     "return (double)(og_splitmix64(seed, counter) >> 12) * 0x1.0p-53;"),
+    ("sample_temperature_times", "w[i] = exp((vals[i] - vals[0]) / temperature);",
+     "w[i] = exp((vals[i] - vals[0]) * temperature);"),
+    ("sample_no_top_p", "if (prefix >= top_p * total)", "if (prefix >= total)"),
+    ("sample_target_not_scaled", "const double target = u * prefix;", "const double target = u;"),
+    ("sample_greedy_last", "        *token = idx[0];\n        return 0;", "        *token = idx[k - 1];\n        return 0;"),
 ]
 
 
