@@ -4,7 +4,7 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/qgemv.h. PyTorch provides device
 memory and the current stream. The functions carry the C names:
 
-  qgemv, qgemv_rmsnorm, qswiglu, qmoe_experts, qlogits_topk,
+  qgemv, qgemv_rmsnorm, qswiglu, qmoe_experts, qlogits_topk, qlogits_sample, qg_sample_topk,
   qg_workspace_bytes, qg_workspace_init, qg_status_str, qg_tune
 
 Import fails loudly when the library has not been built; there is no CPU
@@ -29,7 +29,8 @@ QG_OP_GEMV, QG_OP_GEMV_RMSNORM, QG_OP_SWIGLU, QG_OP_MOE, QG_OP_LOGITS_TOPK = 0, 
 QG_MAX_TOPK = 1024
 
 EXPORTED = ("qg_status_str", "qg_workspace_bytes", "qg_workspace_init", "qg_tune", "qgemv",
-            "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk", "qg_probe_read",
+            "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk", "qlogits_sample",
+            "qg_sample_topk", "qg_probe_read",
             "qg_probe_copy")
 
 
@@ -66,6 +67,10 @@ def lib():
         L.qswiglu.argtypes = [Q, Q, I, I, I, I, I, I, P, I, P, F, P, P, S, P]
         L.qmoe_experts.argtypes = [Q, Q, Q, I, I, I, I, I, I, Q, P, I, P, F, P, P, P, P, P, S, P]
         L.qlogits_topk.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P, S, P]
+        U64 = ctypes.c_uint64
+        L.qlogits_sample.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, F, F, U64, P, P,
+                                     P, S, P]
+        L.qg_sample_topk.argtypes = [P, P, I, F, F, U64, P, P, P]
         L.qg_probe_read.argtypes = [P, S, P, I, I, P]
         L.qg_probe_copy.argtypes = [P, P, S, I, P]
         for name in EXPORTED:
@@ -266,3 +271,40 @@ def qlogits_topk(W: QMat, x, k: int, norm_w=None, eps: float = 1e-5, logits=None
                               _xdtype(x), _ptr(norm_w), float(eps), _ptr(logits), k, _ptr(idx),
                               _ptr(vals), wp, wn, _stream(stream)), "qlogits_topk")
     return logits, idx, vals
+
+
+def qlogits_sample(W: QMat, x, k: int, temperature: float, top_p: float, seed: int,
+                   counter=None, norm_w=None, eps: float = 1e-5, logits=None, idx=None,
+                   vals=None, token=None, ws=None, stream=None):
+    """(logits, idx, vals, token): qlogits_topk, then one token drawn from the
+    k candidates (token: int32[1] on the device; counter: int64[1] on the
+    device, read and advanced by one, or None for draw number 0)."""
+    import torch
+    dev = x.device
+    if logits is None:
+        logits = torch.empty(W.N, dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(k, dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty(k, dtype=torch.float32, device=dev)
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=dev)
+    wp, wn = _ws_args(ws)
+    _check(lib().qlogits_sample(ctypes.byref(W.c), W.N, W.K, W.group, W.bits, W.fmt, _ptr(x),
+                                _xdtype(x), _ptr(norm_w), float(eps), _ptr(logits), k, _ptr(idx),
+                                _ptr(vals), float(temperature), float(top_p),
+                                seed & (2**64 - 1), _ptr(counter), _ptr(token), wp, wn,
+                                _stream(stream)), "qlogits_sample")
+    return logits, idx, vals, token
+
+
+def qg_sample_topk(idx, vals, temperature: float, top_p: float, seed: int, counter=None,
+                   token=None, stream=None):
+    """token (int32[1] on the device) drawn from a top-k list (idx, vals)."""
+    import torch
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=idx.device)
+    _check(lib().qg_sample_topk(_ptr(idx), _ptr(vals), int(idx.numel()), float(temperature),
+                                float(top_p), seed & (2**64 - 1), _ptr(counter), _ptr(token),
+                                _stream(stream)), "qg_sample_topk")
+    return token

@@ -2,6 +2,7 @@
 // argument validation, variant selection (lanes per row, rows per lane,
 // split-K) from the shape and the device's compute-unit count, and launches.
 // Nothing here allocates, frees or synchronizes.
+#include <cfloat>
 #include <atomic>
 #include <mutex>
 #include <string.h>
@@ -16,9 +17,6 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
                         const float* x, float* y, int32_t* sel_ids, float* sel_w, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 size_t moe_workspace_bytes(int F, int H, int top_k);
-int plan_and_launch_topk(const float* logits, int V, int k, int32_t* idx, float* vals, void* ws,
-                         size_t ws_bytes, hipStream_t stream);
-size_t topk_workspace_bytes(int V, int k);
 }  // namespace qg
 
 using namespace qg;
@@ -333,6 +331,22 @@ size_t mv_workspace_bytes(int N, int epi) { return mv_ws_bytes(N, 1, epi); }
 int device_ok() { return device_info().ok; }
 }  // namespace qg
 
+namespace {
+// Validates the draw arguments and fills dp. QG_OK or QG_EINVAL.
+int make_draw(float temperature, float top_p, uint64_t seed, uint64_t* counter, int32_t* token,
+              DrawParams* dp) {
+  if (!(temperature >= 0.f) || !(temperature <= FLT_MAX)) return QG_EINVAL;
+  if (!(top_p > 0.f) || !(top_p <= 1.f)) return QG_EINVAL;
+  if (!token || !aligned(token, 4) || (counter && !aligned(counter, 8))) return QG_EINVAL;
+  dp->temperature = temperature;
+  dp->top_p = top_p;
+  dp->seed = seed;
+  dp->counter = counter;
+  dp->token = token;
+  return QG_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* qg_status_str(int status) {
@@ -445,7 +459,44 @@ int qlogits_topk(const qg_qmat* W, int V, int K, int group, int bits, int fmt, c
   rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps, nullptr,
               logits, mvws, ws_bytes - tk, stream);
   if (rc) return rc;
-  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, stream);
+  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, DrawParams{}, stream);
+}
+
+int qlogits_sample(const qg_qmat* W, int V, int K, int group, int bits, int fmt, const void* x,
+                   int x_dtype, const uint16_t* norm_w, float eps, float* logits, int k,
+                   int32_t* idx, float* vals, float temperature, float top_p, uint64_t seed,
+                   uint64_t* counter, int32_t* token, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  DrawParams dp;
+  int rc = make_draw(temperature, top_p, seed, counter, token, &dp);
+  if (rc) return rc;
+  rc = check_common(V, K, 1, group, bits, fmt, x_dtype);
+  if (rc) return rc;
+  if (V < 1) return QG_EINVAL;
+  if (k < 1 || k > V) return QG_EINVAL;
+  if (k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
+  if (!logits || !idx || !vals || !aligned(logits, 4) || !aligned(idx, 4) || !aligned(vals, 4))
+    return QG_EINVAL;
+  if (norm_w && !(eps >= 0.f)) return QG_EINVAL;
+  const size_t tk = topk_workspace_bytes(V, k);
+  const size_t need = tk + mv_ws_bytes(V, 1, kEpiStore);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return QG_EWORKSPACE;
+  char* mvws = static_cast<char*>(ws) + tk;
+  rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps, nullptr,
+              logits, mvws, ws_bytes - tk, stream);
+  if (rc) return rc;
+  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, dp, stream);
+}
+
+int qg_sample_topk(const int32_t* idx, const float* vals, int k, float temperature, float top_p,
+                   uint64_t seed, uint64_t* counter, int32_t* token, hipStream_t stream) {
+  DrawParams dp;
+  const int rc = make_draw(temperature, top_p, seed, counter, token, &dp);
+  if (rc) return rc;
+  if (k < 1) return QG_EINVAL;
+  if (k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
+  if (!idx || !vals || !aligned(idx, 4) || !aligned(vals, 4)) return QG_EINVAL;
+  return launch_sample(idx, vals, k, dp, stream) == hipSuccess ? QG_OK : QG_ELAUNCH;
 }
 
 }  // extern "C"

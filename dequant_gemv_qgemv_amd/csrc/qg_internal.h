@@ -102,6 +102,25 @@ hipError_t launch_mm(int bits, int fmt, int epi, const MvPlan& plan, const MvPar
                      hipStream_t stream);
 int mm_slice_codes();
 
+// One token drawn from a sorted top-k list (temperature, top-p, a uniform
+// number from draw `*counter` of SplitMix64 started at `seed`).
+struct DrawParams {
+  float temperature;  // 0: greedy
+  float top_p;        // in (0, 1]
+  uint64_t seed;
+  uint64_t* counter;  // device; read, then advanced by one; nullptr: draw 0
+  int32_t* token;     // device; nullptr: no draw
+};
+
+size_t topk_workspace_bytes(int V, int k);
+// Top-k of logits[V] into idx/vals; with dp.token set, the last workgroup
+// also draws the token. Returns 0, -3 (workspace too small) or -4 (launch).
+int plan_and_launch_topk(const float* logits, int V, int k, int32_t* idx, float* vals, void* ws,
+                         size_t ws_bytes, const DrawParams& dp, hipStream_t stream);
+// The draw alone, from idx/vals as the top-k writes them.
+hipError_t launch_sample(const int32_t* idx, const float* vals, int k, const DrawParams& dp,
+                         hipStream_t stream);
+
 // Fill kernel (graph-safe replacement for hipMemsetAsync).
 hipError_t launch_fill_u32(uint32_t* dst, size_t n, uint32_t value, hipStream_t stream);
 

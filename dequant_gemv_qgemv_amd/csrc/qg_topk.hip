@@ -12,7 +12,9 @@
 // slice (radix select on 8-bit digits with per-wave LDS histograms, stopping
 // once a digit bin holds exactly the keys still wanted) and writes them to the
 // workspace; the last workgroup to finish (integer ticket) repeats the
-// selection over all candidates and sorts the k winners.
+// selection over all candidates and sorts the k winners, and can then draw the
+// token from them (same page and section: top-k sampling on the GPU, only the
+// token comes back).
 #include "qg_common.h"
 
 namespace qg {
@@ -32,6 +34,7 @@ struct SelectShared {
   uint32_t digit, rem, count, done;
   int last;
 };
+static_assert(sizeof(SelectShared::hist) >= kTkMaxK * sizeof(double), "the draw reuses the histograms");
 
 // Bitwise AND and OR of all nonzero keys of the block (for the common prefix).
 template <class ForEach>
@@ -216,9 +219,86 @@ __device__ void sort_desc(uint32_t kk, SelectShared& sh) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The draw. The page names the step, not its rule; the reading used:
+// temperature 0 is greedy (the first candidate); otherwise the weights
+// w_i = exp((v_i - v_0) / T) of the k candidates in order (v_0 the largest),
+// the shortest prefix whose weight sum reaches top_p of the total (at least
+// one candidate), and the first candidate whose running sum exceeds u times
+// that prefix sum. u is the top 53 bits of output number `counter` of the
+// SplitMix64 generator started at `seed` (Steele, Lea and Flood, "Fast
+// splittable pseudorandom number generators", OOPSLA 2014: the state advances
+// by the golden-ratio increment and each output is the state through two
+// xor-shift-multiply rounds and a final xor-shift). Double precision; the
+// lanes compute the weights, one lane forms the sums in index order, so the
+// choice is that of a plain sequential evaluation (the device exp may differ
+// from another library's in the last bit, which can only matter when u lands
+// within a few ulps of a boundary).
+
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t counter) {
+  uint64_t z = seed + (counter + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Called by all 64 lanes of one wave. val(i), id(i): candidate i of k
+// (larger first). w: LDS scratch for k doubles. Every call consumes one draw
+// number (also the greedy ones), so a captured graph replayed n times draws
+// n successive numbers.
+template <class Val, class Id>
+__device__ void draw_token(int k, Val val, Id id, const DrawParams& dp, double* w) {
+  const int lane = threadIdx.x & 63;
+  const bool greedy = dp.temperature == 0.f;
+  if (!greedy) {
+    const double T = (double)dp.temperature;
+    const double v0 = (double)val(0);
+    for (int i = lane; i < k; i += 64) w[i] = exp(((double)val(i) - v0) / T);
+  }
+  wave_sync_lds();
+  if (lane == 0) {
+    const uint64_t c = dp.counter ? *dp.counter : 0ull;
+    int pick = 0;
+    if (!greedy) {
+      const double u = (double)(splitmix64_at(dp.seed, c) >> 11) * 0x1.0p-53;
+      double total = 0.0;
+      for (int i = 0; i < k; ++i) total += w[i];
+      const double cut = (double)dp.top_p * total;
+      int m = 0;
+      double prefix = 0.0;
+      while (m < k) {
+        prefix += w[m];
+        ++m;
+        if (prefix >= cut) break;
+      }
+      const double target = u * prefix;
+      double run = 0.0;
+      pick = m - 1;
+      for (int i = 0; i < m; ++i) {
+        run += w[i];
+        if (run > target) {
+          pick = i;
+          break;
+        }
+      }
+    }
+    *dp.token = id(pick);
+    if (dp.counter) *dp.counter = c + 1ull;
+  }
+}
+
+__global__ __launch_bounds__(64) void sample_kernel(const int32_t* __restrict__ idx,
+                                                    const float* __restrict__ vals, int k,
+                                                    DrawParams dp) {
+  __shared__ double w[kTkMaxK];
+  draw_token(
+      k, [&](int i) { return vals[i]; }, [&](int i) { return idx[i]; }, dp, w);
+}
+
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ z, int V, int k,
                                                           uint64_t* cand, uint32_t* ticket,
-                                                          int32_t* idx, float* vals) {
+                                                          int32_t* idx, float* vals,
+                                                          DrawParams dp) {
   __shared__ SelectShared sh;
   const int b = blockIdx.x;
   const int base = b * kTkSlice;
@@ -273,6 +353,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
     vals[r] = z[i];
   }
   if (threadIdx.x == 0) handoff_store(ticket, 0u);
+  if (dp.token) {
+    __syncthreads();  // the histograms are free: they hold the draw's weights
+    if (threadIdx.x < 64)
+      draw_token(
+          k, [&](int i) { return z[key_index(sh.list[i])]; },
+          [&](int i) { return (int32_t)key_index(sh.list[i]); }, dp,
+          reinterpret_cast<double*>(&sh.hist[0][0]));
+  }
 }
 
 }  // namespace
@@ -283,14 +371,20 @@ size_t topk_workspace_bytes(int V, int k) {
 }
 
 int plan_and_launch_topk(const float* logits, int V, int k, int32_t* idx, float* vals, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+                         size_t ws_bytes, const DrawParams& dp, hipStream_t stream) {
   if (ws_bytes < topk_workspace_bytes(V, k)) return -3;
   const int G = (V + kTkSlice - 1) / kTkSlice;
   uint32_t* ticket = static_cast<uint32_t*>(ws);
   uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 256);
   hipLaunchKernelGGL(topk_kernel, dim3(G), dim3(kTkThreads), 0, stream, logits, V, k, cand,
-                     ticket, idx, vals);
+                     ticket, idx, vals, dp);
   return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+hipError_t launch_sample(const int32_t* idx, const float* vals, int k, const DrawParams& dp,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL(sample_kernel, dim3(1), dim3(64), 0, stream, idx, vals, k, dp);
+  return hipGetLastError();
 }
 
 }  // namespace qg

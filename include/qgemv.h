@@ -198,6 +198,42 @@ int qlogits_topk(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
                  float *logits, int k, int32_t *idx, float *vals,
                  void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Sampling after top-k ([F] section 1: logits matvec + top-k sampling on the
+ * GPU, only the token comes back). The page names the step, not its rule;
+ * the rule implemented:
+ *   temperature == 0: the token is idx[0] (greedy);
+ *   otherwise w_i = exp((vals_i - vals_0) / temperature) over the k
+ *   candidates in their order (vals_0 is the largest); top_p keeps the
+ *   shortest prefix whose weight sum reaches top_p times the total (at least
+ *   one candidate); the token is idx[i] for the first i whose running sum
+ *   w_0 + ... + w_i exceeds u times that prefix sum.
+ * u = (splitmix64(seed, c) >> 11) * 2^-53 in [0, 1): output number c of the
+ * SplitMix64 generator started at state `seed` (Steele, Lea and Flood,
+ * OOPSLA 2014). c = *counter, and the call then stores c + 1 there, so every
+ * call (greedy ones too) consumes one number and a captured graph replayed n
+ * times draws n successive numbers; counter NULL means c = 0 on every call.
+ * Evaluated in double precision, sums in index order.
+ *   temperature  >= 0 and finite;   top_p  in (0, 1]
+ *   counter      device uint64, 8-byte aligned, or NULL
+ *   token        device int32 (receives the token id)
+ * QG_EINVAL for an argument outside these ranges. */
+
+/* qlogits_sample -- qlogits_topk (same arguments, workspace and results)
+ * followed by the draw from its k candidates, in the same launch as the
+ * top-k. */
+int qlogits_sample(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
+                   const void *x, int x_dtype, const uint16_t *norm_w, float eps,
+                   float *logits, int k, int32_t *idx, float *vals,
+                   float temperature, float top_p, uint64_t seed, uint64_t *counter,
+                   int32_t *token, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* qg_sample_topk -- the draw alone, from a top-k list in the form
+ * qlogits_topk writes it: idx[k] (int32), vals[k] (fp32, larger first), both
+ * device pointers. 1 <= k <= QG_MAX_TOPK. One small launch on `stream`. */
+int qg_sample_topk(const int32_t *idx, const float *vals, int k, float temperature,
+                   float top_p, uint64_t seed, uint64_t *counter, int32_t *token,
+                   hipStream_t stream);
+
 /* ---- bandwidth probes (measurement only) ---------------------------------
  * The decode matvec is bound by HBM bandwidth ([F] TL;DR: time per token is
  * about the bytes read divided by the bandwidth); these give the achievable

@@ -25,13 +25,14 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qg\w+|qgemv\w*|qswiglu|qmoe_experts|qlogits_topk)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qg\w+|qgemv\w*|qswiglu|qmoe_experts|qlogits_\w+)\s*\(",
                                  text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("qgemv", "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk",
+              "qlogits_sample", "qg_sample_topk",
               "qg_workspace_bytes", "qg_workspace_init", "qg_status_str", "qg_tune"):
         assert n in names
 
@@ -116,6 +117,26 @@ def test_other_entry_points_reject(L):
                           idx, vals, None, 0, None) == qg.QG_EUNSUPPORTED
     assert L.qlogits_topk(ctypes.byref(W), 64, 128, 64, 4, 0, X, 1, None, 0.0, logits, 8, idx,
                           vals, None, 0, None) == qg.QG_EWORKSPACE
+    # sampling: temperature, top_p, k, token and counter alignment are checked
+    # before anything else; qlogits_sample then checks like qlogits_topk
+    tok, ctr = ctypes.c_void_p(0x500000), ctypes.c_void_p(0x600000)
+    S = L.qg_sample_topk
+    for T, tp, k, t, c in ((-1.0, 1.0, 8, tok, ctr), (float("nan"), 1.0, 8, tok, ctr),
+                           (float("inf"), 1.0, 8, tok, ctr), (1.0, 0.0, 8, tok, ctr),
+                           (1.0, 1.5, 8, tok, ctr), (1.0, float("nan"), 8, tok, ctr),
+                           (1.0, 1.0, 0, tok, ctr), (1.0, 1.0, 8, None, ctr),
+                           (1.0, 1.0, 8, ctypes.c_void_p(0x500002), ctr),
+                           (1.0, 1.0, 8, tok, ctypes.c_void_p(0x600004))):
+        assert S(idx, vals, k, T, tp, 1, c, t, None) == qg.QG_EINVAL, (T, tp, k)
+    assert S(idx, vals, 1025, 1.0, 1.0, 1, ctr, tok, None) == qg.QG_EUNSUPPORTED
+    assert S(None, vals, 8, 1.0, 1.0, 1, ctr, tok, None) == qg.QG_EINVAL
+    QS = L.qlogits_sample
+    assert QS(ctypes.byref(W), 64, 128, 64, 4, 0, X, 1, None, 0.0, logits, 8, idx, vals, -1.0,
+              1.0, 1, ctr, tok, None, 0, None) == qg.QG_EINVAL
+    assert QS(ctypes.byref(W), 64, 128, 64, 4, 0, X, 1, None, 0.0, logits, 65, idx, vals, 1.0,
+              1.0, 1, ctr, tok, None, 0, None) == qg.QG_EINVAL
+    assert QS(ctypes.byref(W), 64, 128, 64, 4, 0, X, 1, None, 0.0, logits, 8, idx, vals, 1.0,
+              1.0, 1, ctr, tok, None, 0, None) == qg.QG_EWORKSPACE
     # MoE: top_k above the limit, then more than the experts
     lg = ctypes.c_void_p(0x400000)
     assert L.qmoe_experts(ctypes.byref(W), ctypes.byref(W), ctypes.byref(W), 16, 128, 256, 64, 4,
