@@ -18,6 +18,9 @@ primitives in the pages' order:
   with the routing weights, add the always-on shared expert with weight 1
   and the residual. (GeekNews item on the 397B MoE engine: "Architecture du
   modele", "Deferred GPU Expert Compute".)
+* decode attention: one query per head against a [Hkv][T][d] fp16 KV cache,
+  softmax over the positions, GQA head grouping ("Booster la vitesse
+  d'inference sur Apple Silicon", section 2 "KV cache").
 * logits head: z = Wlm . rmsnorm(x; g_final), then the top-k of z, and
   optionally one token drawn from the top-k (temperature, top-p, a uniform
   number from the counter-based SplitMix64 generator).
@@ -88,12 +91,13 @@ def lib():
             D = ctypes.c_double
             U64 = ctypes.c_uint64
             L.og_sample.argtypes = [P, P, I, D, D, D, P]
+            L.og_attention.argtypes = [P, P, P, I, I, I, I, I, D, P]
             L.og_splitmix64.argtypes = [U64, U64]
             L.og_splitmix64.restype = U64
             L.og_uniform.argtypes = [U64, U64]
             L.og_uniform.restype = D
             for f in ("og_unpack", "og_dequant", "og_gemv", "og_rmsnorm", "og_swiglu",
-                      "og_topk", "og_route", "og_sample"):
+                      "og_topk", "og_route", "og_sample", "og_attention"):
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -218,6 +222,21 @@ def sample(vals, idx, temperature: float, top_p: float, u: float) -> int:
     return int(tok[0])
 
 
+def attention(q, k_cache, v_cache, n: int, scale: float):
+    """out[H][d] of one decode step: q [H][d] (float64), caches [Hkv][T_max][d]
+    fp16, attending positions 0..n-1."""
+    Q = _c(q, np.float64)
+    Kc = np.ascontiguousarray(k_cache, np.float16)
+    Vc = np.ascontiguousarray(v_cache, np.float16)
+    H, d = Q.shape
+    Hkv, T_max, d2 = Kc.shape
+    assert d2 == d and Vc.shape == Kc.shape
+    out = np.empty((H, d), np.float64)
+    _check(lib().og_attention(Q.ctypes.data, Kc.ctypes.data, Vc.ctypes.data, H, Hkv, d, T_max,
+                              int(n), float(scale), out.ctypes.data), "attention")
+    return out
+
+
 def splitmix64(seed: int, counter: int) -> int:
     """Output number `counter` of the SplitMix64 generator started at `seed`."""
     return int(lib().og_splitmix64(seed & (2**64 - 1), counter & (2**64 - 1)))
@@ -312,6 +331,9 @@ PINS = {
     "splitmix64": "published first output for state 0 (0xE220A8397B1DCDAF); Python big-int "
                   "arithmetic of the published mixing steps over random seeds",
     "uniform": "range [0, 1); mean and variance of 200000 draws; top-53-bit mapping",
+    "attention": "one position gives V exactly; equal keys give the mean of V; scipy softmax "
+                 "times V brute force; GQA head mapping against per-group calls; scale "
+                 "invariance",
     "sample": "greedy at temperature 0; two- and three-candidate closed forms of the inverse "
               "CDF at chosen u; temperature scaling invariance; top-p prefix cut; empirical "
               "frequencies of 40000 counter draws against softmax probabilities",

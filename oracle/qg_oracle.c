@@ -367,3 +367,50 @@ double og_uniform(uint64_t seed, uint64_t counter)
 {
     return (double)(og_splitmix64(seed, counter) >> 11) * 0x1.0p-53;
 }
+
+/* ---- Decode attention over a KV cache ([F] section 2 "KV cache") --------
+ * The cache of one layer is [Hkv][T_max][d] fp16 per tensor (K and V), laid
+ * out along the time axis per head; GQA: query head h reads kv head
+ * h / (H / Hkv). One query per head (decode). For positions t = 0..n-1:
+ *   s_t = scale * sum_j q[h][j] * K[g][t][j],
+ *   out[h][j] = sum_t softmax(s)_t * V[g][t][j]   (softmax over t < n).
+ * The page asks for split-K along the cache for long contexts; splitting
+ * is an evaluation order, so the oracle is the plain definition. */
+int og_attention(const double *q, const uint16_t *k_cache, const uint16_t *v_cache, int H, int Hkv,
+                 int d, int T_max, int n, double scale, double *out)
+{
+    if (!q || !k_cache || !v_cache || !out || H < 1 || Hkv < 1 || H % Hkv || d < 1 || n < 1 ||
+        n > T_max)
+        return -1;
+    double *s = (double *)malloc((size_t)n * sizeof(double));
+    if (!s)
+        return -1;
+    const int G = H / Hkv;
+    for (int h = 0; h < H; ++h) {
+        const int g = h / G;
+        const uint16_t *Kg = k_cache + (size_t)g * T_max * d;
+        const uint16_t *Vg = v_cache + (size_t)g * T_max * d;
+        double smax = -INFINITY;
+        for (int t = 0; t < n; ++t) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j)
+                acc += q[(size_t)h * d + j] * og_half_to_double(Kg[(size_t)t * d + j]);
+            s[t] = scale * acc;
+            if (s[t] > smax)
+                smax = s[t];
+        }
+        double den = 0.0;
+        for (int t = 0; t < n; ++t) {
+            s[t] = exp(s[t] - smax);
+            den += s[t];
+        }
+        for (int j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int t = 0; t < n; ++t)
+                acc += s[t] * og_half_to_double(Vg[(size_t)t * d + j]);
+            out[(size_t)h * d + j] = acc / den;
+        }
+    }
+    free(s);
+    return 0;
+}

@@ -444,3 +444,79 @@ def test_sample_rejects_bad_arguments():
                      (1.0, 1.0, -0.1), (float("nan"), 1.0, 0.5)):
         with pytest.raises(Exception):
             oracle.sample(v, i, T, tp, u)
+
+
+# ---------------------------------------------------------------------------
+# decode attention over a [Hkv][T_max][d] fp16 cache
+
+def _cache(rng, Hkv, T_max, d):
+    return (rng.normal(size=(Hkv, T_max, d)).astype(np.float16),
+            rng.normal(size=(Hkv, T_max, d)).astype(np.float16))
+
+
+def test_attention_one_position_is_v():
+    rng = np.random.default_rng(1)
+    Kc, Vc = _cache(rng, 2, 5, 16)
+    q = rng.normal(size=(4, 16))
+    out = oracle.attention(q, Kc, Vc, 1, 0.25)
+    for h in range(4):
+        assert np.array_equal(out[h], Vc[h // 2, 0].astype(np.float64))
+
+
+def test_attention_equal_keys_average_v():
+    rng = np.random.default_rng(2)
+    Kc, Vc = _cache(rng, 1, 9, 8)
+    Kc[:] = Kc[:, :1]  # every position has the same key
+    q = rng.normal(size=(3, 8))
+    out = oracle.attention(q, Kc, Vc, 7, 0.3)
+    ref = Vc[0, :7].astype(np.float64).mean(axis=0)
+    assert np.allclose(out, ref[None, :], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("H,Hkv,d,n", [(4, 4, 16, 13), (8, 2, 32, 50), (6, 1, 8, 3)])
+def test_attention_matches_library_softmax(H, Hkv, d, n):
+    rng = np.random.default_rng(H * 100 + n)
+    Kc, Vc = _cache(rng, Hkv, n + 5, d)
+    q = rng.normal(size=(H, d))
+    scale = 1 / np.sqrt(d)
+    out = oracle.attention(q, Kc, Vc, n, scale)
+    G = H // Hkv
+    for h in range(H):
+        Kg = Kc[h // G, :n].astype(np.float64)
+        Vg = Vc[h // G, :n].astype(np.float64)
+        p = scipy.special.softmax(scale * (Kg @ q[h]))
+        assert np.allclose(out[h], p @ Vg, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_gqa_groups_are_independent_caches():
+    rng = np.random.default_rng(4)
+    Kc, Vc = _cache(rng, 2, 20, 16)
+    q = rng.normal(size=(8, 16))
+    both = oracle.attention(q, Kc, Vc, 17, 0.2)
+    for g in range(2):
+        one = oracle.attention(q[4 * g:4 * g + 4], Kc[g:g + 1], Vc[g:g + 1], 17, 0.2)
+        assert np.array_equal(both[4 * g:4 * g + 4], one)
+
+
+def test_attention_scale_and_one_hot():
+    rng = np.random.default_rng(5)
+    Kc, Vc = _cache(rng, 1, 12, 16)
+    q = rng.normal(size=(2, 16))
+    assert np.allclose(oracle.attention(q, Kc, Vc, 12, 0.5), oracle.attention(q * 0.5, Kc, Vc, 12, 1.0),
+                       rtol=1e-12, atol=1e-12)
+    # a query far along one key picks that position's value
+    q1 = 200.0 * Kc[0, 7:8].astype(np.float64)
+    Kn = Kc.copy()
+    Kn[0] /= np.linalg.norm(Kn[0].astype(np.float64), axis=1, keepdims=True).astype(np.float16)
+    q1 = 200.0 * Kn[0, 7:8].astype(np.float64)
+    out = oracle.attention(q1, Kn, Vc, 12, 1.0)
+    assert np.allclose(out[0], Vc[0, 7].astype(np.float64), atol=1e-3)
+
+
+def test_attention_rejects_bad_shapes():
+    rng = np.random.default_rng(6)
+    Kc, Vc = _cache(rng, 2, 4, 8)
+    with pytest.raises(Exception):
+        oracle.attention(rng.normal(size=(3, 8)), Kc, Vc, 2, 1.0)  # H not a multiple of Hkv
+    with pytest.raises(Exception):
+        oracle.attention(rng.normal(size=(4, 8)), Kc, Vc, 5, 1.0)  # n > T_max

@@ -47,6 +47,11 @@ MUTANTS = [
      "w[i] = exp((vals[i] - vals[0]) * temperature);"),
     ("sample_no_top_p", "if (prefix >= top_p * total)", "if (prefix >= total)"),
     ("sample_target_not_scaled", "const double target = u * prefix;", "const double target = u;"),
+    ("attn_head_mapping", "const int g = h / G;", "const int g = h % Hkv;"),
+    ("attn_no_scale", "s[t] = scale * acc;", "s[t] = acc;"),
+    ("attn_unnormalized", "out[(size_t)h * d + j] = acc / den;", "out[(size_t)h * d + j] = acc;"),
+    ("attn_drops_last_position", "        for (int t = 0; t < n; ++t) {\n            s[t] = exp(s[t] - smax);",
+     "        for (int t = 0; t < n; ++t) {\n            if (t == n - 1) { s[t] = 0.0; continue; }\n            s[t] = exp(s[t] - smax);"),
     ("sample_greedy_last", "        *token = idx[0];\n        return 0;", "        *token = idx[k - 1];\n        return 0;"),
 ]
 
