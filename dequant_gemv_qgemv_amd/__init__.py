@@ -5,6 +5,7 @@ kernels behind the C ABI declared in include/qgemv.h. PyTorch provides device
 memory and the current stream. The functions carry the C names:
 
   qgemv, qgemv_rmsnorm, qswiglu, qmoe_experts, qlogits_topk, qlogits_sample, qg_sample_topk,
+  qattn_decode,
   qg_workspace_bytes, qg_workspace_init, qg_status_str, qg_tune
 
 Import fails loudly when the library has not been built; there is no CPU
@@ -25,12 +26,12 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_EWORKSPACE, QG_ELAUNCH, QG_EDEVICE = 0, -1, -2, -3, -4, -5
 QG_AFFINE, QG_LUT = 0, 1
 QG_F16, QG_F32 = 0, 1
-QG_OP_GEMV, QG_OP_GEMV_RMSNORM, QG_OP_SWIGLU, QG_OP_MOE, QG_OP_LOGITS_TOPK = 0, 1, 2, 3, 4
+QG_OP_GEMV, QG_OP_GEMV_RMSNORM, QG_OP_SWIGLU, QG_OP_MOE, QG_OP_LOGITS_TOPK, QG_OP_ATTN = 0, 1, 2, 3, 4, 5
 QG_MAX_TOPK = 1024
 
 EXPORTED = ("qg_status_str", "qg_workspace_bytes", "qg_workspace_init", "qg_tune", "qgemv",
             "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk", "qlogits_sample",
-            "qg_sample_topk", "qg_probe_read",
+            "qg_sample_topk", "qattn_decode", "qg_probe_read",
             "qg_probe_copy")
 
 
@@ -71,6 +72,7 @@ def lib():
         L.qlogits_sample.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, F, F, U64, P, P,
                                      P, S, P]
         L.qg_sample_topk.argtypes = [P, P, I, F, F, U64, P, P, P]
+        L.qattn_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, P, S, P]
         L.qg_probe_read.argtypes = [P, S, P, I, I, P]
         L.qg_probe_copy.argtypes = [P, P, S, I, P]
         for name in EXPORTED:
@@ -296,6 +298,23 @@ def qlogits_sample(W: QMat, x, k: int, temperature: float, top_p: float, seed: i
                                 seed & (2**64 - 1), _ptr(counter), _ptr(token), wp, wn,
                                 _stream(stream)), "qlogits_sample")
     return logits, idx, vals, token
+
+
+def qattn_decode(q, k_cache, v_cache, pos: int, scale: float, k_new=None, v_new=None, out=None,
+                 ws=None, stream=None):
+    """out [H][d] fp32: one decode step of attention. q [H][d] fp32; caches
+    [Hkv][T_max][d] fp16 (k_new/v_new [Hkv][d] fp32 are written at pos first
+    when given); positions 0..pos are attended."""
+    import torch
+    H, d = q.shape
+    Hkv, T_max, d2 = k_cache.shape
+    if out is None:
+        out = torch.empty(H, d, dtype=torch.float32, device=q.device)
+    wp, wn = _ws_args(ws)
+    _check(lib().qattn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                              H, Hkv, d, T_max, int(pos), float(scale), _ptr(out), wp, wn,
+                              _stream(stream)), "qattn_decode")
+    return out
 
 
 def qg_sample_topk(idx, vals, temperature: float, top_p: float, seed: int, counter=None,

@@ -14,7 +14,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqgemv.so")
-SOURCES = ["qg_api.hip", "qg_mv.hip", "qg_mm.hip", "qg_topk.hip", "qg_moe.hip", "qg_probe.hip"]
+SOURCES = ["qg_api.hip", "qg_mv.hip", "qg_mm.hip", "qg_topk.hip", "qg_moe.hip", "qg_attn.hip", "qg_probe.hip"]
 ARCH = "gfx950"
 
 

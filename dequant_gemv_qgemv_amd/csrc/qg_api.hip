@@ -378,6 +378,12 @@ int qg_workspace_bytes(int op, int N, int K, int M, int bits, int fmt, int k, si
       if (k < 1 || k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
       *bytes = topk_workspace_bytes(N, k) + mv_ws_bytes(N, 1, kEpiStore);
       return QG_OK;
+    case QG_OP_ATTN:
+      if (N < 1 || N % M) return QG_EINVAL;
+      if ((k != 64 && k != 128) || (N / M != 1 && N / M != 2 && N / M != 4 && N / M != 8))
+        return QG_EUNSUPPORTED;
+      *bytes = attn_ws_bytes(N, M, k);
+      return QG_OK;
     default: return QG_EINVAL;
   }
 }
@@ -486,6 +492,25 @@ int qlogits_sample(const qg_qmat* W, int V, int K, int group, int bits, int fmt,
               logits, mvws, ws_bytes - tk, stream);
   if (rc) return rc;
   return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, dp, stream);
+}
+
+int qattn_decode(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
+                 uint16_t* v_cache, int H, int Hkv, int d, int T_max, int pos, float scale,
+                 float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (H < 1 || Hkv < 1 || H % Hkv || T_max < 1 || pos < 0 || pos >= T_max) return QG_EINVAL;
+  if (!(scale == scale) || scale > FLT_MAX || scale < -FLT_MAX) return QG_EINVAL;
+  const int G = H / Hkv;
+  if ((d != 64 && d != 128) || (G != 1 && G != 2 && G != 4 && G != 8)) return QG_EUNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !out || !aligned(q, 16) || !aligned(out, 4) ||
+      !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return QG_EINVAL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return QG_EINVAL;
+  if (k_new && (!aligned(k_new, 4) || !aligned(v_new, 4))) return QG_EINVAL;
+  if ((size_t)Hkv * T_max * d * 2 > 0x7fffffffull) return QG_EUNSUPPORTED;  // 32-bit buffer offsets
+  if (!ws || ws_bytes < attn_ws_bytes(H, Hkv, d) || !aligned(ws, 256)) return QG_EWORKSPACE;
+  const hipError_t e = launch_attn(q, k_new, v_new, k_cache, v_cache, H, Hkv, d, T_max, pos,
+                                   scale, out, ws, stream);
+  return e == hipSuccess ? QG_OK : QG_ELAUNCH;
 }
 
 int qg_sample_topk(const int32_t* idx, const float* vals, int k, float temperature, float top_p,

@@ -121,6 +121,12 @@ int plan_and_launch_topk(const float* logits, int V, int k, int32_t* idx, float*
 hipError_t launch_sample(const int32_t* idx, const float* vals, int k, const DrawParams& dp,
                          hipStream_t stream);
 
+// Decode attention against a [Hkv][T_max][d] fp16 KV cache.
+size_t attn_ws_bytes(int H, int Hkv, int d);
+hipError_t launch_attn(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,
+                       uint16_t* v_cache, int H, int Hkv, int d, int T_max, int pos, float scale,
+                       float* out, void* ws, hipStream_t stream);
+
 // Fill kernel (graph-safe replacement for hipMemsetAsync).
 hipError_t launch_fill_u32(uint32_t* dst, size_t n, uint32_t value, hipStream_t stream);
 

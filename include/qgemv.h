@@ -100,6 +100,7 @@ extern "C" {
 #define QG_OP_SWIGLU 2
 #define QG_OP_MOE 3
 #define QG_OP_LOGITS_TOPK 4
+#define QG_OP_ATTN 5
 
 /* Limits. K counts columns of one matrix (for qmoe_experts: the hidden size
  * and the expert FFN size); k counts top-k entries. */
@@ -123,7 +124,10 @@ const char *qg_status_str(int status);
 /* Bytes of workspace that `op` needs for these sizes (0 if none). For
  * QG_OP_MOE, N is the hidden size, K the expert FFN size and k the number of
  * routed experts; for QG_OP_LOGITS_TOPK, N is the vocabulary size and k the
- * number of entries returned. Returns a status; *bytes is set on QG_OK. */
+ * number of entries returned; for QG_OP_ATTN, N is the number of query heads
+ * H, M the number of kv heads Hkv and k the head dimension d (K, bits and fmt
+ * are not used; the size does not depend on the cache length). Returns a
+ * status; *bytes is set on QG_OK. */
 int qg_workspace_bytes(int op, int N, int K, int M, int bits, int fmt, int k, size_t *bytes);
 
 /* Clears a workspace before its first use (a fill kernel on `stream`, safe to
@@ -233,6 +237,25 @@ int qlogits_sample(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
 int qg_sample_topk(const int32_t *idx, const float *vals, int k, float temperature,
                    float top_p, uint64_t seed, uint64_t *counter, int32_t *token,
                    hipStream_t stream);
+
+/* qattn_decode -- one decode step of attention against a KV cache ([F]
+ * section 2 "KV cache": preallocated at its maximum length, laid out along the
+ * time axis per head, fp16; one query per head; split along the cache for
+ * long contexts; GQA).
+ *   k_cache, v_cache  [Hkv][T_max][d] fp16, device, 16-byte aligned
+ *   q                 [H][d] fp32 (16-byte aligned), out [H][d] fp32
+ *   k_new, v_new      [Hkv][d] fp32 or both NULL: when given, they are first
+ *                     written (rounded to nearest fp16) at position pos
+ * Then, for query head h and kv head g = h / (H / Hkv), over t = 0..pos:
+ *   out[h] = sum_t softmax_t(scale * q[h] . K[g][t]) V[g][t].
+ * d must be 64 or 128 and H / Hkv one of 1, 2, 4, 8 (QG_EUNSUPPORTED
+ * otherwise); 0 <= pos < T_max. The workspace (QG_OP_ATTN) holds the
+ * slices' partial results and one ticket per kv head; cleared once with
+ * qg_workspace_init, it is left clear by every call. out must not overlap q
+ * or the caches. */
+int qattn_decode(const float *q, const float *k_new, const float *v_new, uint16_t *k_cache,
+                 uint16_t *v_cache, int H, int Hkv, int d, int T_max, int pos, float scale,
+                 float *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- bandwidth probes (measurement only) ---------------------------------
  * The decode matvec is bound by HBM bandwidth ([F] TL;DR: time per token is

@@ -25,14 +25,14 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qg\w+|qgemv\w*|qswiglu|qmoe_experts|qlogits_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qg\w+|qgemv\w*|qswiglu|qmoe_experts|qlogits_\w+|qattn_\w+)\s*\(",
                                  text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("qgemv", "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk",
-              "qlogits_sample", "qg_sample_topk",
+              "qlogits_sample", "qg_sample_topk", "qattn_decode",
               "qg_workspace_bytes", "qg_workspace_init", "qg_status_str", "qg_tune"):
         assert n in names
 
@@ -137,6 +137,24 @@ def test_other_entry_points_reject(L):
               1.0, 1, ctr, tok, None, 0, None) == qg.QG_EINVAL
     assert QS(ctypes.byref(W), 64, 128, 64, 4, 0, X, 1, None, 0.0, logits, 8, idx, vals, 1.0,
               1.0, 1, ctr, tok, None, 0, None) == qg.QG_EWORKSPACE
+    # attention: shapes, head grouping, position range, alignment, workspace
+    A = L.qattn_decode
+    qp, kcp, vcp, op = (ctypes.c_void_p(a) for a in (0x700000, 0x800000, 0x900000, 0xA00000))
+    ok = dict(q=qp, kn=None, vn=None, kc=kcp, vc=vcp, H=32, Hkv=8, d=128, T=4096, pos=10, sc=0.1, o=op)
+    def attn(**kw):
+        a = dict(ok, **kw)
+        return A(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["H"], a["Hkv"], a["d"], a["T"],
+                 a["pos"], a["sc"], a["o"], None, 0, None)
+    assert attn(H=30) == qg.QG_EINVAL
+    assert attn(pos=4096) == qg.QG_EINVAL and attn(pos=-1) == qg.QG_EINVAL
+    assert attn(d=96) == qg.QG_EUNSUPPORTED and attn(H=48, Hkv=3) == qg.QG_EUNSUPPORTED
+    assert attn(q=ctypes.c_void_p(0x700004)) == qg.QG_EINVAL
+    assert attn(kn=ctypes.c_void_p(0xB00000)) == qg.QG_EINVAL  # k without v
+    assert attn(sc=float("nan")) == qg.QG_EINVAL
+    assert attn() == qg.QG_EWORKSPACE
+    n = ctypes.c_size_t()
+    assert L.qg_workspace_bytes(5, 32, 4096, 8, 4, 0, 128, ctypes.byref(n)) == qg.QG_OK and n.value > 0
+    assert L.qg_workspace_bytes(5, 32, 4096, 8, 4, 0, 96, ctypes.byref(n)) == qg.QG_EUNSUPPORTED
     # MoE: top_k above the limit, then more than the experts
     lg = ctypes.c_void_p(0x400000)
     assert L.qmoe_experts(ctypes.byref(W), ctypes.byref(W), ctypes.byref(W), 16, 128, 256, 64, 4,
