@@ -12,7 +12,8 @@ are captured once in a HIP graph and replayed.
 Other workloads (each prints its own line): --config stack with --bits 2 or
 --fmt 1 (16-entry table) and --m 1..8 activation vectors per step; --config
 single (one 2048 x 2048 4-bit matvec, rotating over 256 weight sets);
---config moe (one 512-expert layer, top-3 + shared expert, 60 chained router
+--config attn (decode attention of 32 Llama-shaped layers against fp16 KV
+caches of --ctx positions); --config moe (one 512-expert layer, top-3 + shared expert, 60 chained router
 draws per token over the same weights); --config qwen (28-layer hidden-1024
 stack + final norm + 151936 x 1024 logits + top-40, three model copies
 rotated per token).
@@ -592,12 +593,64 @@ def run_qwen(args, qg, synth, dev):
          step_bytes, ms, dom, copy_gbs, cpu)
 
 
+def run_attn(args, qg, synth, dev):
+    """Decode attention of a Llama-3-8B-shaped model (32 query heads, 8 kv
+    heads, head dimension 128) at context length --ctx: one step is the
+    attention of all layers at position ctx-1 (the new k/v rows are written
+    there first), each layer with its own fp16 cache, so a step reads more
+    than the 256 MB last-level cache holds for ctx >= 4096."""
+    import torch
+    H, Hkv, d, L, T = 32, 8, 128, args.layers, args.ctx
+    pos = T - 1
+    scale = 1.0 / float(np.sqrt(d))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    kc = [torch.randn(Hkv, T, d, generator=gen, device=dev).half() for _ in range(L)]
+    vc = [torch.randn(Hkv, T, d, generator=gen, device=dev).half() for _ in range(L)]
+    q = torch.randn(L, H, d, generator=gen, device=dev)
+    kn = torch.randn(L, Hkv, d, generator=gen, device=dev)
+    vn = torch.randn(L, Hkv, d, generator=gen, device=dev)
+    out = torch.empty(L, H, d, device=dev)
+    ws = qg.workspace(qg.QG_OP_ATTN, H, T, Hkv, k=d, device=dev)
+    layer_bytes = 2 * Hkv * (pos + 1) * d * 2 + 2 * H * d * 4 + 2 * Hkv * d * (4 + 2)
+
+    def step():
+        for l in range(L):
+            qg.qattn_decode(q[l], kc[l], vc[l], pos, scale, kn[l], vn[l], out=out[l], ws=ws)
+
+    run, graph = graph_step(step, not args.no_graph, out)
+    ms = time_steps(run, args.steps, args.warmup)
+    us = time_launches(step, L, not args.no_graph)
+    dom = roofline(f"qattn_decode H32/Hkv8/d128, {pos + 1} positions", layer_bytes, us)
+    copy_gbs = copy_peak(dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        hk = [kc[l].cpu().numpy() for l in range(2)]
+        hv = [vc[l].cpu().numpy() for l in range(2)]
+        hq = q[:2].double().cpu().numpy()
+
+        def work(i):
+            oracle.attention(hq[i % 2], hk[i % 2], hv[i % 2], pos + 1, scale)
+            return layer_bytes
+
+        done, n, dt = cpu_sample(work, args.cpu_seconds)
+        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} layers of attention over {pos + 1} positions in {dt:.1f} s, "
+                         "fp64 scalar C, one thread"}
+    cfg = {"layers": L, "heads": H, "kv_heads": Hkv, "head_dim": d, "context": pos + 1,
+           "graph": graph is not None}
+    emit(args, f"llama3-8b-shaped decode attention, {L} layers, fp16 KV cache, context {pos + 1}",
+         cfg, layer_bytes * L, ms, dom, copy_gbs, cpu, dtype="f32")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="stack", choices=["stack", "single", "moe", "qwen"])
+    ap.add_argument("--config", default="stack", choices=["stack", "single", "moe", "qwen", "attn"])
+    ap.add_argument("--ctx", type=int, default=8192, help="attn: context length (positions)")
     ap.add_argument("--bits", type=int, default=4, choices=[2, 4], help="stack: code width")
     ap.add_argument("--fmt", type=int, default=0, choices=[0, 1],
                     help="stack: 0 = scale + bias per group, 1 = 16-entry table per row (4-bit)")
@@ -646,8 +699,8 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    {"stack": run_stack, "single": run_single, "moe": run_moe, "qwen": run_qwen}[args.config](
-        args, qg, synth, dev)
+    {"stack": run_stack, "single": run_single, "moe": run_moe, "qwen": run_qwen,
+     "attn": run_attn}[args.config](args, qg, synth, dev)
 
 
 if __name__ == "__main__":

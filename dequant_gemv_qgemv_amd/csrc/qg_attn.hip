@@ -33,8 +33,32 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr float kNeg = -3.0e38f;  // "no position yet": finite, so empty merges stay 0 * 1
+// Slices: about kAttnTargetGroups workgroups over all kv heads, at most
+// kAttnMaxSlices per kv head, each at least kAttnMinPositions positions long.
+constexpr int kAttnTargetGroups = 256;
+constexpr int kAttnMaxSlices = 256;
+constexpr int kAttnMinPositions = 128;
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Sum over aligned groups of N lanes (8 or 16), every lane of the group
+// getting the same bits: quad swaps, then the mirror within 8 and within 16.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror: lanes of each 8 see the other quad
+  if constexpr (N == 16) v += dpp_f<0x140>(v);  // row_mirror: the other half of the row
+  return v;
+}
+
+// 2^x for x <= 0 (the softmax weights): the hardware exp2, whose results
+// below the normal range flush to zero.
+__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int G>
 struct Slot {
@@ -47,7 +71,7 @@ __device__ __forceinline__ void merge(Slot<G>& a, const float* m2, const float* 
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float M = fmaxf(a.m[h], m2[h]);
-    const float ca = exp2f(a.m[h] - M), cb = exp2f(m2[h] - M);
+    const float ca = exp2_neg(a.m[h] - M), cb = exp2_neg(m2[h] - M);
     a.l[h] = a.l[h] * ca + l2[h] * cb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a.acc[h][i] = a.acc[h][i] * ca + acc2[h][i] * cb;
@@ -87,6 +111,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const AttnParams p) 
   constexpr int STEP = PPW * kAttnWaves;
   __shared__ float red_m[kAttnWaves][G], red_l[kAttnWaves][G];
   __shared__ float red_acc[kAttnWaves][G][D];
+  __shared__ float sl_m[kAttnMaxSlices * G], sl_l[kAttnMaxSlices * G], tot_l[G];
   __shared__ int last_flag;
 
   const int g = blockIdx.x / p.nslice;
@@ -178,11 +203,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const AttnParams p) 
         float sc = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) sc = fmaf(qv[h][i], kf[i], sc);
-#pragma unroll
-        for (int m = LPP / 2; m >= 1; m >>= 1) sc += shfl_xor_f(sc, m);
+        sc = group_sum<LPP>(sc);
         const float M = valid ? fmaxf(s.m[h], sc) : s.m[h];
-        const float c = exp2f(s.m[h] - M);
-        const float e = valid ? exp2f(sc - M) : 0.f;
+        const float c = exp2_neg(s.m[h] - M);
+        const float e = valid ? exp2_neg(sc - M) : 0.f;
         s.l[h] = s.l[h] * c + e;
 #pragma unroll
         for (int i = 0; i < 8; ++i) s.acc[h][i] = fmaf(e, vf[i], s.acc[h][i] * c);
@@ -226,7 +250,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const AttnParams p) 
     float l = 0.f, a = 0.f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
-      const float c = exp2f(red_m[w][h] - M);
+      const float c = exp2_neg(red_m[w][h] - M);
       l = fmaf(red_l[w][h], c, l);
       a = fmaf(red_acc[w][h][j], c, a);
     }
@@ -249,19 +273,46 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(const AttnParams p) 
   if (threadIdx.x == 0) last_flag = take_ticket(&p.tickets[g]) == (uint32_t)(p.nslice - 1);
   __syncthreads();
   if (!last_flag) return;
+  const size_t rec = 2 + D;  // floats per (slice, head) record
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(p.partials + (size_t)g * p.nslice * G * rec, (uint32_t)(p.nslice * G * rec * 4));
+  // every slice's (max, sum) into LDS; each head's overall max, the slice
+  // weights 2^(m - max) and the weighted sum, in slice order
+  for (int e = threadIdx.x; e < p.nslice * G; e += kAttnThreads) {
+    sl_m[e] = coherent_f32(rp, (uint32_t)(e * rec * 4));
+    sl_l[e] = coherent_f32(rp, (uint32_t)((e * rec + 1) * 4));
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float M = kNeg;
+    for (int sl = 0; sl < p.nslice; ++sl) M = fmaxf(M, sl_m[sl * G + h]);
+    float l = 0.f;
+    for (int sl = 0; sl < p.nslice; ++sl) {
+      const float w = exp2_neg(sl_m[sl * G + h] - M);
+      sl_m[sl * G + h] = w;
+      l = fmaf(sl_l[sl * G + h], w, l);
+    }
+    tot_l[h] = l;
+  }
+  __syncthreads();
+  // element (h, j): the weighted sum of the slices' accumulators, sixteen
+  // loads in flight at a time
   for (int e = threadIdx.x; e < G * D; e += kAttnThreads) {
     const int h = e / D, j = e % D;
-    const float* base = p.partials + ((size_t)g * p.nslice * G + h) * (2 + D);
-    const size_t stride = (size_t)G * (2 + D);
-    float M = kNeg;
-    for (int sl = 0; sl < p.nslice; ++sl) M = fmaxf(M, handoff_load(&base[sl * stride]));
-    float l = 0.f, a = 0.f;
-    for (int sl = 0; sl < p.nslice; ++sl) {
-      const float c = exp2f(handoff_load(&base[sl * stride]) - M);
-      l = fmaf(handoff_load(&base[sl * stride + 1]), c, l);
-      a = fmaf(handoff_load(&base[sl * stride + 2 + j]), c, a);
+    float a = 0.f;
+    for (int sl0 = 0; sl0 < p.nslice; sl0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int sl = min(sl0 + u, p.nslice - 1);
+        v[u] = coherent_f32(rp, (uint32_t)(((sl * G + h) * rec + 2 + j) * 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (sl0 + u < p.nslice) a = fmaf(sl_m[(sl0 + u) * G + h], v[u], a);
     }
-    p.out[(size_t)(g * G + h) * D + j] = a / l;
+    p.out[(size_t)(g * G + h) * D + j] = a / tot_l[h];
   }
   if (threadIdx.x == 0) handoff_store(&p.tickets[g], 0u);
 }
@@ -281,12 +332,7 @@ hipError_t launch_d(int G, const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// Slices: enough workgroups to cover the device (kAttnTargetGroups over all
-// kv heads), each at least kAttnMinPositions positions long.
-constexpr int kAttnTargetGroups = 512;
-constexpr int kAttnMinPositions = 64;
-
-int attn_max_slices(int Hkv) { return (kAttnTargetGroups + Hkv - 1) / Hkv; }
+int attn_max_slices(int Hkv) { return min((kAttnTargetGroups + Hkv - 1) / Hkv, kAttnMaxSlices); }
 
 size_t attn_ws_bytes(int H, int Hkv, int d) {
   const size_t tickets = ((size_t)Hkv * 4 + 255) / 256 * 256;
@@ -310,7 +356,7 @@ hipError_t launch_attn(const float* q, const float* k_new, const float* v_new, u
   const int max_slices = attn_max_slices(Hkv);
   int per = (p.n + max_slices - 1) / max_slices;
   per = max(per, kAttnMinPositions);
-  per = (per + 63) / 64 * 64;
+  per = (per + 63) / 64 * 64;  // whole steps of the wave loop
   p.per_slice = per;
   p.nslice = (p.n + per - 1) / per;
   p.scale_log2 = scale * 1.4426950408889634f;

@@ -176,11 +176,33 @@ template <typename T>
 __device__ __forceinline__ void handoff_store(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <typename T>
-__device__ __forceinline__ T handoff_load(const T* p) {
-  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Agent-coherent (sc1) reads as ordinary buffer loads. (Relaxed atomic loads
+// compile to the same instruction, but the compiler waits for each one before
+// issuing the next, which serializes a reduction over many partials at a full
+// memory latency per term; these are issued back to back.)
+__device__ __forceinline__ float coherent_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 16));
+}
+__device__ __forceinline__ uint64_t coherent_u64(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 16);
+  return ((uint64_t)v[1] << 32) | (uint64_t)v[0];
+}
+// sum over s < n of the floats at byte offsets off0 + s * stride, added in s
+// order, four loads in flight at a time (offsets past n read nothing).
+__device__ __forceinline__ float coherent_sum(__amdgpu_buffer_rsrc_t r, uint32_t off0, uint32_t stride,
+                                              int n) {
+  float t = 0.f;
+  for (int s0 = 0; s0 < n; s0 += 4) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = coherent_f32(r, s0 + u < n ? off0 + (uint32_t)(s0 + u) * stride : kOOB);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + u < n) t += v[u];
+  }
+  return t;
+}
 __device__ __forceinline__ uint32_t take_ticket(uint32_t* t) {
   return __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -568,17 +568,15 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
     __syncthreads();
     if (!last_flag) return;
     if (out_thread) {
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.partials, (uint32_t)(p.splits * NACC * M * p.N * 4));
+      const uint32_t sstride = (uint32_t)(NACC * M * p.N * 4);
       for (int b = tile; b < nbands; b += p.grid_x) {
         const int n = b * kBand + orow;
         if (n >= p.N) continue;
         float v[NACC];
 #pragma unroll
-        for (int a = 0; a < NACC; ++a) {
-          float t = 0.f;
-          for (int s = 0; s < p.splits; ++s)
-            t += handoff_load(&p.partials[(((size_t)s * NACC + a) * M + ot) * p.N + n]);
-          v[a] = t;
-        }
+        for (int a = 0; a < NACC; ++a)
+          v[a] = coherent_sum(rp, (uint32_t)(((a * M + ot) * p.N + n) * 4), sstride, p.splits);
         finish(n, v);
       }
     }

@@ -808,15 +808,14 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
     if (threadIdx.x == 0) last_flag = take_ticket(&p.tickets[tile]) == (uint32_t)(p.splits - 1);
     __syncthreads();
     if (!last_flag) return;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.partials, (uint32_t)(p.splits * NACC * p.N * 4));
+    const uint32_t sstride = (uint32_t)(NACC * p.N * 4);
     for (int band = tile * kWaves + wave; band < nbands; band += band_stride) {
       if (lane < RPB) {
         const int n = band * RPB + lane;
         if (n < p.N) {
-          float a = 0.f, b = 0.f;
-          for (int s = 0; s < p.splits; ++s) {
-            a += handoff_load(&p.partials[((size_t)s * NACC) * p.N + n]);
-            if constexpr (TWO) b += handoff_load(&p.partials[((size_t)s * NACC + 1) * p.N + n]);
-          }
+          const float a = coherent_sum(rp, (uint32_t)n * 4u, sstride, p.splits);
+          const float b = TWO ? coherent_sum(rp, (uint32_t)(p.N + n) * 4u, sstride, p.splits) : 0.f;
           if constexpr (TWO) {
             p.y[n] = silu(a) * b;
           } else {

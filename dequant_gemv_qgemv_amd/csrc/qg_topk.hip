@@ -331,17 +331,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   // the last workgroup: the k largest of all candidates (held in registers
   // when they fit), sorted
   const int total = gridDim.x * k;
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(cand, (uint32_t)total * 8u);
   if (total <= kTkSlice) {
 #pragma unroll
     for (int j = 0; j < kTkPer; ++j) {
       const int i = threadIdx.x + j * kTkThreads;
-      keys[j] = i < total ? handoff_load(&cand[i]) : 0ull;
+      keys[j] = coherent_u64(rc, i < total ? (uint32_t)i * 8u : kOOB);
     }
     const uint64_t thr2 = kth_largest(regs, (uint32_t)k, sh);
     gather(regs, thr2, sh);
   } else {
     auto all = [&](auto&& f) {
-      for (int i = threadIdx.x; i < total; i += kTkThreads) f(handoff_load(&cand[i]));
+      for (int i = threadIdx.x; i < total; i += kTkThreads) f(coherent_u64(rc, (uint32_t)i * 8u));
     };
     const uint64_t thr2 = kth_largest(all, (uint32_t)k, sh);
     gather(all, thr2, sh);
