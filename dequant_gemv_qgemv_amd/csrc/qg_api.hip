@@ -139,7 +139,14 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
         break;
       }
   }
-  pl.rows = g_knob[1].load() ? g_knob[1].load() : 1;
+  // Two rows per lane for long 4-bit affine rows: half the workgroups, so
+  // half the copies of a 56 KB x staged from L2 (measured on the 4096 x 14336
+  // down projection: 11.5 -> 10.9 us). Measured slower for 2-bit codes (whose
+  // kernels already hold one workgroup per CU: 9.2 -> 11.6 us) and for the
+  // table format (per-band tables).
+  pl.rows = g_knob[1].load()
+                ? g_knob[1].load()
+                : (s.bits == 4 && s.fmt == QG_AFFINE && s.seg == kSegNone && s.K >= 8192 ? 2 : 1);
   pl.depth = g_knob[4].load() ? g_knob[4].load() : 2;
   // Resident workgroups per CU: two 8-wave groups keep 16 waves in flight
   // where the kernel's registers allow it (the 2-bit kernels fit one).
