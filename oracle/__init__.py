@@ -44,6 +44,7 @@ _LIB_PATH = os.environ.get("QG_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so
 
 AFFINE = 0
 LUT = 1
+DENSE = 2
 
 
 def build(force: bool = True) -> str:

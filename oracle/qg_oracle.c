@@ -19,6 +19,9 @@
  *       shared), "Noyau de dequantification optimise FMA" (the weight is
  *       nibble*scale+bias), "Shaders de calcul Metal" and "Deferred GPU
  *       Expert Compute" (MoE combine + residual + norm on the GPU).
+ *  [B]  gist.science explainer of the BaseRT paper, "Methodologie": one
+ *       matvec variant per quantization format from Q2 to FP16, each
+ *       dequantizing inside its inner loop.
  *
  * Readings where the pages are silent:
  *  - code k of a row sits in word k/(32/bits) at bit offset bits*(k mod
@@ -31,10 +34,17 @@
  *    below every number;
  *  - routing weights: softmax over the selected logits only;
  *  - sampling after top-k: temperature and top-p over the k candidates, one
- *    uniform draw from the counter-based SplitMix64 generator (see og_sample).
+ *    uniform draw from the counter-based SplitMix64 generator (see og_sample);
+ *  - the per-format matvec variants from Q2 to FP16 (BaseRT explainer,
+ *    "Methodologie"): Q8 is the affine format with 8-bit codes, four to a
+ *    word; FP16 is the dense format, where each 16-bit field of a word is the
+ *    fp16 weight itself (two to a word, so a little-endian fp16 row is its
+ *    own packing) and there is no scale, bias or table.
  *
  * Everything is computed in double. Dequantized weights q*s+b are exact in
- * double (q has 4 bits, s and b are fp16). Dot products run in k order.
+ * double (q has at most 8 bits, s and b are fp16: q*s needs at most 19
+ * significant bits and the sum spans 2^-24..2^9). Dot products run in k
+ * order.
  */
 #include <math.h>
 #include <pthread.h>
@@ -44,6 +54,7 @@
 
 #define OG_AFFINE 0
 #define OG_LUT 1
+#define OG_DENSE 2
 
 /* A planar quantized matrix as the oracle sees it ([F] section 3 item 4). */
 typedef struct og_qmat {
@@ -51,7 +62,7 @@ typedef struct og_qmat {
     const uint16_t *scales; /* [N][K/group] fp16 bits, affine only */
     const uint16_t *biases; /* [N][K/group] fp16 bits, affine only */
     const uint16_t *lut;    /* [N][2^bits] fp16 bits, LUT only */
-    int N, K, group, bits, fmt;
+    int N, K, group, bits, fmt; /* fmt: OG_AFFINE (bits 2, 4, 8), OG_LUT, OG_DENSE (bits 16) */
 } og_qmat;
 
 /* IEEE 754 binary16 -> double, from the format definition: 1 sign bit,
@@ -76,14 +87,16 @@ static int valid_qmat(const og_qmat *W)
 {
     if (!W || !W->q || W->N < 0 || W->K < 0)
         return 0;
-    if (W->bits != 2 && W->bits != 4)
+    if (W->fmt == OG_DENSE)
+        return W->bits == 16 && (W->K * 16) % 32 == 0;
+    if (W->bits != 2 && W->bits != 4 && W->bits != 8)
         return 0;
     if (W->group <= 0 || W->K % W->group || (W->K * W->bits) % 32)
         return 0;
     if (W->fmt == OG_AFFINE)
         return W->scales && W->biases;
     if (W->fmt == OG_LUT)
-        return W->lut != NULL;
+        return W->lut != NULL && W->bits <= 4;
     return 0;
 }
 
@@ -98,11 +111,14 @@ static unsigned code_at(const og_qmat *W, int n, int k)
 }
 
 /* Dequantized weight W[n][k]: code*scale + bias for the affine format
- * ([G] FMA section writes the weight as nibble*scale + bias), or the row's
- * table entry for the LUT format ([F] section 3 item 4). */
+ * ([G] FMA section writes the weight as nibble*scale + bias), the row's
+ * table entry for the LUT format ([F] section 3 item 4), or the 16-bit field
+ * read as an fp16 number for the dense format. */
 static double weight_at(const og_qmat *W, int n, int k)
 {
     unsigned c = code_at(W, n, k);
+    if (W->fmt == OG_DENSE)
+        return og_half_to_double((uint16_t)c);
     if (W->fmt == OG_LUT)
         return og_half_to_double(W->lut[(size_t)n * (1u << W->bits) + c]);
     size_t groups_per_row = (size_t)W->K / W->group;
@@ -113,7 +129,7 @@ static double weight_at(const og_qmat *W, int n, int k)
 /* Codes of rows [0,N): codes[n*K + k]. */
 int og_unpack(const og_qmat *W, uint8_t *codes)
 {
-    if (!valid_qmat(W) || !codes)
+    if (!valid_qmat(W) || !codes || W->bits > 8)
         return -1;
     for (int n = 0; n < W->N; ++n)
         for (int k = 0; k < W->K; ++k)

@@ -14,6 +14,9 @@ Distributions (one set for every workload):
     is uniform over its range;
   * scales: fp16 ~ U(0.005, 0.02); biases: fp16 ~ U(-0.1, 0.1);
   * LUT entries: fp16 ~ N(0, 0.02) (std 0.02), 16 per output row;
+  * 8-bit codes: scales drawn as above times 15/255, so that the weights
+    cover the same range as the 4-bit ones (codes 0..255 instead of 0..15);
+  * dense fp16 weights (no codes): fp16 ~ N(0, 0.02);
   * activations: N(0, 1) rounded to fp16 (held as fp16 or widened to fp32);
   * RMSNorm weights: fp16 ~ 1 + N(0, 0.1);
   * router logits: fp32 ~ N(0, 1).
@@ -33,6 +36,8 @@ NORM_STD = 0.1
 
 AFFINE = 0
 LUT = 1
+DENSE = 2
+Q8_SCALE_FACTOR = 15.0 / 255.0
 
 
 def _tag_int(t) -> int:
@@ -68,13 +73,23 @@ def words_per_row(K: int, bits: int) -> int:
 def qmat(seed: int, tag, N: int, K: int, bits: int = 4, fmt: int = AFFINE,
          group: int = 64) -> dict:
     """A planar quantized N x K matrix: code words [N][K*bits/32] plus either
-    fp16 scales and biases [N][K/group] (affine) or a fp16 LUT [N][16]."""
+    fp16 scales and biases [N][K/group] (affine) or a fp16 LUT [N][16]; or,
+    for fmt=DENSE (bits 16), the fp16 weights themselves packed two to a
+    word (little endian, so the words are the fp16 row's bytes)."""
+    if fmt == DENSE:
+        if bits != 16 or K % 2:
+            raise ValueError("the dense format holds 16-bit fields and an even K")
+        w16 = normal(stream(seed, tag, "w"), (N, K), 0.0, LUT_STD, np.float16)
+        return {"N": N, "K": K, "bits": 16, "fmt": DENSE, "group": group,
+                "q": np.ascontiguousarray(w16).view(np.uint32), "scales": None,
+                "biases": None, "lut": None}
     if K % group or (K * bits) % 32:
         raise ValueError(f"K={K} must be a multiple of group={group}")
     out = {"N": N, "K": K, "bits": bits, "fmt": fmt, "group": group,
            "q": words(stream(seed, tag, "q"), (N, words_per_row(K, bits)))}
     if fmt == AFFINE:
-        out["scales"] = uniform(stream(seed, tag, "s"), (N, K // group), SCALE_LO, SCALE_HI)
+        f = Q8_SCALE_FACTOR if bits == 8 else 1.0
+        out["scales"] = uniform(stream(seed, tag, "s"), (N, K // group), SCALE_LO * f, SCALE_HI * f)
         out["biases"] = uniform(stream(seed, tag, "b"), (N, K // group), BIAS_LO, BIAS_HI)
         out["lut"] = None
     else:
@@ -129,6 +144,8 @@ def layer_weights(seed: int, model: dict, layer: int, bits: int = 4, fmt: int = 
 def qmat_bytes(N: int, K: int, bits: int = 4, fmt: int = AFFINE, group: int = 64) -> int:
     """Stored bytes of a planar quantized matrix (codes + scales/biases or LUT)."""
     codes = N * K * bits // 8
+    if fmt == DENSE:
+        return codes
     if fmt == AFFINE:
         return codes + N * (K // group) * 4
     return codes + N * (1 << bits) * 2

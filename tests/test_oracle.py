@@ -61,7 +61,7 @@ def test_unpack_hand_words(case):
         assert list(codes[w * per:(w + 1) * per]) == case["codes"]
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 2, 8])
 def test_unpack_roundtrip_independent_packer(bits):
     rng = np.random.default_rng(7)
     codes = rng.integers(0, 1 << bits, size=(5, 192), dtype=np.uint8)
@@ -72,7 +72,7 @@ def test_unpack_roundtrip_independent_packer(bits):
     assert np.array_equal(pack_codes(oracle.unpack(W2), bits), W2["q"])
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 2, 8])
 def test_dequant_special_cases(bits):
     rng = np.random.default_rng(11)
     N, K = 6, 256
@@ -118,7 +118,61 @@ def test_gemv_hand_cases(case):
     assert oracle.gemv(W, x)[0] == case["y"]
 
 
-@pytest.mark.parametrize("bits,fmt", [(4, synth.AFFINE), (2, synth.AFFINE), (4, synth.LUT)])
+def dense_mat(K, word, N=1):
+    return {"N": N, "K": K, "bits": 16, "fmt": synth.DENSE, "group": 64,
+            "q": np.full((N, K // 2), word, np.uint32), "scales": None, "biases": None, "lut": None}
+
+
+@pytest.mark.parametrize("case", GOLDEN["dense"])
+def test_dense_hand_cases(case):
+    x = np.ones(case["K"]) if case["x"] == "ones" else np.tile([1.0, -1.0], case["K"] // 2)
+    assert oracle.gemv(dense_mat(case["K"], int(case["word"], 16)), x)[0] == case["y"]
+
+
+def test_dense_matches_numpy_fp16():
+    """The dense format's weights are numpy's own reading of the row bytes as
+    little-endian fp16, and the matvec is numpy's matmul of them."""
+    W = synth.qmat(5, "dense", 29, 192, 16, synth.DENSE)
+    ref = W["q"].view(np.float16).astype(np.float64)
+    assert ref.shape == (29, 192)
+    assert np.array_equal(oracle.dequant(W), ref)
+    X = synth.activations(5, "densex", (2, 192), np.float32)
+    np.testing.assert_allclose(oracle.gemv(W, X), X.astype(np.float64) @ ref.T, rtol=1e-12, atol=1e-12)
+    # every fp16 pattern of one word decodes as numpy does (field 0 = low half)
+    pats = np.array([0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x8001, 0xC000, 0xFBFF], np.uint16)
+    words = pats[::2].astype(np.uint32) | (pats[1::2].astype(np.uint32) << 16)
+    D = {"N": 1, "K": 8, "bits": 16, "fmt": synth.DENSE, "group": 64, "q": words[None, :],
+         "scales": None, "biases": None, "lut": None}
+    assert np.array_equal(oracle.dequant(D)[0], pats.view(np.float16).astype(np.float64))
+
+
+def test_dense_rejects_codes_and_other_widths():
+    W = synth.qmat(1, "dbad", 2, 64, 16, synth.DENSE)
+    with pytest.raises(ValueError):
+        oracle.unpack(W)
+    W["bits"] = 8
+    with pytest.raises(ValueError):
+        oracle.gemv(W, np.ones(64))
+
+
+def test_gemv_power256_probe_decodes_8bit_codes():
+    """s=1, b=0 and x = 256^j at three columns: y_n spells out three 8-bit
+    codes (every partial sum is an integer below 2^24)."""
+    W = synth.qmat(9, "p256", 40, 192, 8)
+    W["scales"][:] = 1
+    W["biases"][:] = 0
+    codes = oracle.unpack(W)
+    cols = [5, 64, 191]
+    x = np.zeros(192)
+    for j, c in enumerate(cols):
+        x[c] = 256.0 ** j
+    y = oracle.gemv(W, x).astype(np.int64)
+    for j, c in enumerate(cols):
+        assert np.array_equal((y >> (8 * j)) & 255, codes[:, c])
+
+
+@pytest.mark.parametrize("bits,fmt", [(4, synth.AFFINE), (2, synth.AFFINE), (4, synth.LUT),
+                                      (8, synth.AFFINE)])
 def test_gemv_matches_library_matmul(bits, fmt):
     W = synth.qmat(5, ("mm", bits, fmt), 37, 320, bits, fmt)
     X = synth.activations(5, "mmx", (3, 320), np.float32)

@@ -52,6 +52,9 @@ MUTANTS = [
     ("attn_unnormalized", "out[(size_t)h * d + j] = acc / den;", "out[(size_t)h * d + j] = acc;"),
     ("attn_drops_last_position", "        for (int t = 0; t < n; ++t) {\n            s[t] = exp(s[t] - smax);",
      "        for (int t = 0; t < n; ++t) {\n            if (t == n - 1) { s[t] = 0.0; continue; }\n            s[t] = exp(s[t] - smax);"),
+    ("dense_read_as_integer", "        return og_half_to_double((uint16_t)c);", "        return (double)c;"),
+    ("byte_mask_for_8bit", "return (word >> shift) & ((1u << W->bits) - 1u);",
+     "return (word >> shift) & (W->bits == 8 ? 0x7Fu : ((1u << W->bits) - 1u));"),
     ("sample_greedy_last", "        *token = idx[0];\n        return 0;", "        *token = idx[k - 1];\n        return 0;"),
 ]
 
