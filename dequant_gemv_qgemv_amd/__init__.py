@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
 # status codes and enums (include/qgemv.h)
 QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_EWORKSPACE, QG_ELAUNCH, QG_EDEVICE = 0, -1, -2, -3, -4, -5
-QG_AFFINE, QG_LUT = 0, 1
+QG_AFFINE, QG_LUT, QG_DENSE = 0, 1, 2
 QG_F16, QG_F32 = 0, 1
 QG_OP_GEMV, QG_OP_GEMV_RMSNORM, QG_OP_SWIGLU, QG_OP_MOE, QG_OP_LOGITS_TOPK, QG_OP_ATTN = 0, 1, 2, 3, 4, 5
 QG_MAX_TOPK = 1024
@@ -113,7 +113,8 @@ def _xdtype(x):
 class QMat:
     """A planar quantized N x K matrix on the device (see include/qgemv.h).
 
-    q: int32 tensor [N, K*bits/32] holding the uint32 code words;
+    q: int32 tensor [N, K*bits/32] holding the uint32 code words (dense
+    format: the fp16 matrix [N, K] read as words);
     scales, biases: float16 [N, K/64] (affine) or None;
     lut: float16 [N, 16] (LUT format) or None."""
 

@@ -63,9 +63,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 int check_common(int N, int K, int M, int group, int bits, int fmt, int x_dtype) {
   if (N < 0 || K <= 0 || M < 1) return QG_EINVAL;
   if (x_dtype != QG_F16 && x_dtype != QG_F32) return QG_EINVAL;
-  if (fmt != QG_AFFINE && fmt != QG_LUT) return QG_EINVAL;
-  if (group != 64 || (bits != 4 && bits != 2)) return QG_EUNSUPPORTED;
+  if (fmt != QG_AFFINE && fmt != QG_LUT && fmt != QG_DENSE) return QG_EINVAL;
+  if (group != 64) return QG_EUNSUPPORTED;
+  if (fmt == QG_AFFINE && bits != 4 && bits != 2 && bits != 8) return QG_EUNSUPPORTED;
   if (fmt == QG_LUT && bits != 4) return QG_EUNSUPPORTED;
+  if (fmt == QG_DENSE && bits != 16) return QG_EUNSUPPORTED;
   if (K % 64) return QG_EINVAL;
   if (K > QG_MAX_K) return QG_EUNSUPPORTED;
   if (M > QG_MAX_M) return QG_EUNSUPPORTED;
@@ -78,7 +80,7 @@ int check_qmat(const qg_qmat* W, int fmt) {
   if (fmt == QG_AFFINE) {
     if (!W->scales || !W->biases || !aligned(W->scales, 2) || !aligned(W->biases, 2))
       return QG_EINVAL;
-  } else {
+  } else if (fmt == QG_LUT) {
     if (!W->lut || !aligned(W->lut, 2)) return QG_EINVAL;
   }
   return QG_OK;
@@ -99,9 +101,12 @@ constexpr int kMaxSplits = 16;
 constexpr size_t kLdsBudget = 64 * 1024;
 
 int codes_per_chunk(int bits) { return 128 / bits; }
-// 16-byte pieces of staged x per chunk: fp16 pairs for the affine formats,
-// fp32 for the LUT format.
-int pieces_per_chunk(int bits, int fmt) { return fmt == QG_LUT ? 8 : (bits == 4 ? 4 : 8); }
+// 16-byte pieces of staged x per chunk: fp16 pairs for the affine and dense
+// formats, fp32 for the LUT format.
+int pieces_per_chunk(int bits, int fmt) {
+  if (fmt == QG_LUT) return 8;
+  return bits == 16 ? 1 : bits == 8 ? 2 : bits == 4 ? 4 : 8;
+}
 
 // Lanes per row: the widest of 64/32/16 that leaves no lane idle in any pass,
 // else the one that idles the fewest.
@@ -191,8 +196,9 @@ size_t mv_ws_bytes(int N, int M, int epi) {
 
 // Extra requirements of the M = 2..8 kernels: each wave loads whole
 // 512-code ranges of a row's scales/biases (or its table) with 16-byte loads.
-int check_mm(const qg_qmat* A, const qg_qmat* B, int K, int fmt) {
+int check_mm(const qg_qmat* A, const qg_qmat* B, int K, int bits, int fmt) {
   if (K % 512) return QG_EUNSUPPORTED;
+  if (bits == 8 || fmt == QG_DENSE) return QG_EUNSUPPORTED;  // matrix-core path: 2- and 4-bit codes
   const qg_qmat* mats[2] = {A, B};
   for (const qg_qmat* W : mats) {
     if (!W) continue;
@@ -267,7 +273,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   const size_t ybytes = (size_t)M * N * 4;
   if (overlaps(x, xbytes, y, ybytes)) return QG_EINVAL;
   if (residual && residual != y && overlaps(residual, ybytes, y, ybytes)) return QG_EINVAL;
-  if (M > 1 && (rc = check_mm(A, epi == kEpiSwiglu ? B : nullptr, K, fmt))) return rc;
+  if (M > 1 && (rc = check_mm(A, epi == kEpiSwiglu ? B : nullptr, K, bits, fmt))) return rc;
   if (N == 0) return QG_OK;
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;

@@ -36,6 +36,14 @@ template <>
 struct Geo<4, 1> {  // LUT: 32 codes; x as 32 fp32 = 8 pieces
   static constexpr int kPerChunk = 32, kPieces = 8, kChunksPerGroup = 2;
 };
+template <>
+struct Geo<8, 0> {  // 16 codes; x as 8 fp16 pairs = 2 pieces
+  static constexpr int kPerChunk = 16, kPieces = 2, kChunksPerGroup = 4;
+};
+template <>
+struct Geo<16, 2> {  // dense fp16: 8 weights; x as 4 fp16 pairs = 1 piece (no groups)
+  static constexpr int kPerChunk = 8, kPieces = 1, kChunksPerGroup = 8;
+};
 
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   const uint32_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
@@ -52,6 +60,19 @@ __device__ __forceinline__ void write_pieces(const float* v, u32x4* dst, int str
     for (int p = 0; p < 8; ++p)
       dst[p * stride] = u32x4{__float_as_uint(v[4 * p]), __float_as_uint(v[4 * p + 1]),
                               __float_as_uint(v[4 * p + 2]), __float_as_uint(v[4 * p + 3])};
+  } else if constexpr (FMT == 2) {
+    // dense fp16: word i holds weights (2i, 2i+1)
+    dst[0] = u32x4{pack_f16(v[0], v[1]), pack_f16(v[2], v[3]), pack_f16(v[4], v[5]),
+                   pack_f16(v[6], v[7])};
+  } else if constexpr (BITS == 8) {
+    // word i holds codes 4i..4i+3; mask 0x00FF00FF takes fields (0, 2), the
+    // same mask after a shift by 8 takes fields (1, 3)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float* w = v + 8 * p;
+      dst[p * stride] = u32x4{pack_f16(w[0], w[2]), pack_f16(w[1], w[3]), pack_f16(w[4], w[6]),
+                              pack_f16(w[5], w[7])};
+    }
   } else if constexpr (BITS == 4) {
     constexpr float r16 = 1.0f / 16.0f;
 #pragma unroll

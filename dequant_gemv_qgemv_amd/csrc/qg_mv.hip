@@ -91,6 +91,31 @@ __device__ __forceinline__ float dot_q2(const u32x4 q, const u32x4* xr) {
   return a0 + a1;
 }
 
+// 8-bit: 2^-24 * sum_k code_k x_k over 16 codes; word i uses half of piece
+// i/2: the pairs (x0,x2) (x1,x3) of its four codes. Codes up to 255 are
+// still exact fp16 subnormals.
+__device__ __forceinline__ float dot_q8(const u32x4 q, const u32x4* xr) {
+  float a0 = 0.f, a1 = 0.f;
+  a0 = dot2(q.x & 0x00FF00FFu, xr[0].x, a0);
+  a1 = dot2((q.x >> 8) & 0x00FF00FFu, xr[0].y, a1);
+  a0 = dot2(q.y & 0x00FF00FFu, xr[0].z, a0);
+  a1 = dot2((q.y >> 8) & 0x00FF00FFu, xr[0].w, a1);
+  a0 = dot2(q.z & 0x00FF00FFu, xr[1].x, a0);
+  a1 = dot2((q.z >> 8) & 0x00FF00FFu, xr[1].y, a1);
+  a0 = dot2(q.w & 0x00FF00FFu, xr[1].z, a0);
+  a1 = dot2((q.w >> 8) & 0x00FF00FFu, xr[1].w, a1);
+  return a0 + a1;
+}
+
+// Dense fp16 weights: sum_k w_k x_k over 8 weights, x in natural order.
+__device__ __forceinline__ float dot_f16w(const u32x4 q, const u32x4* xr) {
+  float a0 = dot2(q.x, xr[0].x, 0.f);
+  float a1 = dot2(q.y, xr[0].y, 0.f);
+  a0 = dot2(q.z, xr[0].z, a0);
+  a1 = dot2(q.w, xr[0].w, a1);
+  return a0 + a1;
+}
+
 // LUT (4-bit codes, 16-entry table per row, held in this wave's LDS slot):
 // sum_k lut[code_k] x_k over the chunk's 32 codes (x in natural order, fp32).
 __device__ __forceinline__ float dot_lut(const u32x4 q, const u32x4* xr, const float* tab) {
@@ -209,7 +234,7 @@ __device__ __forceinline__ float stage_chunk(const MvParams& p, float* v, const 
     m = fmaxf(m, fabsf(v[i]));
   }
   float back = 1.0f;
-  if constexpr (FMT == 0) {
+  if constexpr (FMT != 1) {  // x staged in fp16 (affine codes, dense fp16 weights)
     const float inv = range_scale(m, &back);
 #pragma unroll
     for (int i = 0; i < CPC; ++i) v[i] *= inv;
@@ -369,7 +394,7 @@ __device__ __forceinline__ float stage_quarter(const MvParams& p, const u32x4* x
   s = quad_sum(s);
   m = quad_max(m);
   float back = 1.0f;
-  if constexpr (FMT == 0) {
+  if constexpr (FMT != 1) {
     const float inv = range_scale(m, &back);
 #pragma unroll
     for (int i = 0; i < QV; ++i) v[i] *= inv;
@@ -481,15 +506,24 @@ __device__ __forceinline__ void compute_pass(const PassData<R, TWO, LUTN>& d, co
       acc_a[r] += dot_lut(d.qa[r], xr, tabs + (2 * r) * 16);
       if constexpr (TWO) acc_b[r] += dot_lut(d.qb[r], xr, tabs + (2 * r + 1) * 16);
     }
+  } else if constexpr (FMT == 2) {
+    // dense fp16 weights: the chunk's back factor carries 2^24 for the codes'
+    // subnormal scale, which these weights do not have
+    const float back = info[pass * LPR + j].back * 0x1p-24f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc_a[r] = fmaf(dot_f16w(d.qa[r], xr), back, acc_a[r]);
+      if constexpr (TWO) acc_b[r] = fmaf(dot_f16w(d.qb[r], xr), back, acc_b[r]);
+    }
   } else {
     const float2 sb = *reinterpret_cast<const float2*>(&info[pass * LPR + j]);  // (xsum, back)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float da = (BITS == 4 ? dot_q4(d.qa[r], xr) : dot_q2(d.qa[r], xr)) * sb.y;
+      const float da = (BITS == 4 ? dot_q4(d.qa[r], xr) : BITS == 8 ? dot_q8(d.qa[r], xr) : dot_q2(d.qa[r], xr)) * sb.y;
       acc_a[r] = fmaf(f16_bits_to_f32(d.sa[r]), da, acc_a[r]);
       acc_a[r] = fmaf(f16_bits_to_f32(d.ba[r]), sb.x, acc_a[r]);
       if constexpr (TWO) {
-        const float db = (BITS == 4 ? dot_q4(d.qb[r], xr) : dot_q2(d.qb[r], xr)) * sb.y;
+        const float db = (BITS == 4 ? dot_q4(d.qb[r], xr) : BITS == 8 ? dot_q8(d.qb[r], xr) : dot_q2(d.qb[r], xr)) * sb.y;
         acc_b[r] = fmaf(f16_bits_to_f32(d.sb[r]), db, acc_b[r]);
         acc_b[r] = fmaf(f16_bits_to_f32(d.bb[r]), sb.x, acc_b[r]);
       }
@@ -689,7 +723,10 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   PD d[DEPTH];
   const bool whole_k = (c0 == 0 && nch == C);
   float ss = 0.f;
-  if (4 * npass * LPR <= kThreads) {
+  // Quarter staging needs quarters of at least 8 values (one 16-byte fp16
+  // load): chunks of 32 codes or more.
+  if (CPC >= 32 && 4 * npass * LPR <= kThreads) {
+   if constexpr (CPC >= 32) {
     // One quarter unit per thread, x requested first; x is waited for only
     // after the weight requests are out.
     const int nunits = 4 * npass * LPR;
@@ -707,6 +744,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
 #pragma unroll
     for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) hold(qg[i]);
     ss = stage_quarter<BITS, FMT, LPR>(p, qx, qg, threadIdx.x, nunits, c0, nch, xl, info);
+   }
   } else if (npass * LPR <= kThreads) {
     XChunk<CPC> xc;
     const int c = threadIdx.x;
@@ -852,7 +890,7 @@ KernelFn pick_kernel(int lpr, int rows, int depth) {
 
 template <int BITS, int FMT>
 KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows, int depth) {
-  if constexpr (FMT == 1) {  // the LUT format is not gathered by experts
+  if constexpr (FMT != 0) {  // the LUT and dense formats are not gathered by experts
     if (seg != kSegNone) return nullptr;
     if (epi == kEpiStore) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows, depth);
     if (epi == kEpiSwiglu) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegNone>(lpr, rows, depth);
@@ -875,6 +913,9 @@ namespace {
 KernelFn select_mv(int bits, int fmt, int epi, int seg, const MvPlan& plan) {
   if (bits == 4 && fmt == 0) return pick_kernel_epi<4, 0>(epi, seg, plan.lpr, plan.rows, plan.depth);
   if (bits == 2 && fmt == 0) return pick_kernel_epi<2, 0>(epi, seg, plan.lpr, plan.rows, plan.depth);
+  if (bits == 8 && fmt == 0) return pick_kernel_epi<8, 0>(epi, seg, plan.lpr, plan.rows, plan.depth);
+  if (bits == 16 && fmt == 2 && seg == kSegNone)
+    return pick_kernel_epi<16, 2>(epi, seg, plan.lpr, plan.rows, plan.depth);
   if (bits == 4 && fmt == 1 && seg == kSegNone) return pick_kernel_epi<4, 1>(epi, seg, plan.lpr, plan.rows, plan.depth);
   return nullptr;
 }

@@ -29,6 +29,10 @@
  *                 and 2-bit dequant matvecs, SwiGLU, RMS norm, and the MoE
  *                 combine + residual on the GPU, handed straight to the next
  *                 layer.
+ *  [B] gist.science explainer of the BaseRT paper ("BaseRT: Best-in-Class LLM
+ *      Inference on Apple Silicon via Native Metal"):
+ *        "Methodologie" -- one matvec variant per quantization format from
+ *                 Q2 to FP16, each dequantizing inside its inner loop.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -47,7 +51,12 @@
  *    word k/(32/bits) at bit offset bits*(k mod 32/bits), least significant
  *    field first. Affine format: scales[n][K/64], biases[n][K/64] fp16, and
  *    W[n][k] = code*scale + bias for the group of 64 consecutive k that holds
- *    k. LUT format (bits = 4 only): lut[n][16] fp16 and W[n][k] = lut[n][code].
+ *    k; bits = 2, 4 or 8 ([B] Methodologie: Q2 to Q8). LUT format (bits = 4
+ *    only): lut[n][16] fp16 and W[n][k] = lut[n][code]. Dense format (bits =
+ *    16, [B] Methodologie: FP16): each 16-bit field is the fp16 weight itself,
+ *    so q is the row-major fp16 matrix [N][K] read as words; no scales,
+ *    biases or table. group must be 64 and K a multiple of 64 for every
+ *    format.
  *  - fp16 arrays are passed as uint16_t bit patterns (IEEE 754 binary16).
  *  - Activations x are [M][K] row-major (fp16 or fp32); outputs are fp32.
  *  - Accumulation is fp32. Results are deterministic: the same call on the
@@ -56,8 +65,9 @@
  *    fp32 arrays 4-byte aligned. Otherwise QG_EINVAL.
  *  - Several activation vectors (M = 2..8; qgemv, qgemv_rmsnorm, qswiglu)
  *    run on the matrix cores ([F] section 1: the dispatcher's choice by M).
- *    They additionally need K % 512 == 0 and 16-byte aligned scales/biases
- *    (affine) or lut (LUT format); otherwise QG_EUNSUPPORTED. With
+ *    They additionally need 2- or 4-bit codes (affine or LUT), K % 512 == 0
+ *    and 16-byte aligned scales/biases (affine) or lut (LUT format);
+ *    otherwise QG_EUNSUPPORTED. With
  *    K > 4096 they need the workspace (QG_EWORKSPACE without it).
  *  - Workspace: calls that need scratch device memory take (ws, ws_bytes);
  *    qg_workspace_bytes() sizes it. The caller allocates it once, clears it
@@ -80,9 +90,10 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define QG_OK 0
 #define QG_EINVAL (-1)        /* NULL required pointer, bad size, misalignment, bad aliasing */
-#define QG_EUNSUPPORTED (-2)  /* valid but not provided: group != 64, bits not 2/4, LUT with
-                                 bits != 4, M outside [1,8], K or k beyond the limits below,
-                                 M > 1 with K % 512 != 0 or scales/biases/lut not 16-byte
+#define QG_EUNSUPPORTED (-2)  /* valid but not provided: group != 64, affine bits not 2/4/8,
+                                 LUT with bits != 4, dense with bits != 16, M outside [1,8],
+                                 K or k beyond the limits below, M > 1 with 8-bit or dense
+                                 weights, K % 512 != 0 or scales/biases/lut not 16-byte
                                  aligned */
 #define QG_EWORKSPACE (-3)    /* ws NULL or smaller than qg_workspace_bytes() */
 #define QG_ELAUNCH (-4)       /* the HIP runtime reported an error while enqueueing */
@@ -91,6 +102,7 @@ extern "C" {
 /* ---- enums ------------------------------------------------------------- */
 #define QG_AFFINE 0 /* W = code*scale + bias per group of 64 */
 #define QG_LUT 1    /* W = lut[row][code], 16 fp16 entries per row, bits = 4 */
+#define QG_DENSE 2  /* W = the fp16 value of each 16-bit field, bits = 16 ([B] FP16 variant) */
 
 #define QG_F16 0 /* activation dtype: IEEE binary16 */
 #define QG_F32 1 /* activation dtype: IEEE binary32 */
@@ -112,7 +124,7 @@ extern "C" {
 /* A planar quantized matrix ([F] section 3 item 4). Host struct holding
  * device pointers; see the layout above. Unused members must be NULL. */
 typedef struct qg_qmat {
-    const uint32_t *q;      /* [N][K*bits/32] code words, 16-byte aligned */
+    const uint32_t *q;      /* [N][K*bits/32] code words (dense: fp16 [N][K]), 16-byte aligned */
     const uint16_t *scales; /* [N][K/64] fp16 (QG_AFFINE) */
     const uint16_t *biases; /* [N][K/64] fp16 (QG_AFFINE) */
     const uint16_t *lut;    /* [N][16] fp16 (QG_LUT) */
@@ -182,7 +194,8 @@ int qswiglu(const qg_qmat *Wgate, const qg_qmat *Wup, int F, int K, int M, int g
  * (n_experts*F) x H), its down is rows [e*H, (e+1)*H) of down_all
  * ((n_experts*H) x F). shared3 = {gate, up, down} of the always-on expert
  * (F x H, F x H, H x F) or NULL for none. Routing, expert selection and the
- * combine all stay on the device. x, y: [H] fp32, y may equal x.
+ * combine all stay on the device. x, y: [H] fp32, y may equal x. Expert
+ * weights take the affine format (2-, 4- or 8-bit codes).
  * router_logits: [n_experts] fp32. sel_ids/sel_w (device, [top_k], int32 /
  * fp32) receive the routing decision when non-NULL. 1 <= top_k <= 8. */
 int qmoe_experts(const qg_qmat *gate_all, const qg_qmat *up_all, const qg_qmat *down_all,

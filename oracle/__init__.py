@@ -318,9 +318,12 @@ def logits_topk(W: dict, x, k: int, g=None, eps: float = 1e-5, nthreads: int = 1
 # What pins each function to something other than itself (tests/test_oracle.py).
 PINS = {
     "half_to_double": "all 65536 fp16 patterns against numpy's fp16 conversion",
-    "unpack": "hand words 0x76543210 / 0xFEDCBA98 / 0xE4E4E4E4; independent packer round trip",
-    "dequant": "matrices built from chosen codes, scales and biases; one-hot and 16^j probes",
-    "gemv": "hand-computed tiny cases; all-ones closed form; numpy matmul of the dense weights",
+    "unpack": "hand words 0x76543210 / 0xFEDCBA98 / 0xE4E4E4E4 / 0x03020100 / 0xFFC08001; "
+              "independent packer round trip (2-, 4- and 8-bit)",
+    "dequant": "matrices built from chosen codes, scales and biases; one-hot, 16^j and 256^j "
+               "probes; dense fp16 fields against numpy's fp16 reading of the row bytes",
+    "gemv": "hand-computed tiny cases (2-, 4-, 8-bit and dense); all-ones closed form; numpy "
+            "matmul of the dense weights",
     "rmsnorm": "constant-vector closed form; hand case [3,4]; unit mean square for eps=0",
     "silu": "z * scipy.special.expit(z)",
     "swiglu": "one-hot and zero-weight closed forms; composition of pinned gemv and silu",
