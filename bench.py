@@ -9,8 +9,9 @@ in by the q-slice of the QKV output. Weights are seeded synthetic data of
 those shapes (3.93 GB, resident in HBM before timing). The launches of a step
 are captured once in a HIP graph and replayed.
 
-Other workloads (each prints its own line): --config stack with --bits 2 or
---fmt 1 (16-entry table) and --m 1..8 activation vectors per step; --config
+Other workloads (each prints its own line): --config stack with --bits 2,
+--bits 8, --fmt 1 (16-entry table) or --bits 16 --fmt 2 (dense fp16 weights),
+and --m 1..8 activation vectors per step (2- and 4-bit codes); --config
 single (one 2048 x 2048 4-bit matvec, rotating over 256 weight sets);
 --config attn (decode attention of 32 Llama-shaped layers against fp16 KV
 caches of --ctx positions); --config moe (one 512-expert layer, top-3 + shared expert, 60 chained router
@@ -121,8 +122,13 @@ def summarize_trace(path):
     q = [r for r in rows if "qmv_kernel" in r["Kernel_Name"]]
     names = ["qkv: rmsnorm + 6144x4096", "o: 4096x4096 + residual",
              "gate.up: swiglu 2 x 14336x4096", "down: 4096x14336 + residual"]
-    nbytes = [6144 * 4096 * 9 // 16, 4096 * 4096 * 9 // 16, 2 * 14336 * 4096 * 9 // 16,
-              4096 * 14336 * 9 // 16]
+    # stored bytes per weight from the kernel's (bits, fmt) template arguments
+    targs = q[0]["Kernel_Name"].split("<", 1)[1].split(",") if q else ["4", "0"]
+    bits, fmt = int(targs[0]), int(targs[1])
+    per_w = {0: bits / 8 + 4 / 64, 1: bits / 8, 2: 2.0}[fmt]
+    lut = 32 if fmt == 1 else 0
+    nbytes = [int(n * k * per_w) + n * lut for n, k in
+              ((6144, 4096), (4096, 4096), (2 * 14336, 4096), (4096, 14336))]
     dur = [[] for _ in names]
     i = 0
     while i + 3 < len(q):
@@ -359,7 +365,8 @@ def run_stack(args, qg, synth, dev):
                 traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
-    fmt_name = {0: f"{bits}-bit g64 planar", 1: "4-bit 16-entry table per row"}[fmt]
+    fmt_name = {0: f"{bits}-bit g64 planar", 1: "4-bit 16-entry table per row",
+                2: "dense fp16 weights"}[fmt]
     kname = ("qswiglu" if M == 1 else f"qswiglu M={M} (matrix cores)") + \
         " 14336x4096 x2 (gate.up, rmsnorm)"
     dom = roofline(kname, sw_bytes, sw_us, traffic)
@@ -651,9 +658,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="stack", choices=["stack", "single", "moe", "qwen", "attn"])
     ap.add_argument("--ctx", type=int, default=8192, help="attn: context length (positions)")
-    ap.add_argument("--bits", type=int, default=4, choices=[2, 4], help="stack: code width")
-    ap.add_argument("--fmt", type=int, default=0, choices=[0, 1],
-                    help="stack: 0 = scale + bias per group, 1 = 16-entry table per row (4-bit)")
+    ap.add_argument("--bits", type=int, default=4, choices=[2, 4, 8, 16],
+                    help="stack: code width (16 = dense fp16 weights, with --fmt 2)")
+    ap.add_argument("--fmt", type=int, default=0, choices=[0, 1, 2],
+                    help="stack: 0 = scale + bias per group, 1 = 16-entry table per row (4-bit), "
+                         "2 = dense fp16 weights (--bits 16)")
     ap.add_argument("--m", type=int, default=1, help="stack: activation vectors per step (1..8)")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--seed", type=int, default=1234)
@@ -682,6 +691,12 @@ def main():
         sys.exit(2)
     if args.fmt == 1 and args.bits != 4:
         print("bench.py: the table format has 4-bit codes", file=sys.stderr)
+        sys.exit(2)
+    if (args.fmt == 2) != (args.bits == 16):
+        print("bench.py: dense fp16 weights are --bits 16 --fmt 2", file=sys.stderr)
+        sys.exit(2)
+    if args.m > 1 and args.bits not in (2, 4):
+        print("bench.py: several vectors per step run for 2- and 4-bit codes only", file=sys.stderr)
         sys.exit(2)
     if not 1 <= args.m <= 8:
         print("bench.py: --m must be 1..8", file=sys.stderr)
