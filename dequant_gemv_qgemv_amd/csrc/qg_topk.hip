@@ -20,9 +20,17 @@
 namespace qg {
 namespace {
 
+// Slices of 4096 keys: measured on MI355X for the 151936 x 1024 logits +
+// top-40 (matvec 18.0 us of it), 8192-key slices with 8 candidates per thread
+// in the last workgroup 40.5 us, 4096 / 2 35.7 us, 2048 / 4 36.1 us,
+// 1024 / 4 38.7 us: the selection is bound by its chain of barriers and
+// memory round trips, and shorter slices shorten the first phase until the
+// last workgroup's candidate list grows too long.
 constexpr int kTkThreads = 1024;
-constexpr int kTkPer = 8;  // keys per thread in the slice phase
+constexpr int kTkPer = 4;  // keys per thread in the slice phase
 constexpr int kTkSlice = kTkThreads * kTkPer;
+constexpr int kFinPer = 2;  // candidate keys per thread held in registers by the last workgroup
+constexpr int kFinKeys = kTkThreads * kFinPer;
 constexpr int kTkMaxK = 1024;
 
 constexpr int kTkWaves = kTkThreads / 64;
@@ -332,14 +340,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
   // when they fit), sorted
   const int total = gridDim.x * k;
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(cand, (uint32_t)total * 8u);
-  if (total <= kTkSlice) {
+  if (total <= kFinKeys) {
+    uint64_t ck[kFinPer];
 #pragma unroll
-    for (int j = 0; j < kTkPer; ++j) {
+    for (int j = 0; j < kFinPer; ++j) {
       const int i = threadIdx.x + j * kTkThreads;
-      keys[j] = coherent_u64(rc, i < total ? (uint32_t)i * 8u : kOOB);
+      ck[j] = coherent_u64(rc, i < total ? (uint32_t)i * 8u : kOOB);
     }
-    const uint64_t thr2 = kth_largest(regs, (uint32_t)k, sh);
-    gather(regs, thr2, sh);
+    auto cregs = [&](auto&& f) {
+#pragma unroll
+      for (int j = 0; j < kFinPer; ++j) f(ck[j]);
+    };
+    const uint64_t thr2 = kth_largest(cregs, (uint32_t)k, sh);
+    gather(cregs, thr2, sh);
   } else {
     auto all = [&](auto&& f) {
       for (int i = threadIdx.x; i < total; i += kTkThreads) f(coherent_u64(rc, (uint32_t)i * 8u));
