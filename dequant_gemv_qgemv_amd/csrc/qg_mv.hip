@@ -299,6 +299,18 @@ __device__ __forceinline__ void quarter_load(const MvParams& p, const XRsrc& r, 
     g[i] = __builtin_amdgcn_raw_buffer_load_b128(r.g, ok && p.norm_w ? (k0 + 8 * i) * 2u : kOOB, 0, 0);
 }
 
+// Routing weight that scales quarter unit u's K segment (1 outside the routed
+// segments or without K segments), requested together with x so that staging
+// does not wait for a second round trip.
+__device__ __forceinline__ float quarter_seg_weight(const MvParams& p, int c0, int u, int nunits) {
+  float w = 1.0f;
+  if (p.seg_mode == kSegCols && p.route.weights && u < nunits) {
+    const int seg = (c0 + (u >> 2)) / p.seg_len;
+    if (seg < p.route.n_routed) w = p.route.weights[seg];
+  }
+  return w;
+}
+
 // Writes quarter q of a chunk's staged x (w already range scaled for the
 // affine formats): the same pieces write_pieces produces for those values.
 template <int BITS, int FMT>
@@ -336,8 +348,9 @@ __device__ __forceinline__ float quad_max(float v) {
 // this lane's sum of squares of its raw x (0 without a norm or outside the
 // slice).
 template <int BITS, int FMT, int LPR>
-__device__ __forceinline__ float stage_quarter(const MvParams& p, const u32x4* x, const u32x4* g, int u,
-                                               int nunits, int c0, int nch, u32x4* xl, ChunkInfo* info) {
+__device__ __forceinline__ float stage_quarter(const MvParams& p, const u32x4* x, const u32x4* g, float wseg,
+                                               int u, int nunits, int c0, int nch, u32x4* xl,
+                                               ChunkInfo* info) {
   constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
   constexpr int QV = CPC / 4;
   constexpr int PIECES = Geo<BITS, FMT>::kPieces;
@@ -378,11 +391,6 @@ __device__ __forceinline__ float stage_quarter(const MvParams& p, const u32x4* x
         v[8 * i + 2 * t + 1] = b * (float)h.y;
       }
     }
-  }
-  float wseg = 1.0f;
-  if (valid && p.seg_mode == kSegCols && p.route.weights) {
-    const int seg = (c0 + c) / p.seg_len;
-    wseg = seg < p.route.n_routed ? p.route.weights[seg] : 1.0f;
   }
   float s = 0.f, m = 0.f;
 #pragma unroll
@@ -587,6 +595,32 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   if (tile * kWaves >= nbands) return;  // same for every slice of this tile: no ticket needed
   const int band_stride = p.grid_x * kWaves;
 
+  // Quarter staging (one quarter unit of x per thread): x and the segment
+  // routing weight are requested before the weight prefetch (loads return in
+  // order, so they arrive first); in a launch that routes its experts itself,
+  // already before the routing, which then overlaps their round trip.
+  const bool quarter = CPC >= 32 && 4 * npass * LPR <= kThreads;
+  const int nunits = 4 * npass * LPR;
+  u32x4 qx[CPC >= 32 ? CPC / 16 : 1], qg[CPC >= 32 ? (CPC / 4 + 7) / 8 : 1];
+  float qw = 1.0f;
+  auto load_quarters = [&]() {
+    if constexpr (CPC >= 32) {
+      if (quarter) {
+        const XRsrc xr = x_rsrc(p);
+#pragma unroll
+        for (int i = 0; i < CPC / 16; ++i) qx[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) qg[i] = u32x4{0u, 0u, 0u, 0u};
+        quarter_load<CPC>(p, xr, c0, nch, threadIdx.x, nunits, qx, qg);
+        qw = quarter_seg_weight(p, c0, threadIdx.x, nunits);
+        asm volatile("" ::: "memory");
+      }
+    }
+  };
+  // (measured: loading x this early in the launches that do not route costs
+  // the 4096 x 14336 gate.up 3 %)
+  if constexpr (SEG == kSegRows) load_quarters();
+
   // Expert ids of a gathered launch: from device memory, or chosen here
   // (workgroup 0 stores them for the launches that follow).
   const int32_t* rids = p.route.ids;
@@ -724,27 +758,20 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   const bool whole_k = (c0 == 0 && nch == C);
   float ss = 0.f;
   // Quarter staging needs quarters of at least 8 values (one 16-byte fp16
-  // load): chunks of 32 codes or more.
-  if (CPC >= 32 && 4 * npass * LPR <= kThreads) {
-   if constexpr (CPC >= 32) {
-    // One quarter unit per thread, x requested first; x is waited for only
-    // after the weight requests are out.
-    const int nunits = 4 * npass * LPR;
-    const XRsrc xr = x_rsrc(p);
-    u32x4 qx[CPC / 16], qg[(CPC / 4 + 7) / 8];
+  // load): chunks of 32 codes or more. x is waited for only after the weight
+  // requests are out.
+  if (quarter) {
+    if constexpr (CPC >= 32) {
+      if constexpr (SEG != kSegRows) load_quarters();
 #pragma unroll
-    for (int i = 0; i < CPC / 16; ++i) qx[i] = u32x4{0u, 0u, 0u, 0u};
+      for (int k = 0; k < DEPTH; ++k) issue(d[k]);
 #pragma unroll
-    for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) qg[i] = u32x4{0u, 0u, 0u, 0u};
-    quarter_load<CPC>(p, xr, c0, nch, threadIdx.x, nunits, qx, qg);
+      for (int i = 0; i < CPC / 16; ++i) hold(qx[i]);
 #pragma unroll
-    for (int k = 0; k < DEPTH; ++k) issue(d[k]);
-#pragma unroll
-    for (int i = 0; i < CPC / 16; ++i) hold(qx[i]);
-#pragma unroll
-    for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) hold(qg[i]);
-    ss = stage_quarter<BITS, FMT, LPR>(p, qx, qg, threadIdx.x, nunits, c0, nch, xl, info);
-   }
+      for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) hold(qg[i]);
+      hold(qw);
+      ss = stage_quarter<BITS, FMT, LPR>(p, qx, qg, qw, threadIdx.x, nunits, c0, nch, xl, info);
+    }
   } else if (npass * LPR <= kThreads) {
     XChunk<CPC> xc;
     const int c = threadIdx.x;
