@@ -114,9 +114,13 @@ int pieces_per_chunk(int bits, int fmt) {
 // items instead of one per item: 151936 x 1024 logits 18.1 us against 20.4,
 // 3072 x 1024 gate.up 4.57 against 4.74). Rows of 96..127 chunks: 64 lanes
 // with a partly empty last pass, which keeps twice the bands of 32 lanes for
-// short matrices (1024 x 3072: 3.64 us against 4.27).
+// short matrices (1024 x 3072: 3.64 us against 4.27). Rows of 33..64 chunks
+// (2-bit codes at K = 4096): two passes of 32 lanes (4096 x 4096 2-bit
+// 4.46 us against 4.52 with one pass of 64, 14336 x 4096 gate.up 11.40
+// against 12.02).
 int pick_lpr(int C) {
   if (C > 16 && C <= 32) return 16;
+  if (C > 32 && C <= 64 && C % 32 == 0) return 32;
   if (C >= 96 && C < 128) return 64;
   const int cands[3] = {64, 32, 16};
   int best = 64;
@@ -161,9 +165,13 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
                 : (s.bits == 4 && s.fmt == QG_AFFINE && s.seg == kSegNone && s.K >= 8192 ? 2 : 1);
   pl.depth = g_knob[4].load() ? g_knob[4].load() : 2;
   // Resident workgroups per CU: two 8-wave groups keep 16 waves in flight
-  // where the kernel's registers allow it (the 2-bit kernels fit one).
+  // where the kernel's registers allow it. 2-bit codes take one: measured on
+  // MI355X, a second group slows them down (4096 x 14336 down 10.22 us
+  // against 8.96 at 64 lanes, 14336 x 4096 gate.up 12.14 against 11.40 at
+  // 32), while the 4-bit kernels gain from it (gate.up 14.22 against 14.88).
   const int resident = mv_resident_per_cu(s.bits, s.fmt, s.epi, s.seg, pl);
-  const int wg_per_cu = g_knob[3].load() ? g_knob[3].load() : (resident < 2 ? resident : 2);
+  const int wg_cap = s.bits == 2 ? 1 : 2;
+  const int wg_per_cu = g_knob[3].load() ? g_knob[3].load() : (resident < wg_cap ? resident : wg_cap);
   const int rpb = (64 / pl.lpr) * pl.rows;
   const int nbands = (s.N + rpb - 1) / rpb;
   const int tiles = (nbands + kWaves - 1) / kWaves;

@@ -603,19 +603,21 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   const int nunits = 4 * npass * LPR;
   u32x4 qx[CPC >= 32 ? CPC / 16 : 1], qg[CPC >= 32 ? (CPC / 4 + 7) / 8 : 1];
   float qw = 1.0f;
-  auto load_quarters = [&]() {
+  // requests quarter unit u (zeros past nunits)
+  auto load_quarters_at = [&](int u) {
     if constexpr (CPC >= 32) {
-      if (quarter) {
-        const XRsrc xr = x_rsrc(p);
+      const XRsrc xr = x_rsrc(p);
 #pragma unroll
-        for (int i = 0; i < CPC / 16; ++i) qx[i] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < CPC / 16; ++i) qx[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) qg[i] = u32x4{0u, 0u, 0u, 0u};
-        quarter_load<CPC>(p, xr, c0, nch, threadIdx.x, nunits, qx, qg);
-        qw = quarter_seg_weight(p, c0, threadIdx.x, nunits);
-        asm volatile("" ::: "memory");
-      }
+      for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) qg[i] = u32x4{0u, 0u, 0u, 0u};
+      quarter_load<CPC>(p, xr, c0, nch, u, nunits, qx, qg);
+      qw = quarter_seg_weight(p, c0, u, nunits);
+      asm volatile("" ::: "memory");
     }
+  };
+  auto load_quarters = [&]() {
+    if (quarter) load_quarters_at(threadIdx.x);
   };
   // (measured: loading x this early in the launches that do not route costs
   // the 4096 x 14336 gate.up 3 %)
@@ -771,6 +773,28 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
       for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) hold(qg[i]);
       hold(qw);
       ss = stage_quarter<BITS, FMT, LPR>(p, qx, qg, qw, threadIdx.x, nunits, c0, nch, xl, info);
+    }
+  } else if constexpr (CPC >= 32) {
+    // More quarter units than threads: the same quarter staging in uniform
+    // rounds (every thread runs every round, so the quads' DPP sums see whole
+    // chunks); the first round's x is requested before the weights. Holding
+    // a whole chunk of x per thread instead (64 values for 2-bit codes) set
+    // the register allocation of every 2-bit kernel to 190-203 VGPRs, one
+    // workgroup per CU.
+    const int rounds = (nunits + kThreads - 1) / kThreads;
+    load_quarters_at(threadIdx.x);
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) issue(d[k]);
+#pragma unroll
+    for (int i = 0; i < CPC / 16; ++i) hold(qx[i]);
+#pragma unroll
+    for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) hold(qg[i]);
+    hold(qw);
+    ss = stage_quarter<BITS, FMT, LPR>(p, qx, qg, qw, threadIdx.x, nunits, c0, nch, xl, info);
+    for (int r = 1; r < rounds; ++r) {
+      const int u = r * kThreads + (int)threadIdx.x;
+      load_quarters_at(u);
+      ss += stage_quarter<BITS, FMT, LPR>(p, qx, qg, qw, u, nunits, c0, nch, xl, info);
     }
   } else if (npass * LPR <= kThreads) {
     XChunk<CPC> xc;
