@@ -387,3 +387,26 @@ def test_graph_replay_matches_eager(qg):
         token()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(x, eager)
+
+
+@pytest.mark.parametrize("bits,fmt", [(4, synth.AFFINE), (2, synth.AFFINE), (4, synth.LUT)])
+@pytest.mark.parametrize("K", [20480, 65536])
+@pytest.mark.parametrize("norm", [False, True])
+def test_long_k_staging_rounds(qg, bits, fmt, K, norm):
+    """K beyond 512 quarter units per slice: x is staged in several uniform
+    rounds, and beyond the LDS slice K is split across workgroups."""
+    N = 300
+    say(f"long K bits={bits} fmt={fmt} K={K} norm={norm}")
+    W = synth.qmat(31, ("longk", bits, fmt, K), N, K, bits, fmt)
+    x = synth.activations(31, ("x", K), K, np.float32)
+    g = synth.norm_weight(31, ("g", K), K) if norm else None
+    ws = qg.workspace(qg.QG_OP_GEMV_RMSNORM, N, K, 1, bits, fmt, 1, DEV)
+    Wd = dev_mat(qg, W)
+    if norm:
+        y = qg.qgemv_rmsnorm(Wd, to_dev(x), to_dev(g), 1e-5, ws=ws)
+        ref = oracle.rmsnorm_gemv(W, x, g, 1e-5, nthreads=8)
+    else:
+        y = qg.qgemv(Wd, to_dev(x), ws=ws)
+        ref = oracle.gemv(W, x, nthreads=8)
+    torch.cuda.synchronize()
+    close(y.cpu().numpy(), ref, what="long K")
