@@ -619,13 +619,27 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   auto load_quarters = [&]() {
     if (quarter) load_quarters_at(threadIdx.x);
   };
-  // (measured: loading x this early in the launches that do not route costs
-  // the 4096 x 14336 gate.up 3 %)
-  if constexpr (SEG == kSegRows) load_quarters();
-
   // Expert ids of a gathered launch: from device memory, or chosen here
   // (workgroup 0 stores them for the launches that follow).
   const int32_t* rids = p.route.ids;
+  // A K-segmented launch (the experts' down projections) switches expert at
+  // every pass; its ids come from device memory once per workgroup into LDS,
+  // requested ahead of x, instead of one dependent lookup per pass.
+  int32_t my_id = 0;
+  if constexpr (SEG == kSegCols) {
+    if (p.route.ids && (int)threadIdx.x < p.route.n_routed) my_id = p.route.ids[threadIdx.x];
+    asm volatile("" ::: "memory");
+  }
+  // (measured: loading x this early in the launches that do not route costs
+  // the 4096 x 14336 gate.up 3 %)
+  if constexpr (SEG != kSegNone) load_quarters();
+  if constexpr (SEG == kSegCols) {
+    if (p.route.ids) {
+      if ((int)threadIdx.x < p.route.n_routed) rt_ids[threadIdx.x] = my_id;
+      __syncthreads();
+      rids = rt_ids;
+    }
+  }
   if constexpr (SEG == kSegRows) {
     if (p.route.logits) {
       if (wave == 0) {
@@ -764,7 +778,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   // requests are out.
   if (quarter) {
     if constexpr (CPC >= 32) {
-      if constexpr (SEG != kSegRows) load_quarters();
+      if constexpr (SEG == kSegNone) load_quarters();
 #pragma unroll
       for (int k = 0; k < DEPTH; ++k) issue(d[k]);
 #pragma unroll
