@@ -274,6 +274,13 @@ __device__ __forceinline__ uint64_t order_key(float v, uint32_t i) {
   return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - i);
 }
 
+// The value a key was made from (-0 comes back as +0, NaN as a NaN): the
+// inverse of the sign-dependent bit flip in order_key.
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t hi = (uint32_t)(key >> 32);
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+
 __device__ __forceinline__ uint32_t key_index(uint64_t key) {
   return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull);
 }
@@ -333,7 +340,7 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits, int
   float lmax = -INFINITY;
 #pragma unroll
   for (int r = 0; r < kMaxRoutes; ++r) {
-    lv[r] = r < top_k ? logits[key_index(chosen[r])] : -INFINITY;
+    lv[r] = r < top_k ? key_value(chosen[r]) : -INFINITY;  // no second trip to memory
     lmax = fmaxf(lmax, lv[r]);
   }
   float den = 0.f;

@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
     __syncthreads();  // the histograms are free: they hold the draw's weights
     if (threadIdx.x < 64)
       draw_token(
-          k, [&](int i) { return z[key_index(sh.list[i])]; },
+          k, [&](int i) { return key_value(sh.list[i]); },  // the logit, without a trip to memory
           [&](int i) { return (int32_t)key_index(sh.list[i]); }, dp,
           reinterpret_cast<double*>(&sh.hist[0][0]));
   }
