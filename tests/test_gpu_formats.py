@@ -248,3 +248,26 @@ def test_several_vectors_unsupported(qg, name):
     with pytest.raises(qg.QgError) as e:
         qg.qgemv(qg.QMat.from_host(W, DEV), x)
     assert e.value.status == qg.QG_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["q8", "f16"])
+@pytest.mark.parametrize("K", [20480, 65536])
+@pytest.mark.parametrize("norm", [False, True])
+def test_long_k_formats(qg, name, K, norm):
+    """Long rows: the one-chunk-per-thread staging loops over several chunks
+    per thread, and K beyond one LDS slice is split across workgroups."""
+    N = 200
+    say(f"long K {name} K={K} norm={norm}")
+    W = mat(32, ("longk", K), N, K, name)
+    x = synth.activations(32, ("x", K), K, np.float32)
+    g = synth.norm_weight(32, ("g", K), K) if norm else None
+    w = ws(qg, qg.QG_OP_GEMV_RMSNORM, N, K, name)
+    Wd = qg.QMat.from_host(W, DEV)
+    if norm:
+        y = qg.qgemv_rmsnorm(Wd, to_dev(x), to_dev(g), 1e-5, ws=w)
+        ref = oracle.rmsnorm_gemv(W, x, g, 1e-5, nthreads=8)
+    else:
+        y = qg.qgemv(Wd, to_dev(x), ws=w)
+        ref = oracle.gemv(W, x, nthreads=8)
+    torch.cuda.synchronize()
+    close(y.cpu().numpy(), ref, what="long K")
