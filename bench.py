@@ -686,7 +686,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py: this build runs on one GPU only; --gpus above 1 is not supported "
+        print("bench.py: the library runs on one GPU; --gpus above 1 is not supported "
               "(the sharding plan is described in the design notes)", file=sys.stderr)
         sys.exit(2)
     if args.fmt == 1 and args.bits != 4:

@@ -1,0 +1,35 @@
+"""bench.py's argument checks, which run before anything touches a GPU. CPU only."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=120)
+
+
+@pytest.mark.parametrize("args,needle", [
+    (["--gpus", "2"], "one GPU"),
+    (["--bits", "16"], "--bits 16 --fmt 2"),
+    (["--fmt", "2"], "--bits 16 --fmt 2"),
+    (["--fmt", "1", "--bits", "2"], "4-bit codes"),
+    (["--m", "2", "--bits", "8"], "2- and 4-bit"),
+    (["--m", "9"], "--m must be 1..8"),
+])
+def test_rejected_before_any_gpu_work(args, needle):
+    r = run(*args)
+    assert r.returncode == 2
+    assert needle in r.stderr
+
+
+def test_several_ranks_are_refused(monkeypatch):
+    env = dict(os.environ, WORLD_SIZE="2")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")], capture_output=True,
+                       text=True, timeout=120, env=env)
+    assert r.returncode == 2 and "one GPU" in r.stderr
