@@ -442,8 +442,12 @@ def run_single(args, qg, synth, dev):
 def run_moe(args, qg, synth, dev):
     """One 512-expert layer (gate, up 4096->1024, down 1024->4096, 4-bit),
     top-3 routed + 1 shared expert; a token runs 60 chained layers over the
-    same weights with fresh router logits each."""
+    same weights with fresh router logits each. With --m M, M tokens run
+    through each layer in one batched call; the algorithmic bytes of a layer
+    are then the union of the experts the M tokens chose, plus the shared
+    one, each counted once."""
     import torch
+    M = args.m
     mdl = synth.MOE_397B
     E, F, H, K, L = mdl["experts"], mdl["ffn"], mdl["hidden"], mdl["top_k"], mdl["draws"]
     t0 = time.time()
@@ -458,48 +462,67 @@ def run_moe(args, qg, synth, dev):
     Gd, Ud, Dd = (qg.QMat.from_host(W, dev) for W in (gate, up, down))
     Sd = tuple(qg.QMat.from_host(W, dev) for W in shared)
     gd = torch.from_numpy(g.view(np.int16)).to(dev)
-    logits = [synth.router_logits(args.seed, ("moe_route", l), E) for l in range(L)]
+    if M == 1:
+        logits = [synth.router_logits(args.seed, ("moe_route", l), E) for l in range(L)]
+        x0h = synth.activations(args.seed, "moe_x0", H, np.float32)
+    else:
+        logits = [synth.router_logits(args.seed, ("moe_route_batch", l), (M, E)) for l in range(L)]
+        x0h = synth.activations(args.seed, "moe_x0_batch", (M, H), np.float32)
     lgd = torch.from_numpy(np.stack(logits)).to(dev)
-    x0 = torch.from_numpy(synth.activations(args.seed, "moe_x0", H, np.float32)).to(dev)
-    x = torch.empty(H, dtype=torch.float32, device=dev)
-    ws = qg.workspace(qg.QG_OP_MOE, H, F, 1, 4, 0, K, dev)
+    x0 = torch.from_numpy(x0h).to(dev)
+    x = torch.empty_like(x0)
+    ws = qg.workspace(qg.QG_OP_MOE, H, F, M, 4, 0, K, dev)
     torch.cuda.synchronize()
     log(f"moe weights {(Gd.nbytes() + Ud.nbytes() + Dd.nbytes()) / 1e9:.2f} GB ({time.time() - t0:.1f} s)")
     expert_bytes = synth.qmat_bytes(F, H) * 2 + synth.qmat_bytes(H, F)
-    layer_bytes = (K + 1) * expert_bytes + E * 4 + H * 4 * 2 + H * 2
+    vec_bytes = M * (E * 4 + H * 4 * 2) + H * 2
+    if M == 1:
+        layer_bytes = [(K + 1) * expert_bytes + vec_bytes] * L
+    else:
+        # the experts each layer's tokens choose (largest logits; exact ties do not occur)
+        layer_bytes = [(len(set(np.argsort(-lg, axis=1, kind="stable")[:, :K].ravel().tolist())) + 1)
+                       * expert_bytes + vec_bytes for lg in logits]
 
     def token():
         x.copy_(x0)
         for l in range(L):
-            qg.qmoe_experts(Gd, Ud, Dd, E, Sd, lgd[l], K, x, gd, EPS, y=x, ws=ws)
+            if M == 1:
+                qg.qmoe_experts(Gd, Ud, Dd, E, Sd, lgd[l], K, x, gd, EPS, y=x, ws=ws)
+            else:
+                qg.qmoe_experts_batch(Gd, Ud, Dd, E, Sd, lgd[l], K, x, gd, EPS, y=x, ws=ws)
 
     step, graph = graph_step(token, not args.no_graph, x)
     ms = time_steps(step, args.steps, args.warmup)
     us_layer = ms * 1e3 / L
-    dom = roofline("qmoe_experts (route, gate.up of 4 experts, down + combine)", layer_bytes, us_layer)
+    kname = ("qmoe_experts (route, gate.up of 4 experts, down + combine)" if M == 1 else
+             f"qmoe_experts_batch M={M} (route, gate.up of 4 experts per token, down + combine)")
+    dom = roofline(kname, sum(layer_bytes) / L, us_layer)
     copy_gbs = copy_peak(dev)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         th = oracle_threads()
-        xh = synth.activations(args.seed, "moe_x0", H, np.float32).astype(np.float64)
+        xh = np.atleast_2d(x0h.astype(np.float64))
 
         def work(i):
             nonlocal xh
             if i >= L:
                 return None
-            xh, _, _ = oracle.moe_layer(gate, up, down, shared, logits[i], K, xh, g, EPS,
-                                        nthreads=th)
-            return layer_bytes
+            lg = np.atleast_2d(logits[i])
+            xh = np.stack([oracle.moe_layer(gate, up, down, shared, lg[m], K, xh[m], g, EPS,
+                                            nthreads=th)[0] for m in range(M)])
+            return layer_bytes[i]
 
         done, n, dt = cpu_sample(work, args.cpu_seconds)
         cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
-               "sample": f"{n} of {L} chained expert layers of one token in {dt:.1f} s, "
-                         f"fp64 scalar C", "tok_per_s": round(n / L / dt, 6)}
+               "sample": f"{n} of {L} chained expert layers of {M} token(s) in {dt:.1f} s, "
+                         f"fp64 scalar C", "tok_per_s": round(M * n / L / dt, 6)}
     cfg = {"experts": E, "hidden": H, "ffn": F, "top_k": K, "shared": 1, "layers_per_token": L,
-           "us_per_layer": round(us_layer, 3), "graph": graph is not None}
-    emit(args, "moe expert layer, 512 experts 4-bit g64, top-3 + shared, 60 chained draws per token",
-         cfg, layer_bytes * L, ms, dom, copy_gbs, cpu)
+           "tokens": M, "us_per_layer": round(us_layer, 3), "graph": graph is not None}
+    name = "moe expert layer, 512 experts 4-bit g64, top-3 + shared, 60 chained draws per token"
+    if M > 1:
+        name += f", {M} tokens per batched call"
+    emit(args, name, cfg, sum(layer_bytes), ms, dom, copy_gbs, cpu)
 
 
 def run_qwen(args, qg, synth, dev):
@@ -663,7 +686,8 @@ def main():
     ap.add_argument("--fmt", type=int, default=0, choices=[0, 1, 2],
                     help="stack: 0 = scale + bias per group, 1 = 16-entry table per row (4-bit), "
                          "2 = dense fp16 weights (--bits 16)")
-    ap.add_argument("--m", type=int, default=1, help="stack: activation vectors per step (1..8)")
+    ap.add_argument("--m", type=int, default=1,
+                    help="stack: activation vectors per step; moe: tokens per batched call (1..8)")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
@@ -695,7 +719,7 @@ def main():
     if (args.fmt == 2) != (args.bits == 16):
         print("bench.py: dense fp16 weights are --bits 16 --fmt 2", file=sys.stderr)
         sys.exit(2)
-    if args.m > 1 and args.bits not in (2, 4):
+    if args.m > 1 and args.config == "stack" and args.bits not in (2, 4):
         print("bench.py: several vectors per step run for 2- and 4-bit codes only", file=sys.stderr)
         sys.exit(2)
     if not 1 <= args.m <= 8:

@@ -4,7 +4,8 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/qgemv.h. PyTorch provides device
 memory and the current stream. The functions carry the C names:
 
-  qgemv, qgemv_rmsnorm, qswiglu, qmoe_experts, qlogits_topk, qlogits_sample, qg_sample_topk,
+  qgemv, qgemv_rmsnorm, qswiglu, qmoe_experts, qmoe_experts_batch, qlogits_topk, qlogits_sample,
+  qg_sample_topk,
   qattn_decode,
   qg_workspace_bytes, qg_workspace_init, qg_status_str, qg_tune
 
@@ -30,7 +31,8 @@ QG_OP_GEMV, QG_OP_GEMV_RMSNORM, QG_OP_SWIGLU, QG_OP_MOE, QG_OP_LOGITS_TOPK, QG_O
 QG_MAX_TOPK = 1024
 
 EXPORTED = ("qg_status_str", "qg_workspace_bytes", "qg_workspace_init", "qg_tune", "qgemv",
-            "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk", "qlogits_sample",
+            "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qmoe_experts_batch", "qlogits_topk",
+            "qlogits_sample",
             "qg_sample_topk", "qattn_decode", "qg_probe_read",
             "qg_probe_copy")
 
@@ -67,6 +69,8 @@ def lib():
         L.qgemv_rmsnorm.argtypes = [Q, I, I, I, I, I, I, P, I, P, F, P, P, P, S, P]
         L.qswiglu.argtypes = [Q, Q, I, I, I, I, I, I, P, I, P, F, P, P, S, P]
         L.qmoe_experts.argtypes = [Q, Q, Q, I, I, I, I, I, I, Q, P, I, P, F, P, P, P, P, P, S, P]
+        L.qmoe_experts_batch.argtypes = [Q, Q, Q, I, I, I, I, I, I, I, Q, P, I, P, F, P, P, P, P, P,
+                                         S, P]
         L.qlogits_topk.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P, S, P]
         U64 = ctypes.c_uint64
         L.qlogits_sample.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, F, F, U64, P, P,
@@ -255,6 +259,30 @@ def qmoe_experts(gate_all: QMat, up_all: QMat, down_all: QMat, n_experts: int, s
                               gate_all.bits, gate_all.fmt, sh, _ptr(router_logits), top_k,
                               _ptr(norm_w), float(eps), _ptr(x), _ptr(y), _ptr(sel_ids),
                               _ptr(sel_w), wp, wn, _stream(stream)), "qmoe_experts")
+    return y
+
+
+def qmoe_experts_batch(gate_all: QMat, up_all: QMat, down_all: QMat, n_experts: int, shared3,
+                       router_logits, top_k: int, x, norm_w=None, eps: float = 1e-5, y=None,
+                       sel_ids=None, sel_w=None, ws=None, stream=None):
+    """qmoe_experts for M tokens: x [M, H], router_logits [M, n_experts], y [M, H],
+    sel_ids / sel_w [M, top_k] or None."""
+    import torch
+    F = gate_all.N // n_experts
+    H = gate_all.K
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    sh = None
+    if shared3 is not None:
+        arr = (qg_qmat * 3)(shared3[0].c, shared3[1].c, shared3[2].c)
+        sh = ctypes.cast(arr, ctypes.POINTER(qg_qmat))
+    wp, wn = _ws_args(ws)
+    _check(lib().qmoe_experts_batch(ctypes.byref(gate_all.c), ctypes.byref(up_all.c),
+                                    ctypes.byref(down_all.c), n_experts, F, H, M, gate_all.group,
+                                    gate_all.bits, gate_all.fmt, sh, _ptr(router_logits), top_k,
+                                    _ptr(norm_w), float(eps), _ptr(x), _ptr(y), _ptr(sel_ids),
+                                    _ptr(sel_w), wp, wn, _stream(stream)), "qmoe_experts_batch")
     return y
 
 

@@ -15,8 +15,8 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
                         int n_experts, int F, int H, int bits, int fmt, const qg_qmat* shared3,
                         const float* router_logits, int top_k, const uint16_t* norm_w, float eps,
                         const float* x, float* y, int32_t* sel_ids, float* sel_w, void* ws,
-                        size_t ws_bytes, hipStream_t stream);
-size_t moe_workspace_bytes(int F, int H, int top_k);
+                        size_t ws_bytes, hipStream_t stream, int M);
+size_t moe_workspace_bytes(int F, int H, int top_k, int M);
 }  // namespace qg
 
 using namespace qg;
@@ -334,16 +334,21 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
 namespace qg {
 // Shared with the MoE launcher.
 int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have_ws, void* ws,
-                       size_t ws_bytes, size_t ws_offset, hipStream_t stream) {
+                       size_t ws_bytes, size_t ws_offset, hipStream_t stream, int tokens) {
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;
   MvParams p = p0;
   const MvPlan pl = plan_mv({p.N, p.K, bits, fmt, epi, p.seg_mode == kSegCols ? p.seg_len : 0,
                              p.seg_mode}, dev.cus, have_ws);
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;
+  // a batched launch keeps each token's K in one slice (its split-K partials
+  // and tickets would need one workspace region per token)
+  if (tokens > 1 && pl.splits > 1) return QG_EUNSUPPORTED;
   p.splits = pl.splits;
   p.slice_chunks = pl.slice_chunks;
   p.grid_x = pl.grid_x;
+  MvPlan lp = pl;
+  lp.tokens = tokens;
   if (pl.splits > 1) {
     const size_t tickets = ((size_t)(p.N + 7) / 8 + 64) * 4;
     const size_t tickets_al = (tickets + 255) / 256 * 256;
@@ -352,7 +357,7 @@ int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have
     p.tickets = reinterpret_cast<uint32_t*>(base);
     p.partials = reinterpret_cast<float*>(base + tickets_al);
   }
-  const hipError_t e = launch_mv(bits, fmt, epi, pl, p, stream);
+  const hipError_t e = launch_mv(bits, fmt, epi, lp, p, stream);
   return e == hipSuccess ? QG_OK : QG_ELAUNCH;
 }
 size_t mv_workspace_bytes(int N, int epi) { return mv_ws_bytes(N, 1, epi); }
@@ -400,7 +405,8 @@ int qg_workspace_bytes(int op, int N, int K, int M, int bits, int fmt, int k, si
     case QG_OP_SWIGLU: *bytes = mv_ws_bytes(N, M, kEpiSwiglu); return QG_OK;
     case QG_OP_MOE:
       if (k < 1 || k > kMaxRoutes) return QG_EUNSUPPORTED;
-      *bytes = moe_workspace_bytes(K, N, k);
+      if (M < 1 || M > QG_MAX_M) return QG_EUNSUPPORTED;
+      *bytes = moe_workspace_bytes(K, N, k, M);
       return QG_OK;
     case QG_OP_LOGITS_TOPK:
       if (k < 1 || k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
@@ -464,6 +470,19 @@ int qmoe_experts(const qg_qmat* gate_all, const qg_qmat* up_all, const qg_qmat* 
                  const qg_qmat* shared3, const float* router_logits, int top_k,
                  const uint16_t* norm_w, float eps, const float* x, float* y, int32_t* sel_ids,
                  float* sel_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return qmoe_experts_batch(gate_all, up_all, down_all, n_experts, F, H, 1, group, bits, fmt,
+                            shared3, router_logits, top_k, norm_w, eps, x, y, sel_ids, sel_w, ws,
+                            ws_bytes, stream);
+}
+
+int qmoe_experts_batch(const qg_qmat* gate_all, const qg_qmat* up_all, const qg_qmat* down_all,
+                       int n_experts, int F, int H, int M, int group, int bits, int fmt,
+                       const qg_qmat* shared3, const float* router_logits, int top_k,
+                       const uint16_t* norm_w, float eps, const float* x, float* y,
+                       int32_t* sel_ids, float* sel_w, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  if (M < 1) return QG_EINVAL;
+  if (M > QG_MAX_M) return QG_EUNSUPPORTED;
   int rc = check_common(F, H, 1, group, bits, fmt, QG_F32);
   if (rc) return rc;
   if ((rc = check_common(H, F, 1, group, bits, fmt, QG_F32))) return rc;
@@ -472,7 +491,7 @@ int qmoe_experts(const qg_qmat* gate_all, const qg_qmat* up_all, const qg_qmat* 
   if (fmt != QG_AFFINE) return QG_EUNSUPPORTED;  // expert layers take the affine format
   return plan_and_launch_moe(gate_all, up_all, down_all, n_experts, F, H, bits, fmt, shared3,
                              router_logits, top_k, norm_w, eps, x, y, sel_ids, sel_w, ws,
-                             ws_bytes, stream);
+                             ws_bytes, stream, M);
 }
 
 int qlogits_topk(const qg_qmat* W, int V, int K, int group, int bits, int fmt, const void* x,

@@ -89,6 +89,7 @@ struct MvPlan {
   int grid_x;
   int depth;          // (band, pass) items in flight per wave: 2 or 4
   size_t lds_bytes;
+  int tokens;         // expert launches: tokens in the batch (grid y; 0 or 1 = one)
 };
 
 hipError_t launch_mv(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,

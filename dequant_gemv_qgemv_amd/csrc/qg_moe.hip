@@ -4,6 +4,10 @@
 // Compute" -- the combine, norm and residual run on the GPU and go straight to
 // the next layer, with no host round trip).
 //
+// A batch of M tokens (1..8) runs in the same two launches: workgroup row
+// blockIdx.y serves token blockIdx.y, with its own routing, expert rows and
+// vectors (tokens do not interact).
+//
 // Two launches on one stream:
 //  1. gate.up SwiGLU over the chosen experts plus the shared one, as one
 //     matvec over (top_k+1)*F gathered rows: every workgroup first picks the
@@ -23,13 +27,15 @@
 namespace qg {
 
 int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have_ws, void* ws,
-                       size_t ws_bytes, size_t ws_offset, hipStream_t stream);
+                       size_t ws_bytes, size_t ws_offset, hipStream_t stream, int tokens);
 size_t mv_workspace_bytes(int N, int epi);
 int device_ok();
 
 namespace {
-constexpr size_t kRouteBytes = 256;
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+// Stored routes of M tokens: ids [M][kMaxRoutes] int32, then weights
+// [M][kMaxRoutes] fp32.
+size_t route_bytes(int M) { return align256((size_t)M * kMaxRoutes * 8); }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -47,19 +53,19 @@ int check_mat(const qg_qmat* W, int fmt) {
 QMat dev(const qg_qmat* W) { return QMat{W->q, W->scales, W->biases, W->lut}; }
 }  // namespace
 
-size_t moe_workspace_bytes(int F, int H, int top_k) {
+size_t moe_workspace_bytes(int F, int H, int top_k, int M) {
   const int nseg = top_k + 1;
-  const size_t u = align256((size_t)nseg * F * 4);
+  const size_t u = align256((size_t)M * nseg * F * 4);
   const size_t gu = mv_workspace_bytes(nseg * F, kEpiSwiglu);
   const size_t dn = mv_workspace_bytes(H, kEpiStore);
-  return kRouteBytes + u + (gu > dn ? gu : dn);
+  return route_bytes(M) + u + (gu > dn ? gu : dn);
 }
 
 int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg_qmat* down_all,
                         int n_experts, int F, int H, int bits, int fmt, const qg_qmat* shared3,
                         const float* router_logits, int top_k, const uint16_t* norm_w, float eps,
                         const float* x, float* y, int32_t* sel_ids, float* sel_w, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+                        size_t ws_bytes, hipStream_t stream, int M) {
   int rc;
   if ((rc = check_mat(gate_all, fmt)) || (rc = check_mat(up_all, fmt)) ||
       (rc = check_mat(down_all, fmt)))
@@ -74,19 +80,19 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
   if (norm_w && (!aligned(norm_w, 16) || !(eps >= 0.f))) return QG_EINVAL;
   if ((sel_ids && !aligned(sel_ids, 4)) || (sel_w && !aligned(sel_w, 4))) return QG_EINVAL;
   if (x != y) {
-    const uintptr_t a = (uintptr_t)x, b = (uintptr_t)y, n = (uintptr_t)H * 4;
+    const uintptr_t a = (uintptr_t)x, b = (uintptr_t)y, n = (uintptr_t)M * H * 4;
     if (a < b + n && b < a + n) return QG_EINVAL;
   }
-  if (!ws || !aligned(ws, 256) || ws_bytes < moe_workspace_bytes(F, H, top_k))
+  if (!ws || !aligned(ws, 256) || ws_bytes < moe_workspace_bytes(F, H, top_k, M))
     return QG_EWORKSPACE;
   if (!device_ok()) return QG_EDEVICE;
 
   const int nseg = top_k + (shared3 ? 1 : 0);
   char* base = static_cast<char*>(ws);
   int32_t* ids_ws = reinterpret_cast<int32_t*>(base);
-  float* w_ws = reinterpret_cast<float*>(base + 64);
-  float* u = reinterpret_cast<float*>(base + kRouteBytes);
-  const size_t mv_off = kRouteBytes + align256((size_t)(top_k + 1) * F * 4);
+  float* w_ws = reinterpret_cast<float*>(base + (size_t)M * kMaxRoutes * 4);
+  float* u = reinterpret_cast<float*>(base + route_bytes(M));
+  const size_t mv_off = route_bytes(M) + align256((size_t)M * (top_k + 1) * F * 4);
 
   // 1. routing + gate.up SwiGLU over the chosen experts' rows (+ shared)
   MvParams p;
@@ -121,7 +127,7 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
   p.eps = eps;
   p.residual = nullptr;
   p.y = u;
-  rc = mv_launch_internal(bits, fmt, kEpiSwiglu, p, true, ws, ws_bytes, mv_off, stream);
+  rc = mv_launch_internal(bits, fmt, kEpiSwiglu, p, true, ws, ws_bytes, mv_off, stream, M);
   if (rc) return rc;
 
   // 2. down over the K-concatenated experts, weighted, + residual
@@ -147,7 +153,7 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
   d.norm_w = nullptr;
   d.residual = x;
   d.y = y;
-  return mv_launch_internal(bits, fmt, kEpiStore, d, true, ws, ws_bytes, mv_off, stream);
+  return mv_launch_internal(bits, fmt, kEpiStore, d, true, ws, ws_bytes, mv_off, stream, M);
 }
 
 }  // namespace qg

@@ -157,12 +157,12 @@ __device__ __forceinline__ float block_reduce(float v, float* red) {
 }
 
 // This thread's share of sum(x^2) over all K (strided groups of 8).
-__device__ float sumsq_all(const MvParams& p) {
+__device__ float sumsq_all(const MvParams& p, const void* xp) {
   float ss = 0.f;
   const int K8 = p.K / 8;
   for (int i = threadIdx.x; i < K8; i += kThreads) {
     float v[8];
-    load_x<8>(p.x, p.x_f32, 8 * i, v);
+    load_x<8>(xp, p.x_f32, 8 * i, v);
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
   }
@@ -179,9 +179,10 @@ struct XChunk {
 };
 
 template <int CPC>
-__device__ __forceinline__ void stage_load(const MvParams& p, int cg, bool have, XChunk<CPC>& xc) {
+__device__ __forceinline__ void stage_load(const MvParams& p, const void* xp, int cg, bool have,
+                                           XChunk<CPC>& xc) {
   if (have) {
-    load_x<CPC>(p.x, p.x_f32, cg * CPC, xc.v);
+    load_x<CPC>(xp, p.x_f32, cg * CPC, xc.v);
     if (p.norm_w) {
       const u32x4* src = reinterpret_cast<const u32x4*>(p.norm_w + cg * CPC);
 #pragma unroll
@@ -202,7 +203,7 @@ __device__ __forceinline__ void stage_load(const MvParams& p, int cg, bool have,
 // No block-wide reduction is involved. Returns the chunk's sum of squares of
 // x (0 without a norm or outside the slice).
 template <int BITS, int FMT, int LPR>
-__device__ __forceinline__ float stage_chunk(const MvParams& p, float* v, const u32x4* g, int c,
+__device__ __forceinline__ float stage_chunk(const MvParams& p, const float* rw, float* v, const u32x4* g, int c,
                                             int cg, bool valid, u32x4* xl, ChunkInfo* info) {
   constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
   constexpr int PIECES = Geo<BITS, FMT>::kPieces;
@@ -222,9 +223,9 @@ __device__ __forceinline__ float stage_chunk(const MvParams& p, float* v, const 
     }
   }
   float wseg = 1.0f;
-  if (valid && p.seg_mode == kSegCols && p.route.weights) {
+  if (valid && p.seg_mode == kSegCols && rw) {
     const int seg = cg / p.seg_len;
-    wseg = seg < p.route.n_routed ? p.route.weights[seg] : 1.0f;
+    wseg = seg < p.route.n_routed ? rw[seg] : 1.0f;
   }
   float s = 0.f, m = 0.f;
 #pragma unroll
@@ -268,10 +269,10 @@ struct XRsrc {
   __amdgpu_buffer_rsrc_t x, g;
 };
 
-__device__ __forceinline__ XRsrc x_rsrc(const MvParams& p) {
+__device__ __forceinline__ XRsrc x_rsrc(const MvParams& p, const void* xp) {
   XRsrc r;
-  r.x = make_rsrc(p.x, (uint32_t)p.K * (p.x_f32 ? 4u : 2u));
-  r.g = make_rsrc(p.norm_w ? (const void*)p.norm_w : p.x, p.norm_w ? (uint32_t)p.K * 2u : 0u);
+  r.x = make_rsrc(xp, (uint32_t)p.K * (p.x_f32 ? 4u : 2u));
+  r.g = make_rsrc(p.norm_w ? (const void*)p.norm_w : xp, p.norm_w ? (uint32_t)p.K * 2u : 0u);
   return r;
 }
 
@@ -302,11 +303,12 @@ __device__ __forceinline__ void quarter_load(const MvParams& p, const XRsrc& r, 
 // Routing weight that scales quarter unit u's K segment (1 outside the routed
 // segments or without K segments), requested together with x so that staging
 // does not wait for a second round trip.
-__device__ __forceinline__ float quarter_seg_weight(const MvParams& p, int c0, int u, int nunits) {
+__device__ __forceinline__ float quarter_seg_weight(const MvParams& p, const float* rw, int c0, int u,
+                                                   int nunits) {
   float w = 1.0f;
-  if (p.seg_mode == kSegCols && p.route.weights && u < nunits) {
+  if (p.seg_mode == kSegCols && rw && u < nunits) {
     const int seg = (c0 + (u >> 2)) / p.seg_len;
-    if (seg < p.route.n_routed) w = p.route.weights[seg];
+    if (seg < p.route.n_routed) w = rw[seg];
   }
   return w;
 }
@@ -425,22 +427,22 @@ __device__ __forceinline__ float stage_quarter(const MvParams& p, const u32x4* x
 // Stages chunks [c0, c0 + nch) (zero padded to npass*LPR) when the chunks
 // outnumber the threads: each thread loops over its chunks, reading x again.
 template <int BITS, int FMT, int LPR>
-__device__ float stage_loop(const MvParams& p, int c0, int nch, int npass, u32x4* xl,
+__device__ float stage_loop(const MvParams& p, const void* xp, const float* rw, int c0, int nch, int npass, u32x4* xl,
                             ChunkInfo* info) {
   constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
   float ss = 0.f;
   for (int c = threadIdx.x; c < npass * LPR; c += kThreads) {
     XChunk<CPC> xc;
-    stage_load<CPC>(p, c0 + c, c < nch, xc);
-    ss += stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
+    stage_load<CPC>(p, xp, c0 + c, c < nch, xc);
+    ss += stage_chunk<BITS, FMT, LPR>(p, rw, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
   }
   return ss;
 }
 
 // 1/sqrt(mean(x^2) + eps) over all of K read from memory (used when this
 // workgroup stages only a slice of K). Every thread of the block calls it.
-__device__ float rms_all(const MvParams& p, float* red) {
-  return 1.0f / sqrtf(block_reduce<false>(sumsq_all(p), red) / (float)p.K + p.eps);
+__device__ float rms_all(const MvParams& p, const void* xp, float* red) {
+  return 1.0f / sqrtf(block_reduce<false>(sumsq_all(p, xp), red) / (float)p.K + p.eps);
 }
 
 // Matrix of segment `seg` (routed experts are looked up from the chosen ids:
@@ -581,6 +583,16 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   __shared__ float rt_w[kMaxRoutes];
 
   params_now(p);
+  // A batched expert launch: workgroup row blockIdx.y serves token blockIdx.y,
+  // whose vectors follow the first token's at fixed strides (x [M][K], y and
+  // residual [M][N], router logits [M][n_experts], stored routes
+  // [M][kMaxRoutes], returned routes [M][n_routed]). Every other launch has
+  // one token, and these are the launch's own pointers.
+  const int tok = (SEG != kSegNone) ? (int)blockIdx.y : 0;
+  const void* const xp = static_cast<const char*>(p.x) + (size_t)tok * p.K * (p.x_f32 ? 4 : 2);
+  float* const yp = p.y + (size_t)tok * p.N;
+  const float* const resp = p.residual ? p.residual + (size_t)tok * p.N : nullptr;
+  const float* const rwp = p.route.weights ? p.route.weights + tok * kMaxRoutes : nullptr;
   const int slice = blockIdx.x / p.grid_x;
   const int tile = blockIdx.x - slice * p.grid_x;
   const int C = p.K / CPC;
@@ -606,13 +618,13 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   // requests quarter unit u (zeros past nunits)
   auto load_quarters_at = [&](int u) {
     if constexpr (CPC >= 32) {
-      const XRsrc xr = x_rsrc(p);
+      const XRsrc xr = x_rsrc(p, xp);
 #pragma unroll
       for (int i = 0; i < CPC / 16; ++i) qx[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) qg[i] = u32x4{0u, 0u, 0u, 0u};
       quarter_load<CPC>(p, xr, c0, nch, u, nunits, qx, qg);
-      qw = quarter_seg_weight(p, c0, u, nunits);
+      qw = quarter_seg_weight(p, rwp, c0, u, nunits);
       asm volatile("" ::: "memory");
     }
   };
@@ -621,20 +633,20 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   };
   // Expert ids of a gathered launch: from device memory, or chosen here
   // (workgroup 0 stores them for the launches that follow).
-  const int32_t* rids = p.route.ids;
+  const int32_t* rids = p.route.ids ? p.route.ids + tok * kMaxRoutes : nullptr;
   // A K-segmented launch (the experts' down projections) switches expert at
   // every pass; its ids come from device memory once per workgroup into LDS,
   // requested ahead of x, instead of one dependent lookup per pass.
   int32_t my_id = 0;
   if constexpr (SEG == kSegCols) {
-    if (p.route.ids && (int)threadIdx.x < p.route.n_routed) my_id = p.route.ids[threadIdx.x];
+    if (rids && (int)threadIdx.x < p.route.n_routed) my_id = rids[threadIdx.x];
     asm volatile("" ::: "memory");
   }
   // (measured: loading x this early in the launches that do not route costs
   // the 4096 x 14336 gate.up 3 %)
   if constexpr (SEG != kSegNone) load_quarters();
   if constexpr (SEG == kSegCols) {
-    if (p.route.ids) {
+    if (rids) {
       if ((int)threadIdx.x < p.route.n_routed) rt_ids[threadIdx.x] = my_id;
       __syncthreads();
       rids = rt_ids;
@@ -645,16 +657,18 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
       if (wave == 0) {
         int32_t ids[kMaxRoutes];
         float w[kMaxRoutes];
-        route_wave(p.route.logits, p.route.n_experts, p.route.n_routed, ids, w);
+        route_wave(p.route.logits + (size_t)tok * p.route.n_experts, p.route.n_experts,
+                   p.route.n_routed, ids, w);
         if (lane == 0) {
+          const int so = tok * kMaxRoutes, sl = tok * p.route.n_routed;
           for (int r = 0; r < p.route.n_routed; ++r) {
             rt_ids[r] = ids[r];
             rt_w[r] = w[r];
             if (blockIdx.x == 0) {
-              p.route.ids_store[r] = ids[r];
-              p.route.w_store[r] = w[r];
-              if (p.route.sel_ids) p.route.sel_ids[r] = ids[r];
-              if (p.route.sel_w) p.route.sel_w[r] = w[r];
+              p.route.ids_store[so + r] = ids[r];
+              p.route.w_store[so + r] = w[r];
+              if (p.route.sel_ids) p.route.sel_ids[sl + r] = ids[r];
+              if (p.route.sel_w) p.route.sel_w[sl + r] = w[r];
             }
           }
         }
@@ -813,24 +827,24 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   } else if (npass * LPR <= kThreads) {
     XChunk<CPC> xc;
     const int c = threadIdx.x;
-    stage_load<CPC>(p, c0 + c, c < nch, xc);
+    stage_load<CPC>(p, xp, c0 + c, c < nch, xc);
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) issue(d[k]);
 #pragma unroll
     for (int i = 0; i < CPC; ++i) hold(xc.v[i]);
 #pragma unroll
     for (int i = 0; i < CPC / 8; ++i) hold(xc.g[i]);
-    if (c < npass * LPR) ss = stage_chunk<BITS, FMT, LPR>(p, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
+    if (c < npass * LPR) ss = stage_chunk<BITS, FMT, LPR>(p, rwp, xc.v, xc.g, c, c0 + c, c < nch, xl, info);
   } else {
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) issue(d[k]);
-    ss = stage_loop<BITS, FMT, LPR>(p, c0, nch, npass, xl, info);
+    ss = stage_loop<BITS, FMT, LPR>(p, xp, rwp, c0, nch, npass, xl, info);
   }
   // RMSNorm scalar: applied to the row sums (W (g*x) / rms = W (g*x/rms)).
   // Whole K staged here: each wave sums its chunks' squares before the
   // barrier, the eight partials are added after it in fixed order.
   float rs = 1.0f;
-  if (p.norm_w && !whole_k) rs = rms_all(p, red);  // contains barriers: every thread
+  if (p.norm_w && !whole_k) rs = rms_all(p, xp, red);  // contains barriers: every thread
   if (p.norm_w && whole_k) {
     const float w_ss = lanes_sum<64>(ss);
     if (lane == 63) red[wave] = w_ss;
@@ -863,9 +877,9 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
             handoff_store(&p.partials[((size_t)slice * NACC) * p.N + n], acc_a[r]);
             if constexpr (TWO) handoff_store(&p.partials[((size_t)slice * NACC + 1) * p.N + n], acc_b[r]);
           } else if constexpr (TWO) {
-            p.y[n] = silu(acc_a[r]) * acc_b[r];
+            yp[n] = silu(acc_a[r]) * acc_b[r];
           } else {
-            p.y[n] = p.residual ? p.residual[n] + acc_a[r] : acc_a[r];
+            yp[n] = resp ? resp[n] + acc_a[r] : acc_a[r];
           }
         }
       }
@@ -920,9 +934,9 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
           const float a = coherent_sum(rp, (uint32_t)n * 4u, sstride, p.splits);
           const float b = TWO ? coherent_sum(rp, (uint32_t)(p.N + n) * 4u, sstride, p.splits) : 0.f;
           if constexpr (TWO) {
-            p.y[n] = silu(a) * b;
+            yp[n] = silu(a) * b;
           } else {
-            p.y[n] = p.residual ? p.residual[n] + a : a;
+            yp[n] = resp ? resp[n] + a : a;
           }
         }
       }
@@ -1009,7 +1023,7 @@ hipError_t launch_mv(int bits, int fmt, int epi, const MvPlan& plan, const MvPar
   const KernelFn fn = select_mv(bits, fmt, epi, p.seg_mode, plan);
   if (!fn) return hipErrorInvalidValue;
   if (plan.lds_bytes > (size_t)kMaxLdsBytes) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(plan.grid_x * plan.splits));
+  const dim3 grid((unsigned)(plan.grid_x * plan.splits), (unsigned)(plan.tokens > 1 ? plan.tokens : 1));
   hipLaunchKernelGGL(fn, grid, dim3(kThreads), plan.lds_bytes, stream, p);
   return hipGetLastError();
 }

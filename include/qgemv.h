@@ -134,7 +134,8 @@ typedef struct qg_qmat {
 const char *qg_status_str(int status);
 
 /* Bytes of workspace that `op` needs for these sizes (0 if none). For
- * QG_OP_MOE, N is the hidden size, K the expert FFN size and k the number of
+ * QG_OP_MOE, N is the hidden size, K the expert FFN size, M the tokens of a
+ * batch (1 for qmoe_experts) and k the number of
  * routed experts; for QG_OP_LOGITS_TOPK, N is the vocabulary size and k the
  * number of entries returned; for QG_OP_ATTN, N is the number of query heads
  * H, M the number of kv heads Hkv and k the head dimension d (K, bits and fmt
@@ -204,6 +205,22 @@ int qmoe_experts(const qg_qmat *gate_all, const qg_qmat *up_all, const qg_qmat *
                  const uint16_t *norm_w, float eps, const float *x, float *y,
                  int32_t *sel_ids, float *sel_w, void *ws, size_t ws_bytes,
                  hipStream_t stream);
+
+/* qmoe_experts_batch -- qmoe_experts for M tokens at once (1 <= M <= QG_MAX_M;
+ * [F] section 1: several vectors per step), in the same two launches. Each
+ * token routes, runs its chosen experts and combines on its own; tokens do
+ * not interact. x, y: [M][H] fp32 row-major (y may equal x, otherwise they
+ * must not overlap); router_logits: [M][n_experts] fp32; sel_ids / sel_w:
+ * NULL or [M][top_k]. Workspace: qg_workspace_bytes(QG_OP_MOE, H, F, M, bits,
+ * fmt, top_k, ...). QG_EUNSUPPORTED when a token's hidden size or
+ * concatenated expert width would need split-K (beyond one LDS slice). Other
+ * arguments and conditions as qmoe_experts, which is this call with M = 1. */
+int qmoe_experts_batch(const qg_qmat *gate_all, const qg_qmat *up_all, const qg_qmat *down_all,
+                       int n_experts, int F, int H, int M, int group, int bits, int fmt,
+                       const qg_qmat *shared3, const float *router_logits, int top_k,
+                       const uint16_t *norm_w, float eps, const float *x, float *y,
+                       int32_t *sel_ids, float *sel_w, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* qlogits_topk -- z = W . x' (x' = rmsnorm(x; norm_w), or x when norm_w is
  * NULL), written to logits[V]; then the k largest entries of z, larger first

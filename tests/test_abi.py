@@ -25,13 +25,13 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qg\w+|qgemv\w*|qswiglu|qmoe_experts|qlogits_\w+|qattn_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qg\w+|qgemv\w*|qswiglu|qmoe_experts\w*|qlogits_\w+|qattn_\w+)\s*\(",
                                  text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("qgemv", "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qlogits_topk",
+    for n in ("qgemv", "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qmoe_experts_batch", "qlogits_topk",
               "qlogits_sample", "qg_sample_topk", "qattn_decode",
               "qg_workspace_bytes", "qg_workspace_init", "qg_status_str", "qg_tune"):
         assert n in names
@@ -173,6 +173,22 @@ def test_other_entry_points_reject(L):
     assert L.qmoe_experts(ctypes.byref(W), ctypes.byref(W), ctypes.byref(W), 16, 128, 256, 64, 4,
                           0, None, lg, 3, None, 0.0, X, X, None, None, None, 0,
                           None) == qg.QG_EWORKSPACE
+
+    # batched MoE: no tokens, too many tokens, output overlapping the input,
+    # then a workspace sized for fewer tokens
+    def moe_batch(M, y=X, ws=None, nb=0):
+        return L.qmoe_experts_batch(ctypes.byref(W), ctypes.byref(W), ctypes.byref(W), 16, 128, 256,
+                                    M, 64, 4, 0, None, lg, 3, None, 0.0, X, y, None, None, ws, nb,
+                                    None)
+    assert moe_batch(0) == qg.QG_EINVAL
+    assert moe_batch(9) == qg.QG_EUNSUPPORTED
+    assert moe_batch(4, y=ctypes.c_void_p(0x10000 + 256 * 4)) == qg.QG_EINVAL  # token 1 of x
+    one, four = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.qg_workspace_bytes(3, 256, 128, 1, 4, 0, 3, ctypes.byref(one)) == qg.QG_OK
+    assert L.qg_workspace_bytes(3, 256, 128, 4, 4, 0, 3, ctypes.byref(four)) == qg.QG_OK
+    assert four.value > one.value
+    assert L.qg_workspace_bytes(3, 256, 128, 9, 4, 0, 3, ctypes.byref(four)) == qg.QG_EUNSUPPORTED
+    assert moe_batch(4, ws=ctypes.c_void_p(0x20000000), nb=one.value) == qg.QG_EWORKSPACE
 
 
 def test_workspace_queries(L):

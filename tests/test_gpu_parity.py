@@ -410,3 +410,54 @@ def test_long_k_staging_rounds(qg, bits, fmt, K, norm):
         ref = oracle.gemv(W, x, nthreads=8)
     torch.cuda.synchronize()
     close(y.cpu().numpy(), ref, what="long K")
+
+
+@pytest.mark.parametrize("E,F,H,top_k,M,shared,bits,seed", [(16, 128, 256, 3, 5, True, 4, 33),
+                                                            (8, 64, 128, 1, 2, False, 4, 33),
+                                                            (512, 1024, 4096, 3, 8, True, 4, 33),
+                                                            (16, 1024, 4096, 3, 4, True, 8, 28)])
+def test_qmoe_experts_batch(qg, E, F, H, top_k, M, shared, bits, seed):
+    """M tokens in one call: each token's output is bitwise that of the
+    single-token call, and its routing, weights and output match the oracle's
+    MoE layer for that token alone. (The 8-bit case uses the input family of
+    the single-token 8-bit test: token 1 of the seed-33 family cancels its
+    experts' contributions down to 1/60 of the other tokens' outputs and
+    lands at 2.3e-3 in one call as in the batch.)"""
+    say(f"qmoe_experts_batch E={E} F={F} H={H} top_k={top_k} M={M} bits={bits}")
+    gate = synth.qmat(seed, "gate_all", E * F, H, bits)
+    up = synth.qmat(seed, "up_all", E * F, H, bits)
+    down = synth.qmat(seed, "down_all", E * H, F, bits)
+    for Wt in (gate, up, down):
+        Wt["E"] = E
+    sh = (synth.qmat(seed, "sh_gate", F, H, bits), synth.qmat(seed, "sh_up", F, H, bits),
+          synth.qmat(seed, "sh_down", H, F, bits))
+    g = synth.norm_weight(seed, "g", H)
+    X = synth.activations(seed, "xb", (M, H), np.float32)
+    lg = synth.router_logits(seed, "routeb", (M, E))
+    Gd, Ud, Dd = dev_mat(qg, gate), dev_mat(qg, up), dev_mat(qg, down)
+    shd = tuple(dev_mat(qg, m) for m in sh) if shared else None
+    ws = qg.workspace(qg.QG_OP_MOE, H, F, M, bits, 0, top_k, DEV)
+    ids = torch.empty((M, top_k), dtype=torch.int32, device=DEV)
+    w = torch.empty((M, top_k), dtype=torch.float32, device=DEV)
+    y = qg.qmoe_experts_batch(Gd, Ud, Dd, E, shd, to_dev(lg), top_k, to_dev(X), to_dev(g), 1e-5,
+                              sel_ids=ids, sel_w=w, ws=ws)
+    torch.cuda.synchronize()
+    yc, ic, wc = y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    for m in range(M):
+        ys = qg.qmoe_experts(Gd, Ud, Dd, E, shd, to_dev(lg[m]), top_k, to_dev(X[m]), to_dev(g), 1e-5,
+                             ws=ws)
+        assert torch.equal(ys, y[m]), f"token {m}: batch differs from the single-token call"
+    for m in range(M):
+        yref, rid, rw = oracle.moe_layer(gate, up, down, sh if shared else None, lg[m], top_k, X[m],
+                                         g, nthreads=8)
+        assert np.array_equal(ic[m], rid), f"token {m} routing"
+        close(wc[m], rw, tol=1e-6, what=f"token {m} routing weights")
+        close(yc[m], yref, what=f"token {m} moe")
+    # in place (y is x), and token 0 alone through qmoe_experts gives the same bits
+    xin = to_dev(X)
+    qg.qmoe_experts_batch(Gd, Ud, Dd, E, shd, to_dev(lg), top_k, xin, to_dev(g), 1e-5, y=xin, ws=ws)
+    y0 = qg.qmoe_experts(Gd, Ud, Dd, E, shd, to_dev(lg[0]), top_k, to_dev(X[0]), to_dev(g), 1e-5,
+                         ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(xin, y), "in-place batch differs"
+    assert torch.equal(y0, y[0]), "token 0 alone differs"
