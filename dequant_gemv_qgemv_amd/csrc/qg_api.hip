@@ -288,16 +288,22 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   const size_t ybytes = (size_t)M * N * 4;
   if (overlaps(x, xbytes, y, ybytes)) return QG_EINVAL;
   if (residual && residual != y && overlaps(residual, ybytes, y, ybytes)) return QG_EINVAL;
-  if (M > 1 && (rc = check_mm(A, epi == kEpiSwiglu ? B : nullptr, K, bits, fmt))) return rc;
+  // Several vectors: 2- and 4-bit codes on the matrix cores; 8-bit and dense
+  // weights through the streaming kernel, one workgroup row per vector.
+  const bool on_mfma = M > 1 && bits != 8 && fmt != QG_DENSE;
+  if (on_mfma && (rc = check_mm(A, epi == kEpiSwiglu ? B : nullptr, K, bits, fmt))) return rc;
   if (N == 0) return QG_OK;
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;
   const bool have_ws = ws && ws_bytes >= mv_ws_bytes(N, M, epi) && aligned(ws, 256);
-  if (M > 1)
+  if (on_mfma)
     return run_mm(A, B, N, K, M, bits, fmt, epi, x, x_dtype, norm_w, eps, residual, y, ws,
                   have_ws, dev.cus, stream);
-  const MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0, kSegNone}, dev.cus, have_ws);
+  MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0, kSegNone}, dev.cus, have_ws);
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;  // K too long for one slice: needs ws
+  // per-vector split-K partials are not provided: several vectors keep K in one slice
+  if (M > 1 && pl.splits > 1) return QG_EUNSUPPORTED;
+  pl.tokens = M;
   MvParams p;
   memset(&p, 0, sizeof(p));
   p.A[0] = to_dev(A);
@@ -319,6 +325,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   p.splits = pl.splits;
   p.slice_chunks = pl.slice_chunks;
   p.grid_x = pl.grid_x;
+  p.tokens = M;
   if (pl.splits > 1) {
     const size_t tickets = ((size_t)(N + 7) / 8 + 64) * 4;
     const size_t tickets_al = (tickets + 255) / 256 * 256;
@@ -349,6 +356,7 @@ int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have
   p.grid_x = pl.grid_x;
   MvPlan lp = pl;
   lp.tokens = tokens;
+  p.tokens = tokens;
   if (pl.splits > 1) {
     const size_t tickets = ((size_t)(p.N + 7) / 8 + 64) * 4;
     const size_t tickets_al = (tickets + 255) / 256 * 256;

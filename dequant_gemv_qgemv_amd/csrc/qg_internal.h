@@ -78,6 +78,7 @@ struct MvParams {
   int grid_x;         // workgroups per slice (multiple of 8: slice s of tile t lands on XCD t%8)
   float* partials;    // [splits][n_acc][N] when splits > 1
   uint32_t* tickets;  // [grid_x] zero-initialized when splits > 1
+  int tokens;         // vectors served by one launch (0 or 1: one; more: splits == 1)
 };
 
 // Launch configuration chosen on the host.

@@ -583,18 +583,28 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   __shared__ float rt_w[kMaxRoutes];
 
   params_now(p);
-  // A batched expert launch: workgroup row blockIdx.y serves token blockIdx.y,
-  // whose vectors follow the first token's at fixed strides (x [M][K], y and
-  // residual [M][N], router logits [M][n_experts], stored routes
-  // [M][kMaxRoutes], returned routes [M][n_routed]). Every other launch has
-  // one token, and these are the launch's own pointers.
-  const int tok = (SEG != kSegNone) ? (int)blockIdx.y : 0;
+  // A launch over several vectors (a batched expert launch, or several
+  // activation vectors of 8-bit or dense weights): each workgroup serves one
+  // vector, whose data follow the first one's at fixed strides (x [M][K], y
+  // and residual [M][N], router logits [M][n_experts], stored routes
+  // [M][kMaxRoutes], returned routes [M][n_routed]). A launch with one vector
+  // uses its own pointers.
+  // Workgroup id -> (vector, tile): with several vectors, the workgroups of
+  // one tile for the successive vectors get ids 8 apart, so they land on the
+  // same XCD (workgroups go round-robin over the 8) one after the other and
+  // share its L2 copy of the tile's weights. One vector: the id is the tile.
+  int tok = 0, bid = (int)blockIdx.x;
+  if (p.tokens > 1) {
+    const int lo = bid & 7, rest = bid >> 3;
+    tok = rest % p.tokens;
+    bid = (rest / p.tokens) * 8 + lo;
+  }
   const void* const xp = static_cast<const char*>(p.x) + (size_t)tok * p.K * (p.x_f32 ? 4 : 2);
   float* const yp = p.y + (size_t)tok * p.N;
   const float* const resp = p.residual ? p.residual + (size_t)tok * p.N : nullptr;
   const float* const rwp = p.route.weights ? p.route.weights + tok * kMaxRoutes : nullptr;
-  const int slice = blockIdx.x / p.grid_x;
-  const int tile = blockIdx.x - slice * p.grid_x;
+  const int slice = bid / p.grid_x;
+  const int tile = bid - slice * p.grid_x;
   const int C = p.K / CPC;
   const int c0 = slice * p.slice_chunks;
   const int nch = min(p.slice_chunks, C - c0);
@@ -664,7 +674,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
           for (int r = 0; r < p.route.n_routed; ++r) {
             rt_ids[r] = ids[r];
             rt_w[r] = w[r];
-            if (blockIdx.x == 0) {
+            if (bid == 0) {  // the vector's first workgroup
               p.route.ids_store[so + r] = ids[r];
               p.route.w_store[so + r] = w[r];
               if (p.route.sel_ids) p.route.sel_ids[sl + r] = ids[r];
@@ -1023,7 +1033,7 @@ hipError_t launch_mv(int bits, int fmt, int epi, const MvPlan& plan, const MvPar
   const KernelFn fn = select_mv(bits, fmt, epi, p.seg_mode, plan);
   if (!fn) return hipErrorInvalidValue;
   if (plan.lds_bytes > (size_t)kMaxLdsBytes) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(plan.grid_x * plan.splits), (unsigned)(plan.tokens > 1 ? plan.tokens : 1));
+  const dim3 grid((unsigned)(plan.grid_x * plan.splits * (plan.tokens > 1 ? plan.tokens : 1)));
   hipLaunchKernelGGL(fn, grid, dim3(kThreads), plan.lds_bytes, stream, p);
   return hipGetLastError();
 }

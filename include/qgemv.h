@@ -63,11 +63,14 @@
  *    same inputs gives bitwise the same outputs (no floating-point atomics).
  *  - Alignment: q and x must be 16-byte aligned; fp16 arrays 2-byte aligned;
  *    fp32 arrays 4-byte aligned. Otherwise QG_EINVAL.
- *  - Several activation vectors (M = 2..8; qgemv, qgemv_rmsnorm, qswiglu)
- *    run on the matrix cores ([F] section 1: the dispatcher's choice by M).
- *    They additionally need 2- or 4-bit codes (affine or LUT), K % 512 == 0
- *    and 16-byte aligned scales/biases (affine) or lut (LUT format);
- *    otherwise QG_EUNSUPPORTED. With
+ *  - Several activation vectors (M = 2..8; qgemv, qgemv_rmsnorm, qswiglu):
+ *    2- and 4-bit codes run on the matrix cores ([F] section 1: the
+ *    dispatcher's choice by M) and additionally need K % 512 == 0 and
+ *    16-byte aligned scales/biases (affine) or lut (LUT format), otherwise
+ *    QG_EUNSUPPORTED. 8-bit and dense weights run the one-vector kernel once
+ *    per vector in the same launch (each vector's weight pass after the first
+ *    mostly hits the last-level cache) and need K within one LDS slice
+ *    (QG_EUNSUPPORTED otherwise). With
  *    K > 4096 they need the workspace (QG_EWORKSPACE without it).
  *  - Workspace: calls that need scratch device memory take (ws, ws_bytes);
  *    qg_workspace_bytes() sizes it. The caller allocates it once, clears it
@@ -92,9 +95,9 @@ extern "C" {
 #define QG_EINVAL (-1)        /* NULL required pointer, bad size, misalignment, bad aliasing */
 #define QG_EUNSUPPORTED (-2)  /* valid but not provided: group != 64, affine bits not 2/4/8,
                                  LUT with bits != 4, dense with bits != 16, M outside [1,8],
-                                 K or k beyond the limits below, M > 1 with 8-bit or dense
-                                 weights, K % 512 != 0 or scales/biases/lut not 16-byte
-                                 aligned */
+                                 K or k beyond the limits below, M > 1 with 2/4-bit codes
+                                 and K % 512 != 0 or scales/biases/lut not 16-byte aligned,
+                                 M > 1 with 8-bit/dense weights and K beyond one slice */
 #define QG_EWORKSPACE (-3)    /* ws NULL or smaller than qg_workspace_bytes() */
 #define QG_ELAUNCH (-4)       /* the HIP runtime reported an error while enqueueing */
 #define QG_EDEVICE (-5)       /* no usable gfx950 device for the current HIP device */

@@ -79,8 +79,7 @@ def call_gemv(L, W=None, N=64, K=128, M=1, group=64, bits=4, fmt=0, x=X, xdt=1, 
     (dict(fmt=1, W=_mat(s=0, b=0, lut=0x4000), bits=8), qg.QG_EUNSUPPORTED),  # LUT needs 4 bits
     (dict(fmt=2, W=_mat(s=0, b=0), bits=4), qg.QG_EUNSUPPORTED),  # dense fields are 16 bits
     (dict(fmt=2, W=_mat(q=0, s=0, b=0), bits=16), qg.QG_EINVAL),  # dense without weights
-    (dict(M=2, K=512, bits=8), qg.QG_EUNSUPPORTED),              # matrix cores: 2/4-bit codes
-    (dict(M=2, K=512, fmt=2, W=_mat(s=0, b=0), bits=16), qg.QG_EUNSUPPORTED),
+    (dict(M=2, K=576, bits=4), qg.QG_EUNSUPPORTED),              # matrix cores: K % 512
     (dict(fmt=1, W=_mat(s=0, b=0, lut=0x4000), bits=2), qg.QG_EUNSUPPORTED),  # LUT needs 4 bits
     (dict(fmt=1, W=_mat()), qg.QG_EINVAL),        # LUT without a table
     (dict(fmt=7), qg.QG_EINVAL),

@@ -19,7 +19,6 @@ def run(*args):
     (["--bits", "16"], "--bits 16 --fmt 2"),
     (["--fmt", "2"], "--bits 16 --fmt 2"),
     (["--fmt", "1", "--bits", "2"], "4-bit codes"),
-    (["--m", "2", "--bits", "8"], "2- and 4-bit"),
     (["--m", "9"], "--m must be 1..8"),
 ])
 def test_rejected_before_any_gpu_work(args, needle):

@@ -241,13 +241,39 @@ def test_qmoe_experts_q8(qg, E, F, H, top_k):
 
 
 @pytest.mark.parametrize("name", ["q8", "f16"])
-def test_several_vectors_unsupported(qg, name):
-    """M > 1 runs on the matrix cores for 2- and 4-bit codes only."""
-    W = mat(29, "m2", 64, 512, name)
-    x = to_dev(synth.activations(29, "x", (2, 512), np.float16))
-    with pytest.raises(qg.QgError) as e:
-        qg.qgemv(qg.QMat.from_host(W, DEV), x)
-    assert e.value.status == qg.QG_EUNSUPPORTED
+@pytest.mark.parametrize("M", [2, 5, 8])
+@pytest.mark.parametrize("N,K", [(300, 1024), (1000, 4096), (64, 14336)])
+def test_several_vectors(qg, name, M, N, K):
+    """M activation vectors in one call (plain with residual, RMSNorm-fused
+    and gate.up SwiGLU): each vector against the oracle, and each equal bit
+    for bit to the one-vector call."""
+    say(f"several vectors {name} M={M} N={N} K={K}")
+    W = mat(34, ("mv", N, K), N, K, name)
+    Wu = mat(34, ("mvu", N, K), N, K, name)
+    X = synth.activations(34, ("x", M, K), (M, K), np.float32)
+    R = synth.activations(34, ("r", M, N), (M, N), np.float32)
+    g = synth.norm_weight(34, ("g", K), K)
+    w = ws(qg, qg.QG_OP_SWIGLU, N, K, name)
+    Wd, Wud = qg.QMat.from_host(W, DEV), qg.QMat.from_host(Wu, DEV)
+    Xd, Rd, gd = to_dev(X), to_dev(R), to_dev(g)
+    y = qg.qgemv(Wd, Xd, residual=Rd, ws=w)
+    yn = qg.qgemv_rmsnorm(Wd, Xd, gd, 1e-5, ws=w)
+    u = qg.qswiglu(Wd, Wud, Xd, gd, 1e-5, ws=w)
+    X16 = to_dev(X.astype(np.float16))
+    y16 = qg.qgemv(Wd, X16, ws=w)
+    torch.cuda.synchronize()
+    rows = sample_rows(N)
+    for m in range(M):
+        close(y.cpu().numpy()[m], oracle.gemv(W, X[m], R[m], nthreads=8), what=f"gemv vector {m}")
+        close(yn.cpu().numpy()[m][rows], oracle.rmsnorm_gemv(rows_of(W, rows), X[m], g, 1e-5),
+              what=f"rmsnorm vector {m}")
+        close(u.cpu().numpy()[m][rows], oracle.rmsnorm_swiglu(rows_of(W, rows), rows_of(Wu, rows), X[m],
+                                                               g, 1e-5), what=f"swiglu vector {m}")
+        close(y16.cpu().numpy()[m], oracle.gemv(W, X[m].astype(np.float16).astype(np.float64),
+                                                nthreads=8), what=f"fp16 x vector {m}")
+        one = qg.qgemv_rmsnorm(Wd, Xd[m].contiguous(), gd, 1e-5, ws=w)
+        torch.cuda.synchronize()
+        assert torch.equal(one, yn[m]), f"vector {m} differs from the one-vector call"
 
 
 @pytest.mark.parametrize("name", ["q8", "f16"])
