@@ -211,9 +211,8 @@ size_t mv_ws_bytes(int N, int M, int epi) {
 
 // Extra requirements of the M = 2..8 kernels: each wave loads whole
 // 512-code ranges of a row's scales/biases (or its table) with 16-byte loads.
-int check_mm(const qg_qmat* A, const qg_qmat* B, int K, int bits, int fmt) {
+int check_mm(const qg_qmat* A, const qg_qmat* B, int K, int fmt) {
   if (K % 512) return QG_EUNSUPPORTED;
-  if (bits == 8 || fmt == QG_DENSE) return QG_EUNSUPPORTED;  // matrix-core path: 2- and 4-bit codes
   const qg_qmat* mats[2] = {A, B};
   for (const qg_qmat* W : mats) {
     if (!W) continue;
@@ -291,7 +290,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   // Several vectors: 2- and 4-bit codes on the matrix cores; 8-bit and dense
   // weights through the streaming kernel, one workgroup row per vector.
   const bool on_mfma = M > 1 && bits != 8 && fmt != QG_DENSE;
-  if (on_mfma && (rc = check_mm(A, epi == kEpiSwiglu ? B : nullptr, K, bits, fmt))) return rc;
+  if (on_mfma && (rc = check_mm(A, epi == kEpiSwiglu ? B : nullptr, K, fmt))) return rc;
   if (N == 0) return QG_OK;
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;
