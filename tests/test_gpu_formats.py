@@ -297,3 +297,55 @@ def test_long_k_formats(qg, name, K, norm):
         ref = oracle.gemv(W, x, nthreads=8)
     torch.cuda.synchronize()
     close(y.cpu().numpy(), ref, what="long K")
+
+
+def test_graph_replay_several_vectors_and_batched_moe(qg):
+    """Q8 with four vectors and a four-token batched MoE layer captured in one
+    HIP graph, replayed several times with eager work between the replays;
+    every replay equals the eager run bit for bit."""
+    M, N, K = 4, 1000, 4096
+    E, F, H, top_k = 16, 128, 256, 3
+    W = mat(35, "graph", N, K, "q8")
+    Wd = qg.QMat.from_host(W, DEV)
+    g = to_dev(synth.norm_weight(35, "g", K))
+    X = to_dev(synth.activations(35, "x", (M, K), np.float32))
+    gate = synth.qmat(35, "gate_all", E * F, H, 8)
+    up = synth.qmat(35, "up_all", E * F, H, 8)
+    down = synth.qmat(35, "down_all", E * H, F, 8)
+    Gd, Ud, Dd = (qg.QMat.from_host(m, DEV) for m in (gate, up, down))
+    sh = tuple(qg.QMat.from_host(synth.qmat(35, n, r, c, 8), DEV)
+               for n, r, c in (("sh_gate", F, H), ("sh_up", F, H), ("sh_down", H, F)))
+    gm = to_dev(synth.norm_weight(35, "gm", H))
+    lg = to_dev(synth.router_logits(35, "route", (M, E)))
+    xm0 = to_dev(synth.activations(35, "xm", (M, H), np.float32))
+    wsv = ws(qg, qg.QG_OP_SWIGLU, N, K, "q8")
+    wsm = qg.workspace(qg.QG_OP_MOE, H, F, M, 8, 0, top_k, DEV)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    xm = torch.empty_like(xm0)
+
+    def step():
+        qg.qgemv_rmsnorm(Wd, X, g, 1e-5, y=y, ws=wsv)
+        xm.copy_(xm0)
+        for _ in range(3):
+            qg.qmoe_experts_batch(Gd, Ud, Dd, E, sh, lg, top_k, xm, gm, 1e-5, y=xm, ws=wsm)
+
+    step()
+    torch.cuda.synchronize()
+    ey, ex = y.clone(), xm.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for rep in range(4):
+        y.zero_()
+        xm.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ey), f"replay {rep}: several vectors differ"
+        assert torch.equal(xm, ex), f"replay {rep}: batched MoE differs"
+        step()  # eager work between the replays
+        torch.cuda.synchronize()
