@@ -298,10 +298,12 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   if (on_mfma)
     return run_mm(A, B, N, K, M, bits, fmt, epi, x, x_dtype, norm_w, eps, residual, y, ws,
                   have_ws, dev.cus, stream);
-  MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0, kSegNone}, dev.cus, have_ws);
-  if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;  // K too long for one slice: needs ws
-  // per-vector split-K partials are not provided: several vectors keep K in one slice
+  // Several vectors keep each vector's K in one slice (per-vector split-K
+  // partials are not provided): planned as if a workspace were there, so a
+  // K that needs slices is refused whatever workspace came with the call.
+  MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0, kSegNone}, dev.cus, M > 1 || have_ws);
   if (M > 1 && pl.splits > 1) return QG_EUNSUPPORTED;
+  if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;  // K too long for one slice: needs ws
   pl.tokens = M;
   MvParams p;
   memset(&p, 0, sizeof(p));

@@ -349,3 +349,19 @@ def test_graph_replay_several_vectors_and_batched_moe(qg):
         assert torch.equal(xm, ex), f"replay {rep}: batched MoE differs"
         step()  # eager work between the replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,K", [("q8", 65536), ("f16", 32768)])
+def test_several_vectors_beyond_one_slice_unsupported(qg, name, K):
+    """Several vectors keep each vector's K in one LDS slice; a K that would
+    need split-K is refused before anything is enqueued."""
+    W = mat(36, ("big", K), 16, K, name)
+    X = to_dev(synth.activations(36, ("x", K), (2, K), np.float32))
+    w = ws(qg, qg.QG_OP_GEMV, 16, K, name)
+    with pytest.raises(qg.QgError) as e:
+        qg.qgemv(qg.QMat.from_host(W, DEV), X, ws=w)
+    assert e.value.status == qg.QG_EUNSUPPORTED
+    # one vector of the same matrix splits K and runs
+    y = qg.qgemv(qg.QMat.from_host(W, DEV), X[0].contiguous(), ws=w)
+    torch.cuda.synchronize()
+    close(y.cpu().numpy(), oracle.gemv(W, X[0].cpu().numpy(), nthreads=8), what="one vector")
