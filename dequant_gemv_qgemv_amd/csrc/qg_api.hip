@@ -340,34 +340,38 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
 }  // namespace
 
 namespace qg {
-// Shared with the MoE launcher.
-int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have_ws, void* ws,
-                       size_t ws_bytes, size_t ws_offset, hipStream_t stream, int tokens) {
+// Shared with the MoE launcher: plans one launch (variant, split-K, grid,
+// workspace regions) into *p and *plan without enqueueing anything, so a
+// caller with several launches can validate all of them first.
+int mv_plan_internal(int bits, int fmt, int epi, MvParams* p, bool have_ws, void* ws,
+                     size_t ws_bytes, size_t ws_offset, int tokens, MvPlan* plan) {
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;
-  MvParams p = p0;
-  const MvPlan pl = plan_mv({p.N, p.K, bits, fmt, epi, p.seg_mode == kSegCols ? p.seg_len : 0,
-                             p.seg_mode}, dev.cus, have_ws);
+  const MvPlan pl = plan_mv({p->N, p->K, bits, fmt, epi, p->seg_mode == kSegCols ? p->seg_len : 0,
+                             p->seg_mode}, dev.cus, have_ws);
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;
   // a batched launch keeps each token's K in one slice (its split-K partials
   // and tickets would need one workspace region per token)
   if (tokens > 1 && pl.splits > 1) return QG_EUNSUPPORTED;
-  p.splits = pl.splits;
-  p.slice_chunks = pl.slice_chunks;
-  p.grid_x = pl.grid_x;
-  MvPlan lp = pl;
-  lp.tokens = tokens;
-  p.tokens = tokens;
+  p->splits = pl.splits;
+  p->slice_chunks = pl.slice_chunks;
+  p->grid_x = pl.grid_x;
+  *plan = pl;
+  plan->tokens = tokens;
+  p->tokens = tokens;
   if (pl.splits > 1) {
-    const size_t tickets = ((size_t)(p.N + 7) / 8 + 64) * 4;
+    const size_t tickets = ((size_t)(p->N + 7) / 8 + 64) * 4;
     const size_t tickets_al = (tickets + 255) / 256 * 256;
-    if (ws_offset + mv_ws_bytes(p.N, 1, epi) > ws_bytes) return QG_EWORKSPACE;
+    if (ws_offset + mv_ws_bytes(p->N, 1, epi) > ws_bytes) return QG_EWORKSPACE;
     char* base = static_cast<char*>(ws) + ws_offset;
-    p.tickets = reinterpret_cast<uint32_t*>(base);
-    p.partials = reinterpret_cast<float*>(base + tickets_al);
+    p->tickets = reinterpret_cast<uint32_t*>(base);
+    p->partials = reinterpret_cast<float*>(base + tickets_al);
   }
-  const hipError_t e = launch_mv(bits, fmt, epi, lp, p, stream);
-  return e == hipSuccess ? QG_OK : QG_ELAUNCH;
+  return QG_OK;
+}
+int mv_launch_planned(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
+                      hipStream_t stream) {
+  return launch_mv(bits, fmt, epi, plan, p, stream) == hipSuccess ? QG_OK : QG_ELAUNCH;
 }
 size_t mv_workspace_bytes(int N, int epi) { return mv_ws_bytes(N, 1, epi); }
 int device_ok() { return device_info().ok; }

@@ -10,8 +10,9 @@ namespace qg {
 
 constexpr int kThreads = 512;          // threads per workgroup (8 wave64s)
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxSeg = 8;             // matrices one launch can gather
 constexpr int kMaxRoutes = 8;          // routed experts per token
+constexpr int kMaxSeg = kMaxRoutes + 1; // matrices one launch can gather: the routed experts + the shared one
+static_assert(kMaxSeg >= kMaxRoutes + 1, "an expert launch gathers every routed expert and the shared one");
 
 // Device pointers of one planar quantized matrix.
 struct QMat {

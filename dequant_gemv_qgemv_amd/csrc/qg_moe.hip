@@ -26,8 +26,10 @@
 
 namespace qg {
 
-int mv_launch_internal(int bits, int fmt, int epi, const MvParams& p0, bool have_ws, void* ws,
-                       size_t ws_bytes, size_t ws_offset, hipStream_t stream, int tokens);
+int mv_plan_internal(int bits, int fmt, int epi, MvParams* p, bool have_ws, void* ws,
+                     size_t ws_bytes, size_t ws_offset, int tokens, MvPlan* plan);
+int mv_launch_planned(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
+                      hipStream_t stream);
 size_t mv_workspace_bytes(int N, int epi);
 int device_ok();
 
@@ -127,8 +129,6 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
   p.eps = eps;
   p.residual = nullptr;
   p.y = u;
-  rc = mv_launch_internal(bits, fmt, kEpiSwiglu, p, true, ws, ws_bytes, mv_off, stream, M);
-  if (rc) return rc;
 
   // 2. down over the K-concatenated experts, weighted, + residual
   MvParams d;
@@ -153,7 +153,16 @@ int plan_and_launch_moe(const qg_qmat* gate_all, const qg_qmat* up_all, const qg
   d.norm_w = nullptr;
   d.residual = x;
   d.y = y;
-  return mv_launch_internal(bits, fmt, kEpiStore, d, true, ws, ws_bytes, mv_off, stream, M);
+  // Both launches are planned before either is enqueued: a down projection
+  // that cannot run (K beyond one LDS slice for a batch, workspace too small)
+  // must not leave the gate.up launch's routes and u behind.
+  MvPlan plan_gu, plan_dn;
+  if ((rc = mv_plan_internal(bits, fmt, kEpiSwiglu, &p, true, ws, ws_bytes, mv_off, M, &plan_gu)))
+    return rc;
+  if ((rc = mv_plan_internal(bits, fmt, kEpiStore, &d, true, ws, ws_bytes, mv_off, M, &plan_dn)))
+    return rc;
+  if ((rc = mv_launch_planned(bits, fmt, kEpiSwiglu, plan_gu, p, stream))) return rc;
+  return mv_launch_planned(bits, fmt, kEpiStore, plan_dn, d, stream);
 }
 
 }  // namespace qg

@@ -1,6 +1,7 @@
-"""GPU parity of whole workloads, call by call: the Qwen3-0.6B-shaped
-28-layer stack with its logits head and top-40, and a token of 60 chained
-512-expert MoE layers. Every call is compared with the oracle applied to
+"""GPU parity of whole workloads, call by call: the Llama-3-8B-shaped
+32-layer stack (4-bit), the same layer shapes with 2-bit codes and with
+16-entry tables, the Qwen3-0.6B-shaped 28-layer stack with its logits head
+and top-40, and a token of 60 chained 512-expert MoE layers. Every call is compared with the oracle applied to
 that call's own GPU input (a chained stack amplifies fp32 rounding in
 tokens that cancel, so end-to-end equality is not a fair bar for one call);
 top-k indices and routing decisions are compared bit-exact."""
@@ -68,6 +69,61 @@ def sample_rows(N, n=160, seed=0):
         return np.arange(N)
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, N - 1], rng.choice(N, n - 2, replace=False)]))
+
+
+def check_layer(qg, w, x, QD, ws, li, n_rows=160):
+    """Runs one decoder layer through the four fused calls on the GPU and
+    checks each call against the oracle on that call's own GPU input (sampled
+    rows). Returns the layer's output (device)."""
+    d = {n: qg.QMat.from_host(w[n], DEV) for n in ("qkv", "o", "gate", "up", "down")}
+    qkv = qg.qgemv_rmsnorm(d["qkv"], x, to_dev(w["g_attn"]), EPS, ws=ws)
+    h = qg.qgemv(d["o"], qkv[:QD], residual=x, ws=ws)
+    u = qg.qswiglu(d["gate"], d["up"], h, to_dev(w["g_ffn"]), EPS, ws=ws)
+    y = qg.qgemv(d["down"], u, residual=h, ws=ws)
+    torch.cuda.synchronize()
+    xc, qc, hc, uc, yc = (t.cpu().numpy() for t in (x, qkv, h, u, y))
+    H = len(xc)
+    rq, rh, rf = (sample_rows(len(qc), n_rows, li), sample_rows(H, n_rows, li + 1),
+                  sample_rows(len(uc), n_rows, li + 2))
+    close(qc[rq], oracle.rmsnorm_gemv(rows_of(w["qkv"], rq), xc, w["g_attn"], EPS),
+          what=f"layer {li} qkv")
+    close(hc[rh], oracle.gemv(rows_of(w["o"], rh), qc[:QD], xc[rh]), what=f"layer {li} o")
+    close(uc[rf], oracle.rmsnorm_swiglu(rows_of(w["gate"], rf), rows_of(w["up"], rf), hc,
+                                        w["g_ffn"], EPS), what=f"layer {li} gate.up")
+    close(yc[rh], oracle.gemv(rows_of(w["down"], rh), uc, hc[rh]), what=f"layer {li} down")
+    return y
+
+
+def test_llama_stack_32_layers(qg):
+    """The Llama-3-8B-shaped stack at M = 1, 4-bit g64, all 32 layers chained
+    on the GPU (the residual grows by orders of magnitude along the chain):
+    every call of every layer against the oracle."""
+    model = synth.LLAMA3_8B
+    H, QD = model["hidden"], model["q_dim"]
+    seed = 1234
+    say("llama stack: 32 layers, 4-bit")
+    x = torch.from_numpy(synth.activations(seed, "x0", H, np.float32)).to(DEV)
+    ws = qg.workspace(qg.QG_OP_SWIGLU, model["ffn"], model["ffn"], 1, 4, 0, 1, DEV)
+    scale0 = float(x.abs().max())
+    for li in range(model["layers"]):
+        x = check_layer(qg, synth.layer_weights(seed, model, li), x, QD, ws, li)
+    # the chain really grows: the fp32 residual ends orders of magnitude above x0
+    assert float(x.abs().max()) > 1e3 * scale0
+
+
+@pytest.mark.parametrize("bits,fmt", [(2, synth.AFFINE), (4, synth.LUT)])
+def test_llama_layers_2bit_and_table(qg, bits, fmt):
+    """The 2-bit and 16-entry-table variants of the Llama layer shapes at
+    M = 1 through the fused calls (rmsnorm + QKV, O + residual, rmsnorm +
+    gate.up SwiGLU, down + residual), four chained layers, call by call."""
+    model = dict(synth.LLAMA3_8B)
+    H, QD = model["hidden"], model["q_dim"]
+    seed = 2024
+    say(f"llama layers bits={bits} fmt={fmt}")
+    x = torch.from_numpy(synth.activations(seed, "x0", H, np.float32)).to(DEV)
+    ws = qg.workspace(qg.QG_OP_SWIGLU, model["ffn"], model["ffn"], 1, bits, fmt, 1, DEV)
+    for li in range(4):
+        x = check_layer(qg, synth.layer_weights(seed, model, li, bits, fmt), x, QD, ws, li)
 
 
 def test_qwen_stack_and_head(qg):

@@ -198,10 +198,20 @@ def test_qgemv_2bit_and_lut(qg, bits, fmt, N, K):
     close(y.cpu().numpy(), oracle.gemv(W, x, nthreads=8), what="2bit/lut")
 
 
+FMTS = [(4, synth.AFFINE), (2, synth.AFFINE), (4, synth.LUT)]
+
+
+def fmt_tag(bits, fmt):
+    return () if (bits, fmt) == (4, synth.AFFINE) else (bits, fmt)
+
+
+@pytest.mark.parametrize("bits,fmt", FMTS)
 @pytest.mark.parametrize("N,K", [(6144, 4096), (2048, 1024), (100, 14336)])
-def test_qgemv_rmsnorm(qg, N, K):
-    say(f"qgemv_rmsnorm N={N} K={K}")
-    W = synth.qmat(9, ("rn", N, K), N, K, 4)
+def test_qgemv_rmsnorm(qg, N, K, bits, fmt):
+    """Includes the Llama QKV shape (6144 x 4096) in every format: the 2-bit
+    and table-format stacks run exactly this launch."""
+    say(f"qgemv_rmsnorm N={N} K={K} bits={bits} fmt={fmt}")
+    W = synth.qmat(9, ("rn", N, K) + fmt_tag(bits, fmt), N, K, bits, fmt)
     g = synth.norm_weight(9, ("g", K), K)
     x = synth.activations(9, ("x", K), K, np.float32) * 3.0
     r = synth.activations(9, ("r", N), N, np.float32)
@@ -213,12 +223,15 @@ def test_qgemv_rmsnorm(qg, N, K):
     close(y.cpu().numpy()[rows], ref, what="rmsnorm")
 
 
+@pytest.mark.parametrize("bits,fmt", FMTS)
 @pytest.mark.parametrize("F,K,norm", [(14336, 4096, True), (3072, 1024, True), (1000, 2048, False),
                                       (8, 64, True)])
-def test_qswiglu(qg, F, K, norm):
-    say(f"qswiglu F={F} K={K} norm={norm}")
-    Wg = synth.qmat(10, ("gate", F, K), F, K, 4)
-    Wu = synth.qmat(10, ("up", F, K), F, K, 4)
+def test_qswiglu(qg, F, K, norm, bits, fmt):
+    """Includes the Llama gate.up shape (2 x 14336 x 4096, normed) in every
+    format: the 2-bit and table-format stacks run exactly this launch."""
+    say(f"qswiglu F={F} K={K} norm={norm} bits={bits} fmt={fmt}")
+    Wg = synth.qmat(10, ("gate", F, K) + fmt_tag(bits, fmt), F, K, bits, fmt)
+    Wu = synth.qmat(10, ("up", F, K) + fmt_tag(bits, fmt), F, K, bits, fmt)
     g = synth.norm_weight(10, ("g", K), K) if norm else None
     x = synth.activations(10, ("x", K), K, np.float32)
     ws = ws_for(qg, qg.QG_OP_SWIGLU, F, K)
@@ -299,8 +312,12 @@ def moe_weights(seed, E, F, H):
 
 
 @pytest.mark.parametrize("E,F,H,top_k,shared", [(16, 128, 256, 3, True), (8, 64, 128, 1, False),
-                                                (512, 1024, 4096, 3, True)])
+                                                (512, 1024, 4096, 3, True), (16, 128, 256, 8, True),
+                                                (12, 64, 192, 8, False), (3, 8192, 256, 3, True)])
 def test_qmoe_experts(qg, E, F, H, top_k, shared):
+    """Includes top_k = 8 with the shared expert (nine gathered matrices in one
+    launch) and F = 8192 with three routed experts + the shared one, whose
+    K-concatenated down projection (32768 codes) is split across workgroups."""
     say(f"qmoe_experts E={E} F={F} H={H} top_k={top_k}")
     gate, up, down, sh = moe_weights(15, E, F, H)
     g = synth.norm_weight(15, "g", H)
@@ -413,6 +430,7 @@ def test_long_k_staging_rounds(qg, bits, fmt, K, norm):
 
 
 @pytest.mark.parametrize("E,F,H,top_k,M,shared,bits,seed", [(16, 128, 256, 3, 5, True, 4, 33),
+                                                            (16, 128, 256, 8, 3, True, 4, 33),
                                                             (8, 64, 128, 1, 2, False, 4, 33),
                                                             (512, 1024, 4096, 3, 8, True, 4, 33),
                                                             (16, 1024, 4096, 3, 4, True, 8, 28)])
@@ -461,3 +479,27 @@ def test_qmoe_experts_batch(qg, E, F, H, top_k, M, shared, bits, seed):
     torch.cuda.synchronize()
     assert torch.equal(xin, y), "in-place batch differs"
     assert torch.equal(y0, y[0]), "token 0 alone differs"
+
+
+def test_qmoe_batch_refused_enqueues_nothing(qg):
+    """A batch whose concatenated down projection needs split-K is refused
+    (QG_EUNSUPPORTED) before either launch is enqueued: the routing outputs
+    keep their previous contents."""
+    E, F, H, top_k, M = 3, 8192, 256, 3, 2
+    say("qmoe_experts_batch refused case")
+    gate, up, down, sh = moe_weights(16, E, F, H)
+    Gd, Ud, Dd = dev_mat(qg, gate), dev_mat(qg, up), dev_mat(qg, down)
+    shd = tuple(dev_mat(qg, m) for m in sh)
+    X = synth.activations(16, "xb", (M, H), np.float32)
+    lg = synth.router_logits(16, "routeb", (M, E))
+    ws = qg.workspace(qg.QG_OP_MOE, H, F, M, 4, 0, top_k, DEV)
+    ids = torch.full((M, top_k), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((M, top_k), -7.0, dtype=torch.float32, device=DEV)
+    xd = to_dev(X)
+    y = torch.full((M, H), 3.0, dtype=torch.float32, device=DEV)
+    with pytest.raises(qg.QgError) as ei:
+        qg.qmoe_experts_batch(Gd, Ud, Dd, E, shd, to_dev(lg), top_k, xd, None, 1e-5, y=y,
+                              sel_ids=ids, sel_w=w, ws=ws)
+    assert ei.value.status == qg.QG_EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((ids == -7).all()) and bool((w == -7.0).all()) and bool((y == 3.0).all())

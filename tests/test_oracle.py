@@ -388,6 +388,97 @@ def test_decoder_layer_zero_weights_identity():
     assert np.array_equal(oracle.decoder_layer(w, x, 128), x)
 
 
+def _rowconst(N, K, b):
+    """N x K 4-bit matrix with scale 0 and bias b[n] in every group: W.v = b_n sum(v)."""
+    b = np.broadcast_to(np.asarray(b, np.float64), (N,))
+    return {"N": N, "K": K, "bits": 4, "fmt": synth.AFFINE, "group": 64,
+            "q": synth.words(synth.stream(0, "rowconst", N, K), (N, K * 4 // 32)),
+            "scales": np.zeros((N, K // 64), np.float16),
+            "biases": np.repeat(b[:, None], K // 64, axis=1).astype(np.float16), "lut": None}
+
+
+def _two_level_x(H, lo, hi):
+    return np.where(np.arange(H) < H // 2, lo, hi).astype(np.float64)
+
+
+def test_decoder_layer_hand_case():
+    """The whole layer against the hand derivation in the golden file: a wrong
+    q-slice, the FFN reading x instead of h, swapped norm weights or a dropped
+    residual each move the answer."""
+    c = GOLDEN["decoder_layer"]
+    H, QD, F = c["hidden"], c["q_dim"], c["ffn"]
+    b_qkv = np.concatenate([np.full(QD, c["b_q"]), np.full(c["qkv_rows"] - QD, c["b_kv"])])
+    w = {"qkv": _rowconst(c["qkv_rows"], H, b_qkv), "o": _rowconst(H, QD, c["b_o"]),
+         "gate": _rowconst(F, H, c["b_gate"]), "up": _rowconst(F, H, c["b_up"]),
+         "down": _rowconst(H, F, c["b_down"]),
+         "g_attn": np.full(H, c["g_attn"], np.float16), "g_ffn": np.full(H, c["g_ffn"], np.float16)}
+    x = _two_level_x(H, 1.0, 7.0)
+    h = _two_level_x(H, 1.8, 7.8)
+    S = 614.4 / np.sqrt(32.04)
+    expect = h + (S / 64) / (1 + np.exp(-S / 64)) * S / 128
+    np.testing.assert_allclose(oracle.decoder_layer(w, x, QD, c["eps"]), expect, rtol=1e-13)
+
+
+def test_rmsnorm_gemv_closed_form():
+    """W . rmsnorm(x; g) + r with rows of constant weight: b_n * sum(g x) / rms(x) + r_n."""
+    H, N = 128, 5
+    b = np.array([1, -2, 3, 0.5, 0.25]) / 64
+    W = _rowconst(N, H, b)
+    x = _two_level_x(H, 1.0, 7.0)  # rms 5
+    g = np.full(H, 2.0, np.float16)
+    r = np.arange(N, dtype=np.float64)
+    y = oracle.rmsnorm_gemv(W, x, g, 0.0, r)
+    np.testing.assert_allclose(y, b * (2 * 64 * 8 / 5) + r, rtol=1e-14)
+    # scale invariance of the norm: 10 x gives the same output
+    np.testing.assert_allclose(oracle.rmsnorm_gemv(W, 10 * x, g, 0.0, r), y, rtol=1e-14)
+
+
+def test_rmsnorm_swiglu_closed_form():
+    """gate rows 1/64 and up rows 1/128 of constant weight after the norm:
+    u = silu(S/64) * S/128 with S = sum(g x) / rms(x) = 102.4."""
+    H, F = 64, 3
+    x = _two_level_x(H, 1.0, 7.0)
+    g = np.full(H, 2.0, np.float16)
+    u = oracle.rmsnorm_swiglu(_rowconst(F, H, 1 / 64), _rowconst(F, H, 1 / 128), x, g, 0.0)
+    np.testing.assert_allclose(u, np.full(F, 0.8 * 1.6 / (1 + np.exp(-1.6))), rtol=1e-14)
+
+
+def test_logits_topk_closed_form():
+    """Rows of constant weight b_n: z_n = b_n * sum(g x) / rms(x), the same for
+    x and 10 x; the top-k follows the order of b (ties by lower index)."""
+    H = 64
+    b = np.array([0.5, -1, 2, 2, 0.25, 1]) / 32
+    W = _rowconst(len(b), H, b)
+    x = _two_level_x(H, 1.0, 7.0)
+    g = np.full(H, 0.5, np.float16)
+    for scale in (1.0, 10.0):
+        z, idx, vals = oracle.logits_topk(W, scale * x, 4, g, 0.0)
+        np.testing.assert_allclose(z, b * (0.5 * 32 * 8 / 5), rtol=1e-14)
+        assert list(idx) == [2, 3, 5, 0]
+
+
+def test_moe_expert_rows_closed_form():
+    """Expert e's rows are rows [e*N, (e+1)*N) of the stacked tensors: expert
+    e's down weight is the constant (e+1)/64, gate/up constants give one known
+    u; the routed expert's number shows in the output."""
+    E, F, H = 5, 64, 64
+    gate = _rowconst(E * F, H, 1 / 64)
+    up = _rowconst(E * F, H, 1 / 128)
+    down = _rowconst(E * H, F, np.repeat((np.arange(E) + 1) / 64, H))
+    for W in (gate, up, down):
+        W["E"] = E
+    x = _two_level_x(H, 1.0, 7.0)
+    a = x.sum() / 64  # gate_j (no norm: x' = x), 4.0
+    c = x.sum() / 128  # up_j, 2.0
+    u = a / (1 + np.exp(-a)) * c
+    for e in range(E):
+        lg = np.full(E, -1.0)
+        lg[e] = 3.0
+        y, ids, w = oracle.moe_layer(gate, up, down, None, lg, 1, x, None)
+        assert list(ids) == [e] and w[0] == 1.0
+        np.testing.assert_allclose(y, x + (e + 1) / 64 * F * u, rtol=1e-14)
+
+
 def test_expert_bytes_match_page():
     """The page's per-expert size pins 4-bit codes + fp16 scale + fp16 bias per 64."""
     c = GOLDEN["expert_bytes"]

@@ -1,9 +1,12 @@
 """The oracle's pins are sharp: each plausible mistake planted in a copy of
 the oracle's C source (a dropped term, a wrong sign or index, a transposed
-field order) makes the pin suite fail. CPU only; the planted copies live in a
-temporary directory and are loaded through QG_ORACLE_LIB in a subprocess."""
+field order) or of its Python compositions (decoder layer, MoE layer, logits
+head) makes the pin suite fail. CPU only; the planted copies live in a
+temporary directory: C mutants are loaded through QG_ORACLE_LIB, Python
+mutants run from a copy of the package tree, both in a subprocess."""
 
 import os
+import shutil
 import subprocess
 import sys
 
@@ -72,4 +75,55 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle.py")],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
+
+
+SRC_PY = os.path.join(ROOT, "oracle", "__init__.py")
+
+PY_MUTANTS = [
+    ("decoder_ffn_reads_x", 'u = rmsnorm_swiglu(w["gate"], w["up"], h, w["g_ffn"], eps, nthreads)',
+     'u = rmsnorm_swiglu(w["gate"], w["up"], x, w["g_ffn"], eps, nthreads)'),
+    ("decoder_norm_weights_swapped",
+     'qkv = rmsnorm_gemv(w["qkv"], x, w["g_attn"], eps, None, nthreads)\n    a = qkv[:q_dim]\n'
+     '    h = gemv(w["o"], a, x, nthreads)\n    u = rmsnorm_swiglu(w["gate"], w["up"], h, w["g_ffn"], eps,',
+     'qkv = rmsnorm_gemv(w["qkv"], x, w["g_ffn"], eps, None, nthreads)\n    a = qkv[:q_dim]\n'
+     '    h = gemv(w["o"], a, x, nthreads)\n    u = rmsnorm_swiglu(w["gate"], w["up"], h, w["g_attn"], eps,'),
+    ("decoder_wrong_q_slice", "a = qkv[:q_dim]", "a = qkv[-q_dim:]"),
+    ("decoder_o_no_residual", 'h = gemv(w["o"], a, x, nthreads)', 'h = gemv(w["o"], a, None, nthreads)'),
+    ("decoder_down_residual_x", 'return gemv(w["down"], u, h, nthreads)',
+     'return gemv(w["down"], u, x, nthreads)'),
+    ("rmsnorm_gemv_drops_residual", "y = gemv(W, Xn, residual, nthreads)",
+     "y = gemv(W, Xn, None, nthreads)"),
+    ("rmsnorm_gemv_no_norm", "Xn = np.stack([rmsnorm(row, g, eps) for row in X])\n    y = gemv",
+     "Xn = X\n    y = gemv"),
+    ("swiglu_gate_up_swapped", "u = swiglu(Wg, Wu, Xn, nthreads)", "u = swiglu(Wu, Wg, Xn, nthreads)"),
+    ("moe_shared_weighted", "y = y + gemv(shared[2], u, None, nthreads)",
+     "y = y + wts[0] * gemv(shared[2], u, None, nthreads)"),
+    ("moe_weights_reversed", "for e, we in zip(ids, wts):", "for e, we in zip(ids, wts[::-1]):"),
+    ("moe_no_norm", "xn = x if g is None else rmsnorm(x, g, eps)\n    ids, wts",
+     "xn = x\n    ids, wts"),
+    ("logits_no_norm", "xn = x if g is None else rmsnorm(x, g, eps)\n    z = gemv",
+     "xn = x\n    z = gemv"),
+    ("expert_slice_next_expert", "out[key] = W_all[key][e * N:(e + 1) * N]",
+     'out[key] = W_all[key][((e + 1) % W_all["E"]) * N:((e + 1) % W_all["E"] + 1) * N]'),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_planted_composition_mistake_is_caught(name, old, new, tmp_path):
+    src = open(SRC_PY).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    for d in ("oracle", "synth"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("__pycache__", "*.so"))
+    os.makedirs(tmp_path / "tests")
+    for f in ("conftest.py", "test_oracle.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    (tmp_path / "oracle" / "__init__.py").write_text(src.replace(old, new))
+    import oracle
+    env = dict(os.environ, QG_ORACLE_LIB=oracle.build(force=False))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        str(tmp_path / "tests" / "test_oracle.py")],
+                       env=env, cwd=str(tmp_path), capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
