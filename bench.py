@@ -22,9 +22,10 @@ rotated per token).
 Prints ONE JSON line: value = algorithmic bytes per step / time per step
 (GB/s), plus equivalent steps/s, the roofline of the dominant kernel
 (back-to-back launches over distinct weights in a graph, timed with HIP
-events on the stream that replays it), the measured device-to-device copy
-bandwidth, and the CPU oracle's throughput on a bounded sample of the same
-workload.
+events on the stream that replays it), the streaming-read and copy peaks
+measured in the same run with the library's own probes (qg_probe_read,
+qg_probe_copy), and the CPU oracle's throughput on a bounded sample of the
+same workload (all threads the host grants, and one thread).
 """
 
 from __future__ import annotations
@@ -44,8 +45,9 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (% of roofline) for 4-bit group-64 GEMV; equiv decode tok/s"
 HBM_PEAK_GBS = 8000.0
 EPS = 1e-5
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qswiglu_llama3_8b.json")
-KERNEL_SOURCES = ["qg_mv.hip", "qg_common.h", "qg_internal.h"]
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["qg_mv.hip", "qg_mm.hip", "qg_topk.hip", "qg_moe.hip", "qg_api.hip", "qg_common.h",
+                  "qg_internal.h"]
 
 
 def log(msg):
@@ -63,54 +65,128 @@ def kernel_hash() -> str:
 REF_READ_BYTES = 64 << 20  # reference streaming read of known size for counter calibration
 
 
-def pmc_pass(qg, layers, model, dev):
+def traffic_name(args) -> str:
+    """File stem of a workload's counter summary under profiles/."""
+    if args.config == "stack":
+        fmt = {0: f"{args.bits}bit", 1: "lut", 2: "dense_f16"}[args.fmt]
+        return f"traffic_llama3_8b_stack_{fmt}_m{args.m}"
+    return {"single": "traffic_qgemv_2048x2048_single", "moe": f"traffic_qmoe_512_experts_m{args.m}",
+            "qwen": "traffic_qwen3_06b_stack_logits", "attn": "traffic_qattn"}[args.config]
+
+
+def pmc_reference_reads(qg, dev):
+    """Two streaming reads of exactly REF_READ_BYTES: the counters' unit."""
     import torch
-    H, FF = model["hidden"], model["ffn"]
-    h = torch.randn(H, device=dev)
-    u = torch.empty(FF, dtype=torch.float32, device=dev)
-    ws = qg.workspace(qg.QG_OP_SWIGLU, FF, H, 1, 4, 0, 1, dev)
-    for i in range(8):
-        d = layers[i % len(layers)]
-        qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
     buf = torch.ones(2 * REF_READ_BYTES // 4, dtype=torch.float32, device=dev)
     out = torch.empty(512 * 256, dtype=torch.int32, device=dev)
     for i in range(2):
         qg.qg_probe_read(buf[i * REF_READ_BYTES // 4:(i + 1) * REF_READ_BYTES // 4], out, 512)
     torch.cuda.synchronize()
-    log("pmc pass done")
 
 
-def summarize_pmc(fetch_csv, write_csv):
-    """HBM bytes per gate.up SwiGLU launch from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), scaled by the FETCH_SIZE the reference read of REF_READ_BYTES
-    reports (the counter's unit on this device)."""
-    import csv
+def pmc_pass(args, qg, dev, run_once, labels, nbytes, outputs):
+    """Counter pass: two reference reads, then the workload's launches once,
+    eagerly, in a known order (labels[i] names product launch i). Writes the
+    labels and each launch's algorithmic bytes next to the counter output."""
+    import torch
+    pmc_reference_reads(qg, dev)
+    run_once()
+    torch.cuda.synchronize()
+    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    meta = {"workload": traffic_name(args), "labels": labels, "bytes": nbytes, "outputs": outputs,
+            "argv": sys.argv[1:], "kernel_hash": kernel_hash()}
+    with open(os.path.join(ROOT, "gpurun_out", "pmc_labels.json"), "w") as fh:
+        json.dump(meta, fh, indent=1)
+    log(f"pmc pass done: {len(labels)} launches")
+
+
+PRODUCT_KERNELS = ("qmv_kernel", "qmm_kernel", "topk_kernel", "sample_kernel", "attn_kernel")
+
+
+def short_kernel(name: str) -> str:
+    """'void qg::(anonymous namespace)::qmv_kernel<4, 0, 64, 1, 0, 0, 2>(qg::MvParams)'
+    -> 'qmv_kernel<4, 0, 64, 1, 0, 0, 2>'."""
     import re
+    m = re.search(r"(\w+_kernel(<[^>]*>)?)", name)
+    return m.group(1) if m else name[:60]
 
-    def per_kernel(path, counter):
-        sw, ref = [], []
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            v = float(r["Counter_Value"]) * 1024.0
-            if re.search(r"qmv_kernel<4, 0, \d+, \d, 1, 0, \d>", r["Kernel_Name"]):
-                sw.append(v)
-            elif "probe_read" in r["Kernel_Name"]:
-                ref.append(v)
-        return sw, ref
 
-    sw_f, ref_f = per_kernel(fetch_csv, "FETCH_SIZE")
-    sw_w, _ = per_kernel(write_csv, "WRITE_SIZE")
-    scale = REF_READ_BYTES / (sum(ref_f) / len(ref_f))
-    fetch = sum(sw_f) / len(sw_f) * scale
-    write = sum(sw_w) / len(sw_w) * scale
-    out = {"kernel": "qswiglu 14336x4096 x2 (gate.up, rmsnorm)", "kernel_hash": kernel_hash(),
-           "counter_scale": round(scale, 4), "fetch_bytes_per_launch": round(fetch),
-           "write_bytes_per_launch": round(write), "bytes_per_launch": round(fetch + write),
-           "launches": len(sw_f)}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
-    print(json.dumps(out))
+def summarize_pmc(fetch_csv, write_csv, labels_json):
+    """HBM bytes per launch of a workload from FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), scaled by what FETCH_SIZE reports for the reference reads
+    of REF_READ_BYTES (the counter's unit on this device); written to
+    profiles/<workload>.json and .md next to the algorithmic bytes."""
+    import csv
+    meta = json.load(open(labels_json))
+
+    def rel(path):
+        return os.path.relpath(os.path.abspath(path), ROOT)
+
+    def dispatches(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        ref = [float(r["Counter_Value"]) * 1024.0 for r in rows if "probe_read" in r["Kernel_Name"]]
+        ours = [(r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0) for r in rows
+                if any(k in r["Kernel_Name"] for k in PRODUCT_KERNELS)]
+        return ref, ours
+
+    ref_f, fetch = dispatches(fetch_csv, "FETCH_SIZE")
+    _, write = dispatches(write_csv, "WRITE_SIZE")
+    labels = meta["labels"]
+    if len(fetch) != len(labels) or len(write) != len(labels):
+        raise SystemExit(f"{len(fetch)}/{len(write)} product dispatches against {len(labels)} labels")
+    scale = REF_READ_BYTES / (sum(ref_f[:2]) / 2)
+    per = {}
+    for lab, (kn, f), (_, w) in zip(labels, fetch, write):
+        d = per.setdefault(lab, {"kernel": short_kernel(kn), "fetch": [], "write": []})
+        d["fetch"].append(f * scale)
+        d["write"].append(w * scale)
+    out = {"workload": meta["workload"], "kernel_hash": meta.get("kernel_hash", kernel_hash()),
+           "counter_scale": round(scale, 4),
+           "argv": meta["argv"], "launches": {}}
+    lines = [f"# HBM traffic per launch: {meta['workload']}", "",
+             "Two counter passes, each on its own run (GPU box, repository root as $R):", "",
+             f"    cd /tmp && timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "
+             f"$R/{rel(os.path.dirname(fetch_csv))} -o run -- python3 $R/bench.py {' '.join(meta['argv'])}",
+             f"    cd /tmp && timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "
+             f"$R/{rel(os.path.dirname(write_csv))} -o run -- python3 $R/bench.py {' '.join(meta['argv'])}",
+             f"    python bench.py --summarize-pmc {rel(fetch_csv)} {rel(write_csv)} {rel(labels_json)}", "",
+             f"The pass first streams two buffers of exactly {REF_READ_BYTES >> 20} MiB with qg_probe_read; "
+             f"FETCH_SIZE reports {sum(ref_f[:2]) / 2 / 1024:.0f} KiB for each, so every FETCH_SIZE and "
+             f"WRITE_SIZE value is multiplied by {scale:.4f}. Values are averages over the launches "
+             "of each kind in one eager pass of the workload.", "",
+             "| launch | kernel | n | algorithmic B | HBM fetch B | HBM write B | traffic / algorithmic "
+             "| outputs | traffic B per output |", "|---|---|---|---|---|---|---|---|---|"]
+    for lab, d in per.items():
+        f = sum(d["fetch"]) / len(d["fetch"])
+        w = sum(d["write"]) / len(d["write"])
+        alg = meta["bytes"][lab]
+        n_out = meta["outputs"][lab]
+        out["launches"][lab] = {"kernel": d["kernel"], "n": len(d["fetch"]), "algorithmic_bytes": alg,
+                                "fetch_bytes": round(f), "write_bytes": round(w),
+                                "bytes_per_launch": round(f + w), "ratio": round((f + w) / alg, 4),
+                                "outputs": n_out, "bytes_per_output": round((f + w) / n_out, 1)}
+        lines.append(f"| {lab} | `{d['kernel']}` | {len(d['fetch'])} | {alg} | {f:.0f} | {w:.0f} | "
+                     f"{(f + w) / alg:.3f} | {n_out} | {(f + w) / n_out:.1f} |")
+    lines += ["", f"Source hash of the kernels these counters were taken on: `{out['kernel_hash']}` "
+              "(bench.py reports a launch's traffic only while the hash matches)."]
+    stem = os.path.join(PROFILES, meta["workload"])
+    json.dump(out, open(stem + ".json", "w"), indent=1)
+    open(stem + ".md", "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_of(args, label):
+    """Counter-measured HBM bytes of one launch kind of this workload, or None
+    when there are none for the current kernel sources."""
+    path = os.path.join(PROFILES, traffic_name(args) + ".json")
+    try:
+        tr = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if tr.get("kernel_hash") != kernel_hash():
+        return None
+    return tr.get("launches", {}).get(label, {}).get("bytes_per_launch")
 
 
 def summarize_trace(path):
@@ -214,21 +290,41 @@ def time_launches(fn, n, use_graph, reps=5):
     return a.elapsed_time(b) * 1e3 / (reps * n)
 
 
-def copy_peak(dev):
-    """Device-to-device copy bandwidth (read + write bytes), 1 GiB buffers."""
+def probe_peaks(qg, dev):
+    """Streaming-read and copy bandwidth of this GPU, measured with the
+    library's probes over 1 GiB (best of several grid sizes, 10 launches
+    each, HIP events), and torch's device copy for reference. Copy figures
+    count read + write bytes."""
     import torch
     nb = 1 << 30
     src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    return 2 * nb * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    out = torch.empty(16384 * 256, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn, moved):
+        rates = []
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            fn(blocks)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                fn(blocks)
+            e1.record()
+            torch.cuda.synchronize()
+            rates.append(moved * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        return max(rates)
+
+    read = max(best(lambda b: qg.qg_probe_read(src, out, b), nb),
+               best(lambda b: qg.qg_probe_read(src, out, b, cached=True), nb))
+    copy = best(lambda b: qg.qg_probe_copy(dst, src, b), 2 * nb)
+    tcopy = best(lambda b: dst.copy_(src), 2 * nb)
+    del src, dst, out
+    torch.cuda.empty_cache()
+    return {"read_gbs": round(read, 1), "copy_gbs": round(copy, 1), "torch_copy_gbs": round(tcopy, 1),
+            "how": "qg_probe_read / qg_probe_copy over 1 GiB, 16-byte accesses (read: non-temporal "
+                   "and cached, copy: non-temporal), best of 1024..16384 workgroups of 256 threads, "
+                   "10 launches each; copy counts read + write bytes"}
 
 
 def cpu_sample(work, seconds):
@@ -247,11 +343,49 @@ def cpu_sample(work, seconds):
 
 
 def oracle_threads():
-    return max(1, min(16, os.cpu_count() or 1))
+    """Threads for the oracle: every core this process may use (the host's
+    CPU share when OMP_NUM_THREADS states it)."""
+    n = os.cpu_count() or 1
+    try:
+        n = min(n, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):
+        pass
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
-def emit(args, workload, cfg, step_bytes, ms, dom, copy_gbs, cpu, dtype="f32"):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(make_work, seconds, describe, extra=None):
+    """The oracle timed on the host: make_work(threads) gives work(i) -> bytes
+    (None when the sample is exhausted); one leg with every thread the host
+    grants, one with a single thread on a fresh sample."""
+    th = oracle_threads()
+    done, n, dt = cpu_sample(make_work(th), seconds)
+    d1, n1, dt1 = cpu_sample(make_work(1), max(seconds / 2, 3.0))
+    out = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+           "sample": describe(n, done, dt) + f", {th} threads",
+           "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+           "single_thread": {"value": round(d1 / dt1 / 1e9, 4), "unit": "GB/s",
+                             "sample": describe(n1, d1, dt1) + ", 1 thread"}}
+    if extra:
+        out.update(extra(n, done, dt))
+    return out
+
+
+def emit(args, workload, cfg, step_bytes, ms, dom, peaks, cpu, dtype):
     gbs = step_bytes / (ms * 1e-3) / 1e9
+    dom["frac_of_read_peak"] = round(dom["achieved"] / peaks["read_gbs"], 4)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -268,12 +402,23 @@ def emit(args, workload, cfg, step_bytes, ms, dom, copy_gbs, cpu, dtype="f32"):
         "config": dict({"workload": workload, "bytes_per_step": step_bytes}, **cfg),
         "steps_per_s": round(1e3 / ms, 2),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "frac_of_copy_peak": round(gbs / copy_gbs, 4),
-        "copy_peak_gbs": round(copy_gbs, 1),
+        "frac_of_read_peak": round(gbs / peaks["read_gbs"], 4),
+        "frac_of_copy_peak": round(gbs / peaks["copy_gbs"], 4),
+        "peaks": peaks,
         "roofline": dom,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def arith_dtype(bits, fmt, m):
+    """The arithmetic the path computes in: affine and dense weights as fp16
+    x fp16 products (codes are exact fp16 values; x is staged in fp16 after a
+    power-of-two range scale) accumulated in fp32; table weights in fp32."""
+    if fmt == 1 and m == 1:
+        return "f32 (fp16 table entries x fp32 x, fp32 accumulate)"
+    core = "mfma f16xf16->f32" if (m > 1 and bits in (2, 4)) else "f16xf16->f32"
+    return f"{core} (x staged in fp16 after a power-of-two scale, fp32 accumulate)"
 
 
 def roofline(kernel, nbytes, us, traffic=None):
@@ -313,10 +458,15 @@ def run_stack(args, qg, synth, dev):
     act_bytes = model["layers"] * (M * 4 * ((H + NQ) + (QD + H + H) + (H + FF) + (FF + H + H))
                                    + 2 * H * 2)
     step_bytes = weight_bytes + act_bytes
-
-    if args.pmc_pass:
-        pmc_pass(qg, layers, model, dev)
-        return
+    # algorithmic bytes of each launch of a layer (weights + the vectors it reads and writes)
+    d0 = layers[0]
+    launch_bytes = {
+        "qkv": d0["qkv"].nbytes() + M * 4 * (H + NQ) + H * 2,
+        "o": d0["o"].nbytes() + M * 4 * (QD + H + H),
+        "gate.up": d0["gate"].nbytes() + d0["up"].nbytes() + M * 4 * (H + FF) + H * 2,
+        "down": d0["down"].nbytes() + M * 4 * (FF + H + H),
+    }
+    launch_outputs = {"qkv": M * NQ, "o": M * H, "gate.up": M * FF, "down": M * H}
 
     shp = (lambda n: (n,)) if M == 1 else (lambda n: (M, n))
     x0 = torch.from_numpy(synth.activations(args.seed, "x0", M * H, np.float32)
@@ -328,18 +478,32 @@ def run_stack(args, qg, synth, dev):
     u = torch.empty(shp(FF), dtype=torch.float32, device=dev)
     ws = qg.workspace(qg.QG_OP_SWIGLU, FF, FF, M, bits, fmt, 1, dev)
 
+    def layer_calls(d):
+        qg.qgemv_rmsnorm(d["qkv"], x, d["g_attn"], EPS, y=qkv, ws=ws)
+        if M == 1:
+            att = qkv[:QD]
+        else:  # stands in for the attention kernel writing its [M][q_dim] output
+            a.copy_(qkv[:, :QD])
+            att = a
+        qg.qgemv(d["o"], att, residual=x, y=h, ws=ws)
+        qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
+        qg.qgemv(d["down"], u, residual=h, y=x, ws=ws)
+
     def token():
         x.copy_(x0)
         for d in layers:
-            qg.qgemv_rmsnorm(d["qkv"], x, d["g_attn"], EPS, y=qkv, ws=ws)
-            if M == 1:
-                att = qkv[:QD]
-            else:  # stands in for the attention kernel writing its [M][q_dim] output
-                a.copy_(qkv[:, :QD])
-                att = a
-            qg.qgemv(d["o"], att, residual=x, y=h, ws=ws)
-            qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
-            qg.qgemv(d["down"], u, residual=h, y=x, ws=ws)
+            layer_calls(d)
+
+    if args.pmc_pass:
+        n = min(4, len(layers))
+
+        def once():
+            x.copy_(x0)
+            for d in layers[:n]:
+                layer_calls(d)
+        pmc_pass(args, qg, dev, once, ["qkv", "o", "gate.up", "down"] * n, launch_bytes,
+                 launch_outputs)
+        return
 
     step, graph = graph_step(token, not args.no_graph, x)
     if not bool(torch.isfinite(x).all()):
@@ -350,53 +514,48 @@ def run_stack(args, qg, synth, dev):
         f"{1e3 / ms:.0f} steps/s")
 
     # dominant kernel: gate.up SwiGLU, one launch per layer over distinct weights
-    sw_bytes = layers[0]["gate"].nbytes() + layers[0]["up"].nbytes() + M * (H * 4 + FF * 4) + H * 2
+    sw_bytes = launch_bytes["gate.up"]
 
     def swiglu_all():
         for d in layers:
             qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
 
     sw_us = time_launches(swiglu_all, len(layers), graph is not None)
-    traffic = None
-    if bits == 4 and fmt == 0 and M == 1 and os.path.exists(TRAFFIC_FILE):
-        try:
-            tr = json.load(open(TRAFFIC_FILE))
-            if tr.get("kernel_hash") == kernel_hash():
-                traffic = tr.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
     fmt_name = {0: f"{bits}-bit g64 planar", 1: "4-bit 16-entry table per row",
                 2: "dense fp16 weights"}[fmt]
     path = "matrix cores" if bits in (2, 4) else "one pass per vector"
     kname = ("qswiglu" if M == 1 else f"qswiglu M={M} ({path})") + \
         " 14336x4096 x2 (gate.up, rmsnorm)"
-    dom = roofline(kname, sw_bytes, sw_us, traffic)
-    copy_gbs = copy_peak(dev)
+    dom = roofline(kname, sw_bytes, sw_us, traffic_of(args, "gate.up"))
+    peaks = probe_peaks(qg, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        th = oracle_threads()
-        xh = synth.activations(args.seed, "x0", M * H, np.float32).reshape(M, H).astype(np.float64)
+        x_start = synth.activations(args.seed, "x0", M * H, np.float32).reshape(M, H).astype(np.float64)
+        layer_w = [sum(int(sum(v.nbytes for v in mm.values() if isinstance(v, np.ndarray)))
+                       for mm in w.values() if isinstance(mm, dict)) for w in host_layers]
 
-        def work(i):
-            nonlocal xh
-            if i >= len(host_layers):
-                return None
-            w = host_layers[i]
-            xh = np.stack([oracle.decoder_layer(w, xh[m], QD, EPS, nthreads=th) for m in range(M)])
-            return sum(int(sum(v.nbytes for k2, v in mm.items() if isinstance(v, np.ndarray)))
-                       for mm in w.values() if isinstance(mm, dict))
+        def make_work(th):
+            st = {"x": x_start.copy()}
 
-        done, nl, dt = cpu_sample(work, args.cpu_seconds)
-        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
-               "sample": f"{nl} of {len(host_layers)} decoder layers of one step ({M} vector(s); "
-                         f"{done / 1e9:.3f} GB of weights) in {dt:.1f} s, fp64 scalar C",
-               "steps_per_s": round(nl / len(host_layers) / dt, 6)}
+            def work(i):
+                if i >= len(host_layers):
+                    return None
+                st["x"] = np.stack([oracle.decoder_layer(host_layers[i], st["x"][m], QD, EPS,
+                                                         nthreads=th) for m in range(M)])
+                return layer_w[i]
+            return work
+
+        cpu = cpu_baseline(
+            make_work, args.cpu_seconds,
+            lambda n, done, dt: (f"{n} of {len(host_layers)} decoder layers of one step ({M} vector(s); "
+                                 f"{done / 1e9:.3f} GB of weights) in {dt:.1f} s, fp64 scalar C"),
+            lambda n, done, dt: {"steps_per_s": round(n / len(host_layers) / dt, 6)})
     workload = f"llama3-8b-shaped decode stack, {fmt_name}, M={M}"
     cfg = {"layers": model["layers"], "hidden": H, "qkv": NQ, "ffn": FF, "bits": bits, "fmt": fmt,
            "m": M, "graph": graph is not None}
-    emit(args, workload, cfg, step_bytes, ms, dom, copy_gbs, cpu)
+    emit(args, workload, cfg, step_bytes, ms, dom, peaks, cpu, arith_dtype(bits, fmt, M))
 
 
 def run_single(args, qg, synth, dev):
@@ -415,29 +574,37 @@ def run_single(args, qg, synth, dev):
         for m in mats:
             qg.qgemv(m, x, y=y)
 
+    if args.pmc_pass:
+        def once():
+            for m in mats[:16]:
+                qg.qgemv(m, x, y=y)
+        pmc_pass(args, qg, dev, once, ["qgemv 2048x2048"] * 16, {"qgemv 2048x2048": unit_bytes},
+                 {"qgemv 2048x2048": N})
+        return
     step, graph = graph_step(all_sets, not args.no_graph, y)
     ms = time_steps(step, args.steps, args.warmup)
     us = ms * 1e3 / sets
-    dom = roofline("qgemv 2048x2048 4-bit g64 (x fp16)", unit_bytes, us)
-    copy_gbs = copy_peak(dev)
+    dom = roofline("qgemv 2048x2048 4-bit g64 (x fp16)", unit_bytes, us,
+                   traffic_of(args, "qgemv 2048x2048"))
+    peaks = probe_peaks(qg, dev)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        th = oracle_threads()
         xh = synth.activations(args.seed, "cfg0x", K, np.float16)
 
-        def work(i):
-            oracle.gemv(host[i % sets], xh, nthreads=th)
-            return unit_bytes
+        def make_work(th):
+            def work(i):
+                oracle.gemv(host[i % sets], xh, nthreads=th)
+                return unit_bytes
+            return work
 
-        done, n, dt = cpu_sample(work, args.cpu_seconds)
-        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
-               "sample": f"{n} matvecs 2048x2048 in {dt:.1f} s, fp64 scalar C",
-               "us_per_matvec": round(dt / n * 1e6, 1)}
+        cpu = cpu_baseline(make_work, args.cpu_seconds,
+                           lambda n, done, dt: f"{n} matvecs 2048x2048 in {dt:.1f} s, fp64 scalar C",
+                           lambda n, done, dt: {"us_per_matvec": round(dt / n * 1e6, 1)})
     cfg = {"n": N, "k": K, "weight_sets": sets, "us_per_matvec": round(us, 3),
            "graph": graph is not None}
     emit(args, "single 4-bit g64 matvec 2048x2048, M=1, back-to-back over 256 weight sets",
-         cfg, unit_bytes * sets, ms, dom, copy_gbs, cpu, dtype="f32")
+         cfg, unit_bytes * sets, ms, dom, peaks, cpu, arith_dtype(4, 0, 1))
 
 
 def run_moe(args, qg, synth, dev):
@@ -492,38 +659,55 @@ def run_moe(args, qg, synth, dev):
             else:
                 qg.qmoe_experts_batch(Gd, Ud, Dd, E, Sd, lgd[l], K, x, gd, EPS, y=x, ws=ws)
 
+    if args.pmc_pass:
+        gu_bytes = (K + 1) * (synth.qmat_bytes(F, H) * 2) + M * (E * 4 + H * 4 + (K + 1) * F * 4) + H * 2
+        dn_bytes = (K + 1) * synth.qmat_bytes(H, F) + M * ((K + 1) * F * 4 + H * 8)
+
+        def once():
+            x.copy_(x0)
+            for l in range(4):
+                if M == 1:
+                    qg.qmoe_experts(Gd, Ud, Dd, E, Sd, lgd[l], K, x, gd, EPS, y=x, ws=ws)
+                else:
+                    qg.qmoe_experts_batch(Gd, Ud, Dd, E, Sd, lgd[l], K, x, gd, EPS, y=x, ws=ws)
+        labels = ["route + gate.up", "down + combine"]
+        pmc_pass(args, qg, dev, once, labels * 4,
+                 {labels[0]: gu_bytes, labels[1]: dn_bytes},
+                 {labels[0]: M * (K + 1) * F, labels[1]: M * H})
+        return
     step, graph = graph_step(token, not args.no_graph, x)
     ms = time_steps(step, args.steps, args.warmup)
     us_layer = ms * 1e3 / L
     kname = ("qmoe_experts (route, gate.up of 4 experts, down + combine)" if M == 1 else
              f"qmoe_experts_batch M={M} (route, gate.up of 4 experts per token, down + combine)")
     dom = roofline(kname, sum(layer_bytes) / L, us_layer)
-    copy_gbs = copy_peak(dev)
+    peaks = probe_peaks(qg, dev)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        th = oracle_threads()
-        xh = np.atleast_2d(x0h.astype(np.float64))
 
-        def work(i):
-            nonlocal xh
-            if i >= L:
-                return None
-            lg = np.atleast_2d(logits[i])
-            xh = np.stack([oracle.moe_layer(gate, up, down, shared, lg[m], K, xh[m], g, EPS,
-                                            nthreads=th)[0] for m in range(M)])
-            return layer_bytes[i]
+        def make_work(th):
+            st = {"x": np.atleast_2d(x0h.astype(np.float64))}
 
-        done, n, dt = cpu_sample(work, args.cpu_seconds)
-        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
-               "sample": f"{n} of {L} chained expert layers of {M} token(s) in {dt:.1f} s, "
-                         f"fp64 scalar C", "tok_per_s": round(M * n / L / dt, 6)}
+            def work(i):
+                if i >= L:
+                    return None
+                lg = np.atleast_2d(logits[i])
+                st["x"] = np.stack([oracle.moe_layer(gate, up, down, shared, lg[m], K, st["x"][m], g,
+                                                     EPS, nthreads=th)[0] for m in range(M)])
+                return layer_bytes[i]
+            return work
+
+        cpu = cpu_baseline(make_work, args.cpu_seconds,
+                           lambda n, done, dt: (f"{n} of {L} chained expert layers of {M} token(s) in "
+                                                f"{dt:.1f} s, fp64 scalar C"),
+                           lambda n, done, dt: {"tok_per_s": round(M * n / L / dt, 6)})
     cfg = {"experts": E, "hidden": H, "ffn": F, "top_k": K, "shared": 1, "layers_per_token": L,
            "tokens": M, "us_per_layer": round(us_layer, 3), "graph": graph is not None}
     name = "moe expert layer, 512 experts 4-bit g64, top-3 + shared, 60 chained draws per token"
     if M > 1:
         name += f", {M} tokens per batched call"
-    emit(args, name, cfg, sum(layer_bytes), ms, dom, copy_gbs, cpu)
+    emit(args, name, cfg, sum(layer_bytes), ms, dom, peaks, cpu, arith_dtype(4, 0, 1))
 
 
 def run_qwen(args, qg, synth, dev):
@@ -574,6 +758,17 @@ def run_qwen(args, qg, synth, dev):
             qg.qlogits_topk(head, x, topk, gf, EPS, logits=z, idx=idx, vals=vals, ws=ws)
         return token
 
+    if args.pmc_pass:
+        layer_b = {n: devs[0][0][0][k].nbytes() for n, k in (("qkv", "qkv"), ("o", "o"), ("down", "down"))}
+        lb = {"qkv": layer_b["qkv"] + 4 * (H + NQ) + H * 2, "o": layer_b["o"] + 4 * (QD + 2 * H),
+              "gate.up": devs[0][0][0]["gate"].nbytes() * 2 + 4 * (H + FF) + H * 2,
+              "down": layer_b["down"] + 4 * (FF + 2 * H),
+              "logits (rmsnorm + matvec)": head_bytes + H * 4 + H * 2 + V * 4,
+              "top-40": V * 4 + topk * 8}
+        outs = {"qkv": NQ, "o": H, "gate.up": FF, "down": H, "logits (rmsnorm + matvec)": V, "top-40": topk}
+        labels = ["qkv", "o", "gate.up", "down"] * model["layers"] + ["logits (rmsnorm + matvec)", "top-40"]
+        pmc_pass(args, qg, dev, token_of(0), labels, lb, outs)
+        return
     steps_c, graph = [], None
     for c in range(copies):
         st, graph = graph_step(token_of(c), not args.no_graph, idx)
@@ -594,34 +789,34 @@ def run_qwen(args, qg, synth, dev):
     head_us = time_launches(heads, copies, graph is not None)
     dom = roofline("qlogits_topk 151936x1024 4-bit + final norm + top-40", head_bytes + H * 4 + V * 8,
                    head_us)
-    copy_gbs = copy_peak(dev)
+    peaks = probe_peaks(qg, dev)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        th = oracle_threads()
         hl, head, gf = hosts[0]
-        xh = synth.activations(args.seed, "qwen_x0", H, np.float32).astype(np.float64)
         per_layer = stack_bytes // model["layers"]
 
-        def work(i):
-            nonlocal xh
-            if i < len(hl):
-                xh = oracle.decoder_layer(hl[i], xh, QD, EPS, nthreads=th)
-                return per_layer
-            if i == len(hl):
-                oracle.logits_topk(head, xh, topk, gf, EPS, nthreads=th)
-                return head_bytes
-            return None
+        def make_work(th):
+            st = {"x": synth.activations(args.seed, "qwen_x0", H, np.float32).astype(np.float64)}
 
-        done, n, dt = cpu_sample(work, args.cpu_seconds)
-        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
-               "sample": f"{min(n, len(hl))} of {len(hl)} decoder layers"
-                         f"{' + logits/top-40' if n > len(hl) else ''} of one token in {dt:.1f} s, "
-                         f"fp64 scalar C"}
+            def work(i):
+                if i < len(hl):
+                    st["x"] = oracle.decoder_layer(hl[i], st["x"], QD, EPS, nthreads=th)
+                    return per_layer
+                if i == len(hl):
+                    oracle.logits_topk(head, st["x"], topk, gf, EPS, nthreads=th)
+                    return head_bytes
+                return None
+            return work
+
+        cpu = cpu_baseline(make_work, args.cpu_seconds,
+                           lambda n, done, dt: (f"{min(n, len(hl))} of {len(hl)} decoder layers"
+                                                f"{' + logits/top-40' if n > len(hl) else ''} of one "
+                                                f"token in {dt:.1f} s, fp64 scalar C"))
     cfg = {"layers": model["layers"], "hidden": H, "vocab": V, "top_k": topk, "copies": copies,
            "graph": graph is not None}
     emit(args, "qwen3-0.6b-shaped decode stack + logits + top-40, 4-bit g64, M=1", cfg,
-         step_bytes, ms, dom, copy_gbs, cpu)
+         step_bytes, ms, dom, peaks, cpu, arith_dtype(4, 0, 1))
 
 
 def run_attn(args, qg, synth, dev):
@@ -653,7 +848,7 @@ def run_attn(args, qg, synth, dev):
     ms = time_steps(run, args.steps, args.warmup)
     us = time_launches(step, L, not args.no_graph)
     dom = roofline(f"qattn_decode H32/Hkv8/d128, {pos + 1} positions", layer_bytes, us)
-    copy_gbs = copy_peak(dev)
+    peaks = probe_peaks(qg, dev)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -661,18 +856,22 @@ def run_attn(args, qg, synth, dev):
         hv = [vc[l].cpu().numpy() for l in range(2)]
         hq = q[:2].double().cpu().numpy()
 
-        def work(i):
-            oracle.attention(hq[i % 2], hk[i % 2], hv[i % 2], pos + 1, scale)
-            return layer_bytes
+        def make_work(th):  # the attention oracle runs on one thread
+            def work(i):
+                if th > 1:
+                    return None
+                oracle.attention(hq[i % 2], hk[i % 2], hv[i % 2], pos + 1, scale)
+                return layer_bytes
+            return work
 
-        done, n, dt = cpu_sample(work, args.cpu_seconds)
+        done, n, dt = cpu_sample(make_work(1), args.cpu_seconds)
         cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"{n} layers of attention over {pos + 1} positions in {dt:.1f} s, "
-                         "fp64 scalar C, one thread"}
+                         "fp64 scalar C, one thread", "nproc": os.cpu_count(), "cpu_model": cpu_model()}
     cfg = {"layers": L, "heads": H, "kv_heads": Hkv, "head_dim": d, "context": pos + 1,
            "graph": graph is not None}
     emit(args, f"llama3-8b-shaped decode attention, {L} layers, fp16 KV cache, context {pos + 1}",
-         cfg, layer_bytes * L, ms, dom, copy_gbs, cpu, dtype="f32")
+         cfg, layer_bytes * L, ms, dom, peaks, cpu, "f16 cache x f32 query, f32 accumulate")
 
 
 def main():
@@ -695,10 +894,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="run only 8 gate.up SwiGLU launches and 2 reference reads of 64 MiB "
-                         "(for rocprofv3 --pmc counter passes)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn the counter CSVs of two --pmc-pass runs into the traffic file")
+                    help="two reference reads of 64 MiB, then the workload's launches once, eagerly "
+                         "(for rocprofv3 --pmc counter passes; writes gpurun_out/pmc_labels.json)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LABELS_JSON"),
+                    help="turn the counter CSVs of two --pmc-pass runs into profiles/traffic_*.{json,md}")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="per-matvec kernel durations of the decode tokens in a rocprofv3 trace")
     args = ap.parse_args()
