@@ -32,7 +32,7 @@ QG_MAX_TOPK = 1024
 
 EXPORTED = ("qg_status_str", "qg_workspace_bytes", "qg_workspace_init", "qg_tune", "qgemv",
             "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qmoe_experts_batch", "qlogits_topk",
-            "qlogits_sample",
+            "qlogits_topk_noalloc", "qlogits_sample",
             "qg_sample_topk", "qattn_decode", "qg_probe_read",
             "qg_probe_copy")
 
@@ -72,6 +72,7 @@ def lib():
         L.qmoe_experts_batch.argtypes = [Q, Q, Q, I, I, I, I, I, I, I, Q, P, I, P, F, P, P, P, P, P,
                                          S, P]
         L.qlogits_topk.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P, S, P]
+        L.qlogits_topk_noalloc.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P]
         U64 = ctypes.c_uint64
         L.qlogits_sample.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, F, F, U64, P, P,
                                      P, S, P]
@@ -301,6 +302,24 @@ def qlogits_topk(W: QMat, x, k: int, norm_w=None, eps: float = 1e-5, logits=None
     _check(lib().qlogits_topk(ctypes.byref(W.c), W.N, W.K, W.group, W.bits, W.fmt, _ptr(x),
                               _xdtype(x), _ptr(norm_w), float(eps), _ptr(logits), k, _ptr(idx),
                               _ptr(vals), wp, wn, _stream(stream)), "qlogits_topk")
+    return logits, idx, vals
+
+
+def qlogits_topk_noalloc(W: QMat, x, k: int, norm_w=None, eps: float = 1e-5, logits=None,
+                         idx=None, vals=None, stream=None):
+    """qlogits_topk on the library's own scratch memory (no workspace)."""
+    import torch
+    dev = x.device
+    if logits is None:
+        logits = torch.empty(W.N, dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(k, dtype=torch.int32, device=dev)
+    if vals is None:
+        vals = torch.empty(k, dtype=torch.float32, device=dev)
+    _check(lib().qlogits_topk_noalloc(ctypes.byref(W.c), W.N, W.K, W.group, W.bits, W.fmt, _ptr(x),
+                                      _xdtype(x), _ptr(norm_w), float(eps), _ptr(logits), k,
+                                      _ptr(idx), _ptr(vals), _stream(stream)),
+           "qlogits_topk_noalloc")
     return logits, idx, vals
 
 

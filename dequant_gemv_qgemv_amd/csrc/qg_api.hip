@@ -209,6 +209,15 @@ size_t mv_ws_bytes(int N, int M, int epi) {
   return tickets_al + (size_t)kMaxSplits * (epi == kEpiSwiglu ? 2 : 1) * M * N * 4;
 }
 
+// Work to enqueue right before a call's first kernel, once every check has
+// passed (so that a refused call still enqueues nothing).
+struct PreLaunch {
+  int (*fn)(void* arg, hipStream_t stream);
+  void* arg;
+};
+
+int run_pre(const PreLaunch* pre, hipStream_t stream) { return pre ? pre->fn(pre->arg, stream) : QG_OK; }
+
 // Extra requirements of the M = 2..8 kernels: each wave loads whole
 // 512-code ranges of a row's scales/biases (or its table) with 16-byte loads.
 int check_mm(const qg_qmat* A, const qg_qmat* B, int K, int fmt) {
@@ -228,10 +237,11 @@ int check_mm(const qg_qmat* A, const qg_qmat* B, int K, int fmt) {
 // workspace for the fp32 partials.
 int run_mm(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int bits, int fmt, int epi,
            const void* x, int x_dtype, const uint16_t* norm_w, float eps, const float* residual,
-           float* y, void* ws, bool have_ws, int cus, hipStream_t stream) {
+           float* y, void* ws, bool have_ws, int cus, hipStream_t stream, const PreLaunch* pre) {
   const int slice = mm_slice_codes();
   const int splits = (K + slice - 1) / slice;
   if (splits > 1 && !have_ws) return QG_EWORKSPACE;
+  if (int rc = run_pre(pre, stream)) return rc;
   const int nbands = (N + 15) / 16;
   // one 8-wave workgroup per compute unit: the waves hold their activations
   // and two to four bands of codes in registers
@@ -275,7 +285,8 @@ int run_mm(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int bits, in
 
 int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, int bits, int fmt,
            int epi, const void* x, int x_dtype, const uint16_t* norm_w, float eps,
-           const float* residual, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+           const float* residual, float* y, void* ws, size_t ws_bytes, hipStream_t stream,
+           const PreLaunch* pre = nullptr) {
   int rc = check_common(N, K, M, group, bits, fmt, x_dtype);
   if (rc) return rc;
   if ((rc = check_qmat(A, fmt))) return rc;
@@ -297,7 +308,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   const bool have_ws = ws && ws_bytes >= mv_ws_bytes(N, M, epi) && aligned(ws, 256);
   if (on_mfma)
     return run_mm(A, B, N, K, M, bits, fmt, epi, x, x_dtype, norm_w, eps, residual, y, ws,
-                  have_ws, dev.cus, stream);
+                  have_ws, dev.cus, stream, pre);
   // Several vectors keep each vector's K in one slice (per-vector split-K
   // partials are not provided): planned as if a workspace were there, so a
   // K that needs slices is refused whatever workspace came with the call.
@@ -333,6 +344,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
     p.tickets = static_cast<uint32_t*>(ws);
     p.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + tickets_al);
   }
+  if ((rc = run_pre(pre, stream))) return rc;
   const hipError_t e = launch_mv(bits, fmt, epi, pl, p, stream);
   return e == hipSuccess ? QG_OK : QG_ELAUNCH;
 }
@@ -378,6 +390,72 @@ int device_ok() { return device_info().ok; }
 }  // namespace qg
 
 namespace {
+// Argument checks shared by the logits entry points (those that run_mv does
+// not make itself).
+int check_logits(int V, int K, int group, int bits, int fmt, int x_dtype, const uint16_t* norm_w,
+                 float eps, const float* logits, int k, const int32_t* idx, const float* vals) {
+  int rc = check_common(V, K, 1, group, bits, fmt, x_dtype);
+  if (rc) return rc;
+  if (V < 1) return QG_EINVAL;
+  if (k < 1 || k > V) return QG_EINVAL;
+  if (k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
+  if (!logits || !idx || !vals || !aligned(logits, 4) || !aligned(idx, 4) || !aligned(vals, 4))
+    return QG_EINVAL;
+  if (norm_w && !(eps >= 0.f)) return QG_EINVAL;
+  return QG_OK;
+}
+
+// ---- library-held scratch for qlogits_topk_noalloc -------------------------
+// One array per GPU, held until the process ends; its device address comes
+// from hipGetSymbolAddress once per device (the array's name in host code is
+// not a device address). Every call on a GPU shares it, so calls that overlap
+// on one GPU race.
+constexpr size_t kStaticScratchBytes = (size_t)24 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct StaticScratch {
+  void* ptr;     // device address of this device's copy of `scratch`
+  bool cleared;  // its integer tickets are known to be zero
+};
+std::mutex g_static_mu;
+StaticScratch g_static[kMaxDevices];
+
+// This device's scratch address (taken once, with the device current).
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QG_EDEVICE;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  StaticScratch& s = g_static[dev];
+  if (!s.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QG_ELAUNCH;
+    s.ptr = p;
+  }
+  *out = s.ptr;
+  return QG_OK;
+}
+
+// Pre-launch step of the first call on a device: clears the whole array with
+// the fill kernel on the call's stream (ahead of the call's kernels; no
+// memset node, so it may be captured). A clear recorded into a graph under
+// capture does not count: the next uncaptured call clears again. Every call
+// leaves the tickets at zero, so later calls need no clear.
+int clear_static_once(void* arg, hipStream_t stream) {
+  (void)arg;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QG_EDEVICE;
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  StaticScratch& s = g_static[dev];
+  if (s.cleared) return QG_OK;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return QG_ELAUNCH;
+  if (launch_fill_u32(static_cast<uint32_t*>(s.ptr), kStaticScratchBytes / 4, 0u, stream) != hipSuccess)
+    return QG_ELAUNCH;
+  if (st == hipStreamCaptureStatusNone) s.cleared = true;
+  return QG_OK;
+}
+
 // Validates the draw arguments and fills dp. QG_OK or QG_EINVAL.
 int make_draw(float temperature, float top_p, uint64_t seed, uint64_t* counter, int32_t* token,
               DrawParams* dp) {
@@ -510,20 +588,32 @@ int qmoe_experts_batch(const qg_qmat* gate_all, const qg_qmat* up_all, const qg_
 int qlogits_topk(const qg_qmat* W, int V, int K, int group, int bits, int fmt, const void* x,
                  int x_dtype, const uint16_t* norm_w, float eps, float* logits, int k,
                  int32_t* idx, float* vals, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int rc = check_common(V, K, 1, group, bits, fmt, x_dtype);
+  int rc = check_logits(V, K, group, bits, fmt, x_dtype, norm_w, eps, logits, k, idx, vals);
   if (rc) return rc;
-  if (V < 1) return QG_EINVAL;
-  if (k < 1 || k > V) return QG_EINVAL;
-  if (k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
-  if (!logits || !idx || !vals || !aligned(logits, 4) || !aligned(idx, 4) || !aligned(vals, 4))
-    return QG_EINVAL;
-  if (norm_w && !(eps >= 0.f)) return QG_EINVAL;
   const size_t tk = topk_workspace_bytes(V, k);
   const size_t need = tk + mv_ws_bytes(V, 1, kEpiStore);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return QG_EWORKSPACE;
   char* mvws = static_cast<char*>(ws) + tk;
   rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps, nullptr,
               logits, mvws, ws_bytes - tk, stream);
+  if (rc) return rc;
+  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, DrawParams{}, stream);
+}
+
+int qlogits_topk_noalloc(const qg_qmat* W, int V, int K, int group, int bits, int fmt,
+                         const void* x, int x_dtype, const uint16_t* norm_w, float eps,
+                         float* logits, int k, int32_t* idx, float* vals, hipStream_t stream) {
+  int rc = check_logits(V, K, group, bits, fmt, x_dtype, norm_w, eps, logits, k, idx, vals);
+  if (rc) return rc;
+  const size_t tk = topk_workspace_bytes(V, k);
+  const size_t need = tk + mv_ws_bytes(V, 1, kEpiStore);
+  if (need > kStaticScratchBytes) return QG_EUNSUPPORTED;
+  if (!device_info().ok) return QG_EDEVICE;
+  void* ws = nullptr;
+  if ((rc = static_scratch(&ws))) return rc;
+  const PreLaunch pre{clear_static_once, nullptr};
+  rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps, nullptr,
+              logits, static_cast<char*>(ws) + tk, need - tk, stream, &pre);
   if (rc) return rc;
   return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, DrawParams{}, stream);
 }
@@ -536,14 +626,8 @@ int qlogits_sample(const qg_qmat* W, int V, int K, int group, int bits, int fmt,
   DrawParams dp;
   int rc = make_draw(temperature, top_p, seed, counter, token, &dp);
   if (rc) return rc;
-  rc = check_common(V, K, 1, group, bits, fmt, x_dtype);
+  rc = check_logits(V, K, group, bits, fmt, x_dtype, norm_w, eps, logits, k, idx, vals);
   if (rc) return rc;
-  if (V < 1) return QG_EINVAL;
-  if (k < 1 || k > V) return QG_EINVAL;
-  if (k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
-  if (!logits || !idx || !vals || !aligned(logits, 4) || !aligned(idx, 4) || !aligned(vals, 4))
-    return QG_EINVAL;
-  if (norm_w && !(eps >= 0.f)) return QG_EINVAL;
   const size_t tk = topk_workspace_bytes(V, k);
   const size_t need = tk + mv_ws_bytes(V, 1, kEpiStore);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return QG_EWORKSPACE;

@@ -235,6 +235,23 @@ int qlogits_topk(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
                  float *logits, int k, int32_t *idx, float *vals,
                  void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* qlogits_topk_noalloc -- qlogits_topk without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments (minus
+ * ws / ws_bytes), results, kernels and errors as qlogits_topk. Its scratch
+ * memory (top-k candidates, split-K partials and tickets) is a
+ * library-held device array of 24 MiB per GPU, kept until the process ends;
+ * a call whose workspace need (qg_workspace_bytes(QG_OP_LOGITS_TOPK, V, K, 1,
+ * bits, fmt, k)) exceeds it returns QG_EUNSUPPORTED (this is about V <= 390000
+ * for k = 40). The call itself allocates and frees nothing; its first call on
+ * a device clears the array with a fill kernel on `stream`, ahead of its own
+ * kernels. Every call on one GPU shares that GPU's array and leaves it ready
+ * for the next call, so calls that may overlap on one GPU (different streams
+ * without ordering between them) race and must not be made. */
+int qlogits_topk_noalloc(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
+                         const void *x, int x_dtype, const uint16_t *norm_w, float eps,
+                         float *logits, int k, int32_t *idx, float *vals, hipStream_t stream);
+
 /* Sampling after top-k ([F] section 1: logits matvec + top-k sampling on the
  * GPU, only the token comes back). The page names the step, not its rule;
  * the rule implemented:

@@ -215,3 +215,23 @@ def test_tune_rejects_bad_values(L):
 def test_empty_rows_is_a_no_op(L):
     # N = 0 is valid and enqueues nothing (it returns before any HIP call)
     assert call_gemv(L, N=0) == qg.QG_OK
+
+
+def test_noalloc_logits_checks_before_any_launch(L):
+    """qlogits_topk_noalloc validates its arguments and the size of its
+    library-held scratch on the host: these refusals never touch a device."""
+    W = _mat()
+    LG, IDX, VALS = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+
+    def call(V=1000, K=128, k=40, logits=LG, idx=IDX, vals=VALS, x=X):
+        return L.qlogits_topk_noalloc(ctypes.byref(W), V, K, 64, 4, 0, x, 1, None, 0.0, logits, k,
+                                      idx, vals, None)
+
+    assert call(logits=None) == qg.QG_EINVAL
+    assert call(idx=None) == qg.QG_EINVAL
+    assert call(k=0) == qg.QG_EINVAL
+    assert call(k=1001) == qg.QG_EINVAL
+    assert call(k=2000, V=5000) == qg.QG_EUNSUPPORTED  # k beyond QG_MAX_TOPK
+    assert call(K=100) == qg.QG_EINVAL  # K not a multiple of the group
+    # a vocabulary whose workspace need exceeds the 24 MiB scratch array
+    assert call(V=600000, K=64) == qg.QG_EUNSUPPORTED
