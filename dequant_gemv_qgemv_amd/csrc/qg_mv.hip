@@ -819,17 +819,40 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
     // a whole chunk of x per thread instead (64 values for 2-bit codes) set
     // the register allocation of every 2-bit kernel to 190-203 VGPRs, one
     // workgroup per CU.
+    // The first kPre rounds' x is requested before the weights: a request
+    // made after them waits until the memory system has served them (the
+    // 4096 x 14336 down projection staged its fourth round ~1.5 us late).
     const int rounds = (nunits + kThreads - 1) / kThreads;
-    load_quarters_at(threadIdx.x);
+    constexpr int kPre = CPC >= 64 ? 2 : 4;
+    constexpr int QXN = CPC / 16, QGN = (CPC / 4 + 7) / 8;
+    u32x4 pqx[kPre][QXN], pqg[kPre][QGN];
+    float pqw[kPre];
+#pragma unroll
+    for (int r = 0; r < kPre; ++r) {
+      if (r < rounds) {
+        load_quarters_at(r * kThreads + (int)threadIdx.x);
+#pragma unroll
+        for (int i = 0; i < QXN; ++i) pqx[r][i] = qx[i];
+#pragma unroll
+        for (int i = 0; i < QGN; ++i) pqg[r][i] = qg[i];
+        pqw[r] = qw;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < DEPTH; ++k) issue(d[k]);
 #pragma unroll
-    for (int i = 0; i < CPC / 16; ++i) hold(qx[i]);
+    for (int r = 0; r < kPre; ++r) {
+      if (r < rounds) {
 #pragma unroll
-    for (int i = 0; i < (CPC / 4 + 7) / 8; ++i) hold(qg[i]);
-    hold(qw);
-    ss = stage_quarter<BITS, FMT, LPR>(p, qx, qg, qw, threadIdx.x, nunits, c0, nch, xl, info);
-    for (int r = 1; r < rounds; ++r) {
+        for (int i = 0; i < QXN; ++i) hold(pqx[r][i]);
+#pragma unroll
+        for (int i = 0; i < QGN; ++i) hold(pqg[r][i]);
+        hold(pqw[r]);
+        ss += stage_quarter<BITS, FMT, LPR>(p, pqx[r], pqg[r], pqw[r], r * kThreads + (int)threadIdx.x, nunits,
+                                            c0, nch, xl, info);
+      }
+    }
+    for (int r = kPre; r < rounds; ++r) {
       const int u = r * kThreads + (int)threadIdx.x;
       load_quarters_at(u);
       ss += stage_quarter<BITS, FMT, LPR>(p, qx, qg, qw, u, nunits, c0, nch, xl, info);
@@ -965,7 +988,8 @@ typedef void (*KernelFn)(const MvParams);
 
 template <int BITS, int FMT, int EPI, int SEG, int LPR>
 KernelFn pick_rd(int rows, int depth) {
-  if (rows == 2) return qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 2>;  // two rows: depth 2 only
+  if (rows == 2) return depth == 4 ? qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 4> : qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 2>;
+  if (depth == 8) return qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 8>;
   return depth == 4 ? qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 4> : qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 2>;
 }
 
