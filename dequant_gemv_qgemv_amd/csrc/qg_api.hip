@@ -524,7 +524,7 @@ int qg_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
 // restores automatic.
 int qg_tune(int knob, int value) {
   if (knob < 0 || knob > 4 || value < 0) return QG_EINVAL;
-  if (knob == 4 && value != 0 && value != 2 && value != 4 && value != 8) return QG_EINVAL;
+  if (knob == 4 && value != 0 && value != 2 && value != 4) return QG_EINVAL;
   if (knob == 1 && value != 0 && value != 1 && value != 2) return QG_EINVAL;
   if (knob == 2 && value != 0 && value != 16 && value != 32 && value != 64) return QG_EINVAL;
   if (knob == 0 && value > kMaxSplits) return QG_EINVAL;

@@ -988,8 +988,7 @@ typedef void (*KernelFn)(const MvParams);
 
 template <int BITS, int FMT, int EPI, int SEG, int LPR>
 KernelFn pick_rd(int rows, int depth) {
-  if (rows == 2) return depth == 4 ? qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 4> : qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 2>;
-  if (depth == 8) return qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 8>;
+  if (rows == 2) return qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 2>;  // two rows: depth 2 only
   return depth == 4 ? qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 4> : qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 2>;
 }
 
