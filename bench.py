@@ -758,15 +758,25 @@ def run_qwen(args, qg, synth, dev):
             qg.qlogits_topk(head, x, topk, gf, EPS, logits=z, idx=idx, vals=vals, ws=ws)
         return token
 
+    # the head is one launch (the matvec's workgroups merge their top-k keys)
+    # or the matvec and then the top-k kernel
+    head_launches = qg.qg_logits_topk_launches(V, H, topk)
     if args.pmc_pass:
         layer_b = {n: devs[0][0][0][k].nbytes() for n, k in (("qkv", "qkv"), ("o", "o"), ("down", "down"))}
         lb = {"qkv": layer_b["qkv"] + 4 * (H + NQ) + H * 2, "o": layer_b["o"] + 4 * (QD + 2 * H),
               "gate.up": devs[0][0][0]["gate"].nbytes() * 2 + 4 * (H + FF) + H * 2,
-              "down": layer_b["down"] + 4 * (FF + 2 * H),
-              "logits (rmsnorm + matvec)": head_bytes + H * 4 + H * 2 + V * 4,
-              "top-40": V * 4 + topk * 8}
-        outs = {"qkv": NQ, "o": H, "gate.up": FF, "down": H, "logits (rmsnorm + matvec)": V, "top-40": topk}
-        labels = ["qkv", "o", "gate.up", "down"] * model["layers"] + ["logits (rmsnorm + matvec)", "top-40"]
+              "down": layer_b["down"] + 4 * (FF + 2 * H)}
+        outs = {"qkv": NQ, "o": H, "gate.up": FF, "down": H}
+        labels = ["qkv", "o", "gate.up", "down"] * model["layers"]
+        if head_launches == 1:
+            lb["logits + top-40 (one launch)"] = head_bytes + H * 4 + H * 2 + V * 4 + topk * 8
+            outs["logits + top-40 (one launch)"] = V + topk
+            labels.append("logits + top-40 (one launch)")
+        else:
+            lb["logits (rmsnorm + matvec)"] = head_bytes + H * 4 + H * 2 + V * 4
+            lb["top-40"] = V * 4 + topk * 8
+            outs["logits (rmsnorm + matvec)"], outs["top-40"] = V, topk
+            labels += ["logits (rmsnorm + matvec)", "top-40"]
         pmc_pass(args, qg, dev, token_of(0), labels, lb, outs)
         return
     steps_c, graph = [], None
@@ -787,8 +797,11 @@ def run_qwen(args, qg, synth, dev):
                             ws=ws)
 
     head_us = time_launches(heads, copies, graph is not None)
-    dom = roofline("qlogits_topk 151936x1024 4-bit + final norm + top-40", head_bytes + H * 4 + V * 8,
-                   head_us)
+    # algorithmic bytes: weights, x, norm weight and logits once, top-k out
+    # (the two-launch form reads the logits back)
+    head_alg = head_bytes + H * 4 + H * 2 + V * 4 + topk * 8 + (V * 4 if head_launches == 2 else 0)
+    dom = roofline(f"qlogits_topk 151936x1024 4-bit + final norm + top-40 ({head_launches} launch"
+                   f"{'es' if head_launches > 1 else ''})", head_alg, head_us)
     peaks = probe_peaks(qg, dev)
     cpu = None
     if not args.no_cpu_baseline:
@@ -814,7 +827,7 @@ def run_qwen(args, qg, synth, dev):
                                                 f"{' + logits/top-40' if n > len(hl) else ''} of one "
                                                 f"token in {dt:.1f} s, fp64 scalar C"))
     cfg = {"layers": model["layers"], "hidden": H, "vocab": V, "top_k": topk, "copies": copies,
-           "graph": graph is not None}
+           "graph": graph is not None, "head_launches": head_launches}
     emit(args, "qwen3-0.6b-shaped decode stack + logits + top-40, 4-bit g64, M=1", cfg,
          step_bytes, ms, dom, peaks, cpu, arith_dtype(4, 0, 1))
 

@@ -32,7 +32,7 @@ QG_MAX_TOPK = 1024
 
 EXPORTED = ("qg_status_str", "qg_workspace_bytes", "qg_workspace_init", "qg_tune", "qgemv",
             "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qmoe_experts_batch", "qlogits_topk",
-            "qlogits_topk_noalloc", "qlogits_sample",
+            "qlogits_topk_noalloc", "qg_logits_topk_launches", "qlogits_sample",
             "qg_sample_topk", "qattn_decode", "qg_probe_read",
             "qg_probe_copy")
 
@@ -73,6 +73,7 @@ def lib():
                                          S, P]
         L.qlogits_topk.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P, S, P]
         L.qlogits_topk_noalloc.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P]
+        L.qg_logits_topk_launches.argtypes = [I, I, I, I, I, I, ctypes.POINTER(I)]
         U64 = ctypes.c_uint64
         L.qlogits_sample.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, F, F, U64, P, P,
                                      P, S, P]
@@ -178,6 +179,15 @@ def workspace(op: int, N: int, K: int, M: int = 1, bits: int = 4, fmt: int = QG_
 
 def qg_tune(knob: int, value: int):
     _check(lib().qg_tune(knob, value), "qg_tune")
+
+
+def qg_logits_topk_launches(V: int, K: int, k: int, bits: int = 4, fmt: int = QG_AFFINE,
+                            group: int = 64) -> int:
+    """Kernels (1 or 2) that qlogits_topk enqueues for this head on the current device."""
+    out = ctypes.c_int(0)
+    _check(lib().qg_logits_topk_launches(V, K, group, bits, fmt, k, ctypes.byref(out)),
+           "qg_logits_topk_launches")
+    return out.value
 
 
 def qg_probe_read(src, out, blocks: int, cached: bool = False, stream=None):

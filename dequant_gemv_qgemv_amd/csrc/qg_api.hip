@@ -163,6 +163,7 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
   pl.rows = g_knob[1].load()
                 ? g_knob[1].load()
                 : (s.bits == 4 && s.fmt == QG_AFFINE && s.seg == kSegNone && s.K >= 8192 ? 2 : 1);
+  if (s.epi == kEpiTopk) pl.rows = 1;  // the fused top-k keeps one row per lane slot
   pl.depth = g_knob[4].load() ? g_knob[4].load() : 2;
   // Resident workgroups per CU: two 8-wave groups keep 16 waves in flight
   // where the kernel's registers allow it. 2-bit codes take one: measured on
@@ -283,10 +284,34 @@ int run_mm(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int bits, in
   return e == hipSuccess ? QG_OK : QG_ELAUNCH;
 }
 
+// Outputs and workspace regions of a matvec launch that also takes the top-k
+// of its rows (kEpiTopk).
+struct TopkOut {
+  int k;
+  int32_t* idx;
+  float* vals;
+  uint32_t* tickets;  // [kTkMaxGroups + 1], zero at rest
+  uint64_t* cand;     // [grid_x + groups][kTkList]
+};
+// run_mv with kEpiTopk: the plan does not allow the one-launch top-k (nothing
+// was enqueued; the caller takes the two-launch path).
+constexpr int kNotFused = 1;
+
+// The one-launch top-k takes a plan where each wave's rows fit its key list,
+// the groups of workgroups fit the last merge, and K is one slice.
+bool topk_fits(const MvPlan& pl, int N, int k) {
+  const int rpb = 64 / pl.lpr;
+  const int nbands = (N + rpb - 1) / rpb;
+  const int waves = pl.grid_x * kWaves;
+  const int per_wave = (nbands + waves - 1) / waves;
+  return k <= kTkList && pl.splits == 1 && pl.rows == 1 && pl.grid_x <= kTkMaxGroups * kTkGroup &&
+         per_wave * rpb <= kTkList;
+}
+
 int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, int bits, int fmt,
            int epi, const void* x, int x_dtype, const uint16_t* norm_w, float eps,
            const float* residual, float* y, void* ws, size_t ws_bytes, hipStream_t stream,
-           const PreLaunch* pre = nullptr) {
+           const PreLaunch* pre = nullptr, const TopkOut* tko = nullptr) {
   int rc = check_common(N, K, M, group, bits, fmt, x_dtype);
   if (rc) return rc;
   if ((rc = check_qmat(A, fmt))) return rc;
@@ -315,6 +340,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0, kSegNone}, dev.cus, M > 1 || have_ws);
   if (M > 1 && pl.splits > 1) return QG_EUNSUPPORTED;
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;  // K too long for one slice: needs ws
+  if (epi == kEpiTopk && (!tko || M != 1 || residual || !topk_fits(pl, N, tko->k))) return kNotFused;
   pl.tokens = M;
   MvParams p;
   memset(&p, 0, sizeof(p));
@@ -338,6 +364,13 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   p.slice_chunks = pl.slice_chunks;
   p.grid_x = pl.grid_x;
   p.tokens = M;
+  if (epi == kEpiTopk) {
+    p.tk_k = tko->k;
+    p.tk_idx = tko->idx;
+    p.tk_vals = tko->vals;
+    p.tk_tickets = tko->tickets;
+    p.tk_cand = tko->cand;
+  }
   if (pl.splits > 1) {
     const size_t tickets = ((size_t)(N + 7) / 8 + 64) * 4;
     const size_t tickets_al = (tickets + 255) / 256 * 256;
@@ -403,6 +436,30 @@ int check_logits(int V, int K, int group, int bits, int fmt, int x_dtype, const 
     return QG_EINVAL;
   if (norm_w && !(eps >= 0.f)) return QG_EINVAL;
   return QG_OK;
+}
+
+// The logits matvec and its top-k ([F] section 1: both on the GPU, only the
+// chosen entries come back). Without a draw, and where the plan allows it, one
+// launch: the matvec's workgroups merge their rows' keys themselves
+// (kEpiTopk). Otherwise the matvec, then the top-k kernel (which also draws).
+// ws starts with the top-k region (topk_workspace_bytes), the matvec's follows.
+int run_logits(const qg_qmat* W, int V, int K, int group, int bits, int fmt, const void* x,
+               int x_dtype, const uint16_t* norm_w, float eps, float* logits, int k, int32_t* idx,
+               float* vals, void* ws, size_t ws_bytes, const DrawParams& dp, hipStream_t stream,
+               const PreLaunch* pre) {
+  const size_t tk = topk_workspace_bytes(V, k);
+  char* const base = static_cast<char*>(ws);
+  if (!dp.token && !g_knob[5].load()) {
+    const TopkOut tko{k, idx, vals, reinterpret_cast<uint32_t*>(base + kTkFusedTicketOffset),
+                      reinterpret_cast<uint64_t*>(base + kTkTicketBytes)};
+    const int rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiTopk, x, x_dtype, norm_w, eps,
+                          nullptr, logits, base + tk, ws_bytes - tk, stream, pre, &tko);
+    if (rc != kNotFused) return rc;
+  }
+  int rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps,
+                  nullptr, logits, base + tk, ws_bytes - tk, stream, pre);
+  if (rc) return rc;
+  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, dp, stream);  // 0, -3 or -4 = QG_ codes
 }
 
 // ---- library-held scratch for qlogits_topk_noalloc -------------------------
@@ -520,10 +577,11 @@ int qg_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
 }
 
 // Tuning override for tests and benchmarks: knob 0 = split count, 1 = rows per
-// lane, 2 = lanes per row, 3 = workgroups per CU, 4 = pipeline depth; value 0
-// restores automatic.
+// lane, 2 = lanes per row, 3 = workgroups per CU, 4 = pipeline depth, 5 = 1
+// for the two-launch logits top-k; value 0 restores automatic.
 int qg_tune(int knob, int value) {
-  if (knob < 0 || knob > 4 || value < 0) return QG_EINVAL;
+  if (knob < 0 || knob > 5 || value < 0) return QG_EINVAL;
+  if (knob == 5 && value > 1) return QG_EINVAL;
   if (knob == 4 && value != 0 && value != 2 && value != 4) return QG_EINVAL;
   if (knob == 1 && value != 0 && value != 1 && value != 2) return QG_EINVAL;
   if (knob == 2 && value != 0 && value != 16 && value != 32 && value != 64) return QG_EINVAL;
@@ -590,14 +648,10 @@ int qlogits_topk(const qg_qmat* W, int V, int K, int group, int bits, int fmt, c
                  int32_t* idx, float* vals, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc = check_logits(V, K, group, bits, fmt, x_dtype, norm_w, eps, logits, k, idx, vals);
   if (rc) return rc;
-  const size_t tk = topk_workspace_bytes(V, k);
-  const size_t need = tk + mv_ws_bytes(V, 1, kEpiStore);
+  const size_t need = topk_workspace_bytes(V, k) + mv_ws_bytes(V, 1, kEpiStore);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return QG_EWORKSPACE;
-  char* mvws = static_cast<char*>(ws) + tk;
-  rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps, nullptr,
-              logits, mvws, ws_bytes - tk, stream);
-  if (rc) return rc;
-  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, DrawParams{}, stream);
+  return run_logits(W, V, K, group, bits, fmt, x, x_dtype, norm_w, eps, logits, k, idx, vals, ws,
+                    ws_bytes, DrawParams{}, stream, nullptr);
 }
 
 int qlogits_topk_noalloc(const qg_qmat* W, int V, int K, int group, int bits, int fmt,
@@ -605,17 +659,27 @@ int qlogits_topk_noalloc(const qg_qmat* W, int V, int K, int group, int bits, in
                          float* logits, int k, int32_t* idx, float* vals, hipStream_t stream) {
   int rc = check_logits(V, K, group, bits, fmt, x_dtype, norm_w, eps, logits, k, idx, vals);
   if (rc) return rc;
-  const size_t tk = topk_workspace_bytes(V, k);
-  const size_t need = tk + mv_ws_bytes(V, 1, kEpiStore);
+  const size_t need = topk_workspace_bytes(V, k) + mv_ws_bytes(V, 1, kEpiStore);
   if (need > kStaticScratchBytes) return QG_EUNSUPPORTED;
   if (!device_info().ok) return QG_EDEVICE;
   void* ws = nullptr;
   if ((rc = static_scratch(&ws))) return rc;
   const PreLaunch pre{clear_static_once, nullptr};
-  rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps, nullptr,
-              logits, static_cast<char*>(ws) + tk, need - tk, stream, &pre);
+  return run_logits(W, V, K, group, bits, fmt, x, x_dtype, norm_w, eps, logits, k, idx, vals, ws,
+                    need, DrawParams{}, stream, &pre);
+}
+
+int qg_logits_topk_launches(int V, int K, int group, int bits, int fmt, int k, int* launches) {
+  if (!launches) return QG_EINVAL;
+  int rc = check_common(V, K, 1, group, bits, fmt, QG_F32);
   if (rc) return rc;
-  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, DrawParams{}, stream);
+  if (V < 1 || k < 1 || k > V) return QG_EINVAL;
+  if (k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
+  const DevInfo dev = device_info();
+  if (!dev.ok) return QG_EDEVICE;
+  const MvPlan pl = plan_mv({V, K, bits, fmt, kEpiTopk, 0, kSegNone}, dev.cus, true);
+  *launches = (!g_knob[5].load() && topk_fits(pl, V, k)) ? 1 : 2;
+  return QG_OK;
 }
 
 int qlogits_sample(const qg_qmat* W, int V, int K, int group, int bits, int fmt, const void* x,
@@ -628,14 +692,10 @@ int qlogits_sample(const qg_qmat* W, int V, int K, int group, int bits, int fmt,
   if (rc) return rc;
   rc = check_logits(V, K, group, bits, fmt, x_dtype, norm_w, eps, logits, k, idx, vals);
   if (rc) return rc;
-  const size_t tk = topk_workspace_bytes(V, k);
-  const size_t need = tk + mv_ws_bytes(V, 1, kEpiStore);
+  const size_t need = topk_workspace_bytes(V, k) + mv_ws_bytes(V, 1, kEpiStore);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return QG_EWORKSPACE;
-  char* mvws = static_cast<char*>(ws) + tk;
-  rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiStore, x, x_dtype, norm_w, eps, nullptr,
-              logits, mvws, ws_bytes - tk, stream);
-  if (rc) return rc;
-  return plan_and_launch_topk(logits, V, k, idx, vals, ws, tk, dp, stream);
+  return run_logits(W, V, K, group, bits, fmt, x, x_dtype, norm_w, eps, logits, k, idx, vals, ws,
+                    ws_bytes, dp, stream, nullptr);
 }
 
 int qattn_decode(const float* q, const float* k_new, const float* v_new, uint16_t* k_cache,

@@ -356,6 +356,97 @@ __device__ __forceinline__ void route_wave(const float* __restrict__ logits, int
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// ---------------------------------------------------------------------------
+// Sorting 64 keys held one per lane. The partner of a compare-exchange is
+// reached through DPP and the gfx950 lane-swap instructions, in registers; a
+// shuffle through the LDS crossbar (ds_bpermute) costs an LDS round trip per
+// step (measured: merging 64 lists that way in one wave took ~24 us).
+
+// the value held by lane (lane ^ S), S = 1, 2, ..., 32
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const uint32_t l = threadIdx.x & 63;
+  if constexpr (S == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (S == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (S == 4) {
+    // row_ror:4 brings lane - 4, row_ror:12 lane + 4 (within rows of 16)
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0xF, false);
+    return (l & 4) ? dn : up;
+  } else if constexpr (S == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (S == 16) {
+    // odd rows of the first operand trade places with even rows of the second
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (l & 16) ? r[0] : r[1];
+  } else {
+    static_assert(S == 32, "lane strides 1..32");
+    // upper half of the first operand trades places with lower half of the second
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (l & 32) ? r[0] : r[1];
+  }
+}
+
+template <int S>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+  return ((uint64_t)xor_lane<S>((uint32_t)(v >> 32)) << 32) | (uint64_t)xor_lane<S>((uint32_t)v);
+}
+
+// One compare-exchange at lane stride S over a run of sorted direction
+// `desc`: each lane keeps its own key or its partner's, the larger one when
+// it is the lower lane of a descending run (or the upper of an ascending).
+template <int S>
+__device__ __forceinline__ uint64_t cmp_xchg(uint64_t v, bool desc) {
+  const uint64_t o = xor_lane64<S>(v);
+  const bool keep_larger = (((threadIdx.x & 63) & S) == 0) == desc;
+  return ((v > o) == keep_larger) ? v : o;  // keys are distinct: v == o never happens
+}
+
+// A bitonic sequence over the wave, sorted larger first (half-cleaners at
+// strides 32 down to 1).
+__device__ __forceinline__ uint64_t bitonic_clean_desc(uint64_t v) {
+  v = cmp_xchg<32>(v, true);
+  v = cmp_xchg<16>(v, true);
+  v = cmp_xchg<8>(v, true);
+  v = cmp_xchg<4>(v, true);
+  v = cmp_xchg<2>(v, true);
+  return cmp_xchg<1>(v, true);
+}
+
+// Bitonic sort of the wave's 64 keys, larger first (lane 0 ends with the
+// largest): runs of 2, 4, ..., 32 sorted in alternating directions (the
+// direction of a lane's run of length m is bit m of its lane number), each
+// pair of runs then forming one bitonic run of twice the length.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+  const uint32_t l = threadIdx.x & 63;
+  v = cmp_xchg<1>(v, (l & 2) == 0);
+  v = cmp_xchg<2>(v, (l & 4) == 0);
+  v = cmp_xchg<1>(v, (l & 4) == 0);
+  v = cmp_xchg<4>(v, (l & 8) == 0);
+  v = cmp_xchg<2>(v, (l & 8) == 0);
+  v = cmp_xchg<1>(v, (l & 8) == 0);
+  v = cmp_xchg<8>(v, (l & 16) == 0);
+  v = cmp_xchg<4>(v, (l & 16) == 0);
+  v = cmp_xchg<2>(v, (l & 16) == 0);
+  v = cmp_xchg<1>(v, (l & 16) == 0);
+  v = cmp_xchg<16>(v, (l & 32) == 0);
+  v = cmp_xchg<8>(v, (l & 32) == 0);
+  v = cmp_xchg<4>(v, (l & 32) == 0);
+  v = cmp_xchg<2>(v, (l & 32) == 0);
+  v = cmp_xchg<1>(v, (l & 32) == 0);
+  return bitonic_clean_desc(v);
+}
+
+// The 64 largest of two lists of distinct keys, sorted larger first: `a`
+// sorted larger first, `b_rev` smaller first (a list read back in reverse
+// lane order). The lane-wise larger of the two is the upper half of the
+// union as a bitonic sequence.
+__device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b_rev) {
+  return bitonic_clean_desc(a > b_rev ? a : b_rev);
+}
+
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -25,7 +25,22 @@ struct QMat {
 enum Epi : int {
   kEpiStore = 0,   // y = acc (+ residual)
   kEpiSwiglu = 1,  // y = silu(acc_A) * acc_B
+  kEpiTopk = 2,    // y = acc, and the k largest (y, row) of the launch into tk_idx / tk_vals
 };
+
+// Top-k fused into the logits matvec: every workgroup sorts its rows' keys
+// and keeps its 64 largest; groups of kTkGroup workgroups and then the groups
+// are merged by the last to finish (integer tickets). Limits of the fused
+// form (the host falls back to a separate top-k launch beyond them).
+constexpr int kTkList = 64;       // keys per list (k <= kTkList)
+constexpr int kTkGroup = 16;      // workgroups per first-level group (the last may be short)
+constexpr int kTkMaxGroups = 32;  // so at most 512 workgroups
+// Top-k workspace (topk_workspace_bytes): a ticket region, then the
+// candidate lists of whichever form runs. The two-launch top-k's ticket is at
+// offset 0, the fused form's kTkMaxGroups + 1 tickets at kTkFusedTicketOffset.
+constexpr size_t kTkTicketBytes = 1024;
+constexpr size_t kTkFusedTicketOffset = 512;
+static_assert(kTkFusedTicketOffset + (kTkMaxGroups + 1) * 4 <= kTkTicketBytes, "fused tickets fit");
 
 // Where the rows / columns of the logical matrix come from.
 //  kSegNone: one matrix, A[0] (and B[0] for SwiGLU).
@@ -80,6 +95,12 @@ struct MvParams {
   float* partials;    // [splits][n_acc][N] when splits > 1
   uint32_t* tickets;  // [grid_x] zero-initialized when splits > 1
   int tokens;         // vectors served by one launch (0 or 1: one; more: splits == 1)
+  // fused top-k (kEpiTopk)
+  int tk_k;
+  uint64_t* tk_cand;     // [grid_x][kTkList] workgroup lists, then [groups][kTkList] group lists
+  uint32_t* tk_tickets;  // [kTkMaxGroups + 1], zero between calls
+  int32_t* tk_idx;       // [tk_k]
+  float* tk_vals;        // [tk_k]
 };
 
 // Launch configuration chosen on the host.

@@ -39,6 +39,7 @@
 // exact power-of-two range scale 2^-e chosen from max|x| over the slice; the
 // chunk result is multiplied back by 2^(24+e). The LUT format keeps x in fp32.
 #include <mutex>
+#include <type_traits>
 #include <unordered_map>
 
 #include "qg_common.h"
@@ -572,6 +573,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   constexpr int SUB = 64 / LPR;
   constexpr int RPB = SUB * R;  // rows per band
   constexpr bool TWO = (EPI == kEpiSwiglu);
+  constexpr bool TOPK = (EPI == kEpiTopk);
   constexpr int NACC = TWO ? 2 : 1;
   constexpr int LUTN = (FMT == 1) ? (R * NACC * 16 + LPR - 1) / LPR : 0;
   typedef PassData<R, TWO, LUTN> PD;
@@ -579,6 +581,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   extern __shared__ u32x4 smem[];
   __shared__ float red[2 * kWaves];
   __shared__ int last_flag;
+  __shared__ uint64_t tk_keys[TOPK ? kWaves : 1][kTkList];  // each wave's row keys, then sorted
   __shared__ int32_t rt_ids[kMaxRoutes];
   __shared__ float rt_w[kMaxRoutes];
 
@@ -614,7 +617,9 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPR;
   const int j = lane % LPR;
-  if (tile * kWaves >= nbands) return;  // same for every slice of this tile: no ticket needed
+  // same for every slice of this tile: no split-K ticket needed (a fused
+  // top-k launch keeps every workgroup: each takes its group's ticket)
+  if (!TOPK && tile * kWaves >= nbands) return;
   const int band_stride = p.grid_x * kWaves;
 
   // Quarter staging (one quarter unit of x per thread): x and the segment
@@ -895,6 +900,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   for (int r = 0; r < R; ++r) acc_a[r] = acc_b[r] = 0.f;
   int cur_band = tile * kWaves + wave, cur_pass = 0;
 
+  int tk_n = 0;  // fused top-k: this wave's keys recorded so far (uniform)
   auto finish_band = [&](int band) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -905,6 +911,11 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int n = band * RPB + sub * R + r;
+        if constexpr (TOPK) {
+          if (band < nbands) tk_keys[wave][tk_n + sub * R + r] = n < p.N ? order_key(acc_a[r], (uint32_t)n) : 0ull;
+          if (n < p.N) handoff_store(&yp[n], acc_a[r]);  // read back by the last workgroup
+          continue;
+        }
         if (n < p.N) {
           if (p.splits > 1) {
             handoff_store(&p.partials[((size_t)slice * NACC) * p.N + n], acc_a[r]);
@@ -919,6 +930,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) acc_a[r] = acc_b[r] = 0.f;
+    if constexpr (TOPK) tk_n += band < nbands ? RPB : 0;
   };
 
   // Every slot runs on every round, also past the last band (zeros in, no
@@ -948,6 +960,89 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
         cur_band += band_stride;
       }
     }
+  }
+
+  if constexpr (TOPK) {
+    // Fused top-k (page "Booster la vitesse d'inference sur Apple Silicon",
+    // section 1: logits matvec + top-k on the GPU). Keys order values larger
+    // first, equal values by lower row, so every list below is a set with no
+    // ties and each merge is exact: the workgroup's 64 largest keys, then a
+    // group's, then the launch's. A list taken as the second operand of a
+    // merge is read in reverse lane order (smaller first).
+    static_assert(kTkGroup % kWaves == 0 && kTkMaxGroups % kWaves == 0, "lists per wave");
+    // Merges the waves' lists (each sorted larger first) in three rounds of
+    // pairs through LDS; wave 0 returns the result. Every thread calls it.
+    auto merge_waves = [&](uint64_t a) -> uint64_t {
+      tk_keys[wave][lane] = a;
+      __syncthreads();
+#pragma unroll
+      for (int half = kWaves / 2; half >= 1; half >>= 1) {
+        if (wave < half) {  // reads slots [half, 2 half), writes [0, half)
+          a = wave_merge_top(a, tk_keys[wave + half][63 - lane]);
+          tk_keys[wave][lane] = a;
+        }
+        __syncthreads();
+      }
+      return a;
+    };
+    // Wave w merges lists w, w + kWaves, ... (< n) of `base`; zeros past n.
+    auto merge_strided = [&](const __amdgpu_buffer_rsrc_t r, int first, int n, auto per) -> uint64_t {
+      constexpr int PER = decltype(per)::value;
+      uint64_t b[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int t = wave + i * kWaves;
+        b[i] = coherent_u64(r, t < n ? (uint32_t)(((first + t) * kTkList + (i ? 63 - lane : lane)) * 8) : kOOB);
+      }
+      uint64_t a = b[0];
+#pragma unroll
+      for (int i = 1; i < PER; ++i)
+        if (wave + i * kWaves < n) a = wave_merge_top(a, b[i]);
+      return a;
+    };
+    wave_sync_lds();
+    uint64_t v = lane < tk_n ? tk_keys[wave][lane] : 0ull;
+    v = merge_waves(wave_sort_desc(v));
+    const int ngroups = (p.grid_x + kTkGroup - 1) / kTkGroup;
+    uint64_t* const wg_lists = p.tk_cand;
+    uint64_t* const grp_lists = p.tk_cand + (size_t)p.grid_x * kTkList;
+    if (wave == 0) handoff_store(&wg_lists[(size_t)tile * kTkList + lane], v);
+    stores_done();  // this workgroup's logits and list, before its ticket
+    __syncthreads();
+    const int g = tile / kTkGroup;
+    const int g0 = g * kTkGroup, gsize = min(kTkGroup, p.grid_x - g0);
+    if (threadIdx.x == 0) last_flag = take_ticket(&p.tk_tickets[g]) == (uint32_t)(gsize - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    // the group's last workgroup merges its lists
+    v = merge_strided(make_rsrc(wg_lists, (uint32_t)(p.grid_x * kTkList * 8)), g0, gsize,
+                      std::integral_constant<int, kTkGroup / kWaves>{});
+    v = merge_waves(v);
+    if (wave == 0) {
+      handoff_store(&grp_lists[(size_t)g * kTkList + lane], v);
+      if (lane == 0) handoff_store(&p.tk_tickets[g], 0u);  // ready for the next call
+    }
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) last_flag = take_ticket(&p.tk_tickets[kTkMaxGroups]) == (uint32_t)(ngroups - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    // the last group merger: the launch's k largest, larger first
+    v = merge_strided(make_rsrc(grp_lists, (uint32_t)(ngroups * kTkList * 8)), 0, ngroups,
+                      std::integral_constant<int, kTkMaxGroups / kWaves>{});
+    v = merge_waves(v);
+    if (wave == 0) {
+      if (lane < p.tk_k) {
+        const uint32_t i = key_index(v);
+        float val = key_value(v);
+        // a zero (its sign) and a NaN (its payload) come back from memory
+        if (val == 0.f || val != val) val = coherent_f32(make_rsrc(yp, (uint32_t)p.N * 4u), i * 4u);
+        p.tk_idx[lane] = (int32_t)i;
+        p.tk_vals[lane] = val;
+      }
+      if (lane == 0) handoff_store(&p.tk_tickets[kTkMaxGroups], 0u);
+    }
+    return;
   }
 
   if (p.splits > 1) {
@@ -1000,8 +1095,21 @@ KernelFn pick_kernel(int lpr, int rows, int depth) {
   return nullptr;
 }
 
+// the fused top-k: one row per lane slot, pipeline depth 2
+template <int BITS, int FMT, int LPR>
+KernelFn pick_topk(int rows) {
+  return rows == 1 ? qmv_kernel<BITS, FMT, LPR, 1, kEpiTopk, kSegNone, 2> : nullptr;
+}
+
 template <int BITS, int FMT>
 KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows, int depth) {
+  if (epi == kEpiTopk) {
+    if (seg != kSegNone) return nullptr;
+    if (lpr == 64) return pick_topk<BITS, FMT, 64>(rows);
+    if (lpr == 32) return pick_topk<BITS, FMT, 32>(rows);
+    if (lpr == 16) return pick_topk<BITS, FMT, 16>(rows);
+    return nullptr;
+  }
   if constexpr (FMT != 0) {  // the LUT and dense formats are not gathered by experts
     if (seg != kSegNone) return nullptr;
     if (epi == kEpiStore) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows, depth);

@@ -381,7 +381,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
 
 size_t topk_workspace_bytes(int V, int k) {
   const size_t G = ((size_t)V + kTkSlice - 1) / kTkSlice;
-  return 256 + ((G * (size_t)k * 8 + 255) / 256) * 256;
+  const size_t two = ((G * (size_t)k * 8 + 255) / 256) * 256;  // slice lists of the top-k kernel
+  // workgroup and group lists of the fused form (at most kTkMaxGroups groups)
+  const size_t fused = (size_t)(kTkMaxGroups * kTkGroup + kTkMaxGroups) * kTkList * 8;
+  return kTkTicketBytes + (two > fused ? two : fused);
 }
 
 int plan_and_launch_topk(const float* logits, int V, int k, int32_t* idx, float* vals, void* ws,
@@ -389,7 +392,7 @@ int plan_and_launch_topk(const float* logits, int V, int k, int32_t* idx, float*
   if (ws_bytes < topk_workspace_bytes(V, k)) return -3;
   const int G = (V + kTkSlice - 1) / kTkSlice;
   uint32_t* ticket = static_cast<uint32_t*>(ws);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 256);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kTkTicketBytes);
   hipLaunchKernelGGL(topk_kernel, dim3(G), dim3(kTkThreads), 0, stream, logits, V, k, cand,
                      ticket, idx, vals, dp);
   return hipGetLastError() == hipSuccess ? 0 : -4;

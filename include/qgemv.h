@@ -153,8 +153,10 @@ int qg_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 /* Variant override for tests and benchmarks; normal callers never need it.
  * knob 0 = number of K slices (split-K, needs a workspace), 1 = rows per lane
  * (1 or 2), 2 = lanes per row (16, 32 or 64), 3 = resident workgroups per
- * compute unit; value 0 restores the automatic choice. Process-wide; affects
- * calls made after it returns. QG_EINVAL for an unknown knob or value. */
+ * compute unit, 4 = (band, pass) items in flight per wave (2 or 4), 5 = 1 for
+ * the two-launch form of qlogits_topk; value 0 restores the automatic choice.
+ * Process-wide; affects calls made after it returns. QG_EINVAL for an unknown
+ * knob or value. */
 int qg_tune(int knob, int value);
 
 /* qgemv -- y[m][n] = residual[m][n] + sum_k W[n][k] * x[m][k]
@@ -229,11 +231,22 @@ int qmoe_experts_batch(const qg_qmat *gate_all, const qg_qmat *up_all, const qg_
  * NULL), written to logits[V]; then the k largest entries of z, larger first
  * and equal values by lower index, into idx[k] (int32) and vals[k] (fp32)
  * ([F] section 1: logits matvec + top-k on the GPU, only the chosen entries
- * need to come back). M must be 1 (x is [K]). 1 <= k <= min(V, QG_MAX_TOPK). */
+ * need to come back). M must be 1 (x is [K]). 1 <= k <= min(V, QG_MAX_TOPK).
+ * For k <= 64 one launch where the shape allows it: each matvec workgroup
+ * keeps its rows' 64 largest and the last workgroups to finish merge the
+ * lists; otherwise the matvec and then a separate top-k launch. Both forms
+ * return the same bits. Calls that overlap on one workspace race. */
 int qlogits_topk(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
                  const void *x, int x_dtype, const uint16_t *norm_w, float eps,
                  float *logits, int k, int32_t *idx, float *vals,
                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* qg_logits_topk_launches -- *launches = the number of kernels (1 or 2) that
+ * qlogits_topk and qlogits_topk_noalloc enqueue for this shape on the current
+ * device under the current tuning (for profilers and graph budgets; the
+ * sampling call always takes 2). Enqueues nothing. Statuses as qlogits_topk;
+ * QG_EDEVICE without a usable gfx950. */
+int qg_logits_topk_launches(int V, int K, int group, int bits, int fmt, int k, int *launches);
 
 /* qlogits_topk_noalloc -- qlogits_topk without a workspace argument, for
  * callers that cannot allocate device memory: code under HIP graph capture,

@@ -208,8 +208,35 @@ def test_tune_rejects_bad_values(L):
     assert L.qg_tune(1, 3) == qg.QG_EINVAL
     assert L.qg_tune(2, 48) == qg.QG_EINVAL
     assert L.qg_tune(0, 17) == qg.QG_EINVAL
-    for k in range(4):
+    assert L.qg_tune(4, 3) == qg.QG_EINVAL
+    assert L.qg_tune(5, 2) == qg.QG_EINVAL
+    assert L.qg_tune(6, 0) == qg.QG_EINVAL
+    for k in range(6):
         assert L.qg_tune(k, 0) == qg.QG_OK
+
+
+def test_logits_workspace_holds_both_topk_forms(L):
+    """The logits workspace: a 1 KiB ticket region, then room for the larger
+    of the one-launch top-k's lists (up to 512 workgroup lists and 32 group
+    lists of 64 eight-byte keys) and the two-launch top-k's lists (k keys per
+    4096-entry slice, rounded up to 256 bytes), then the matvec's region."""
+    one = (512 + 32) * 64 * 8
+    for V, k in ((151936, 40), (1000, 1), (9000, 1024), (1 << 20, 1024)):
+        slices = -(-V // 4096)
+        two = -(-slices * k * 8 // 256) * 256
+        mv = qg.qg_workspace_bytes(qg.QG_OP_GEMV, V, 1024)
+        got = qg.qg_workspace_bytes(qg.QG_OP_LOGITS_TOPK, V, 1024, 1, 4, 0, k)
+        assert got == 1024 + max(one, two) + mv, (V, k)
+
+
+def test_launch_query_checks_arguments(L):
+    n = ctypes.c_int(0)
+    assert L.qg_logits_topk_launches(1000, 1024, 64, 4, 0, 40, None) == qg.QG_EINVAL
+    assert L.qg_logits_topk_launches(1000, 1024, 64, 4, 0, 1001, ctypes.byref(n)) == qg.QG_EINVAL
+    assert L.qg_logits_topk_launches(1000, 1024, 64, 4, 0, 0, ctypes.byref(n)) == qg.QG_EINVAL
+    assert L.qg_logits_topk_launches(5000, 1024, 64, 4, 0, 1025, ctypes.byref(n)) == qg.QG_EUNSUPPORTED
+    assert L.qg_logits_topk_launches(1000, 1000, 64, 4, 0, 4, ctypes.byref(n)) == qg.QG_EINVAL
+    assert L.qg_logits_topk_launches(1000, 1024, 32, 4, 0, 4, ctypes.byref(n)) == qg.QG_EUNSUPPORTED
 
 
 def test_empty_rows_is_a_no_op(L):

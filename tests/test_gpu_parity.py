@@ -31,8 +31,17 @@ def qg():
         pytest.skip("no GPU")
     qg.lib()
     yield qg
-    for k in range(4):
+    for k in range(6):
         qg.qg_tune(k, 0)
+
+
+# the logits top-k: one launch (the matvec's workgroups merge their rows'
+# keys) or the matvec and then the top-k kernel (knob 5 = 1)
+TOPK_PATHS = ["one_launch", "two_launch"]
+
+
+def set_topk_path(qg, path):
+    qg.qg_tune(5, 1 if path == "two_launch" else 0)
 
 
 DEV = "cuda"
@@ -256,8 +265,11 @@ def test_residual_in_place(qg):
 
 
 # ---------------------------------------------------------------------------
-def test_topk_ties_bit_exact(qg):
-    """s = 0 and x = 1 make logit_n = 64 * b_n exactly; duplicate b give ties."""
+@pytest.mark.parametrize("path", TOPK_PATHS)
+def test_topk_ties_bit_exact(qg, path):
+    """s = 0 and x = 1 make logit_n = 64 * b_n exactly; duplicate b give ties
+    (and -0 ties +0: order by index, the value comes back with its sign)."""
+    set_topk_path(qg, path)
     V, K, k = 5000, 64, 40
     W = synth.qmat(13, "ties", V, K, 4)
     W["scales"][:] = 0
@@ -271,13 +283,18 @@ def test_topk_ties_bit_exact(qg):
     assert np.array_equal(zc, (64.0 * W["biases"][:, 0].astype(np.float64)).astype(np.float32))
     ridx, rvals = oracle.topk(zc, k)
     assert np.array_equal(idx.cpu().numpy(), ridx)
-    assert np.array_equal(vals.cpu().numpy(), rvals.astype(np.float32))
+    assert np.array_equal(vals.cpu().numpy().view(np.uint32),
+                          rvals.astype(np.float32).view(np.uint32))
+    qg.qg_tune(5, 0)
 
 
+@pytest.mark.parametrize("path", TOPK_PATHS)
 @pytest.mark.parametrize("V,K,k,norm", [(151936, 1024, 40, True), (1000, 256, 1, False),
-                                        (40, 128, 40, True), (9000, 64, 1024, False)])
-def test_qlogits_topk(qg, V, K, k, norm):
-    say(f"qlogits_topk V={V} K={K} k={k}")
+                                        (40, 128, 40, True), (9000, 64, 1024, False),
+                                        (1, 64, 1, False), (151936, 1024, 64, False)])
+def test_qlogits_topk(qg, V, K, k, norm, path):
+    say(f"qlogits_topk V={V} K={K} k={k} {path}")
+    set_topk_path(qg, path)
     W = synth.qmat(14, ("lm", V, K), V, K, 4)
     g = synth.norm_weight(14, "gf", K) if norm else None
     x = synth.activations(14, "x", K, np.float32) * 5.0
@@ -297,6 +314,47 @@ def test_qlogits_topk(qg, V, K, k, norm):
                                  None if g is None else to_dev(g), 1e-5, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
+    qg.qg_tune(5, 0)
+
+
+def test_topk_launch_count(qg):
+    """One launch for the Qwen-shaped head at k <= 64, two past 64 keys, for
+    more rows per wave than a key list holds, and under knob 5."""
+    assert qg.qg_logits_topk_launches(151936, 1024, 40) == 1
+    assert qg.qg_logits_topk_launches(151936, 1024, 64) == 1
+    assert qg.qg_logits_topk_launches(151936, 1024, 65) == 2
+    assert qg.qg_logits_topk_launches(300007, 64, 8) == 2
+    qg.qg_tune(5, 1)
+    try:
+        assert qg.qg_logits_topk_launches(151936, 1024, 40) == 2
+    finally:
+        qg.qg_tune(5, 0)
+
+
+@pytest.mark.parametrize("bits,fmt", FMTS + [(8, synth.AFFINE), (16, synth.DENSE)])
+@pytest.mark.parametrize("V,K,k", [(20011, 512, 64), (300007, 64, 8), (4099, 4096, 17)])
+def test_topk_one_launch_equals_two(qg, bits, fmt, V, K, k):
+    """Every weight format, ragged vocabularies: the one-launch head gives the
+    same logits, indices and values, bit for bit, as the matvec followed by
+    the separate top-k, and its indices are the oracle's top-k of those
+    logits. 300007 x 64 has more rows per wave than one key list holds, so it
+    takes the two-launch form on both sides."""
+    say(f"topk one vs two launches V={V} K={K} k={k} bits={bits} fmt={fmt}")
+    W = dev_mat(qg, synth.qmat(15, ("tk1", V, K) + fmt_tag(bits, fmt), V, K, bits, fmt))
+    x = to_dev(synth.activations(15, ("tk1x", K), K, np.float32) * 3.0)
+    ws = qg.workspace(qg.QG_OP_LOGITS_TOPK, V, K, 1, bits, fmt, k, DEV)
+    out = []
+    for path in ("one_launch", "two_launch", "one_launch"):
+        set_topk_path(qg, path)
+        out.append(qg.qlogits_topk(W, x, k, ws=ws))
+    qg.qg_tune(5, 0)
+    torch.cuda.synchronize()
+    for (z, i, v) in out[1:]:
+        assert torch.equal(z, out[0][0]) and torch.equal(i, out[0][1]) and torch.equal(v, out[0][2])
+    zc = out[0][0].cpu().numpy()
+    ridx, rvals = oracle.topk(zc, k)
+    assert np.array_equal(out[0][1].cpu().numpy(), ridx)
+    assert np.array_equal(out[0][2].cpu().numpy(), rvals.astype(np.float32))
 
 
 # ---------------------------------------------------------------------------
