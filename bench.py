@@ -71,7 +71,8 @@ def traffic_name(args) -> str:
         fmt = {0: f"{args.bits}bit", 1: "lut", 2: "dense_f16"}[args.fmt]
         return f"traffic_llama3_8b_stack_{fmt}_m{args.m}"
     return {"single": "traffic_qgemv_2048x2048_single", "moe": f"traffic_qmoe_512_experts_m{args.m}",
-            "qwen": "traffic_qwen3_06b_stack_logits", "attn": "traffic_qattn"}[args.config]
+            "qwen": "traffic_qwen3_06b_stack_logits", "attn": "traffic_qattn",
+            "phases": "traffic_phases"}[args.config]
 
 
 def pmc_reference_reads(qg, dev):
@@ -832,6 +833,91 @@ def run_qwen(args, qg, synth, dev):
          step_bytes, ms, dom, peaks, cpu, arith_dtype(4, 0, 1))
 
 
+def run_phases(args, qg, synth, dev):
+    """The Llama-3-8B-shaped token's matvec byte ranges (qkv, o, gate.up,
+    down per layer) read with no arithmetic, three ways: one launch per range
+    (the launch-per-matvec design), one launch over every range, and one
+    launch with a device-wide barrier between ranges (what a persistent
+    whole-token kernel needs, each matvec's x being the previous one's
+    output). Prices the launch boundary against the barrier on the same
+    bytes; the line's value is the launch-per-range rate."""
+    import torch
+    model = dict(synth.LLAMA3_8B)
+    model["layers"] = args.layers
+    H, FF, QD, NQ = model["hidden"], model["ffn"], model["q_dim"], model["qkv"]
+    per_layer = [synth.qmat_bytes(NQ, H), synth.qmat_bytes(H, QD), 2 * synth.qmat_bytes(FF, H),
+                 synth.qmat_bytes(H, FF)]
+    flat, off = [], 0
+    for _ in range(model["layers"]):
+        for b in per_layer:
+            flat += [off, b]
+            off += -(-b // 256) * 256
+    n, total = len(flat) // 2, off
+    src = torch.empty(total, dtype=torch.uint8, device=dev)
+    src.fill_(7)
+    rng = torch.tensor(flat, dtype=torch.int64, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(2 * cus * 512, dtype=torch.int32, device=dev)
+    flags = torch.zeros(2 * cus, dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = sum(flat[1::2])
+    log(f"phases: {n} ranges, {nbytes / 1e9:.3f} GB")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(3, min(args.steps, 20))
+
+    def timed(launch, prep=None):
+        ts = []
+        for r in range(reps + 2):
+            if prep:
+                prep()
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    res = {}
+    for wg_per_cu in (1, 2):
+        blocks = cus * wg_per_cu
+
+        def per_range():
+            for q in range(n):
+                qg.qg_probe_phases(src, rng[2 * q:], 1, False, out, blocks)
+
+        # one launch per range, replayed from a graph like the decode token
+        per_range()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            per_range()
+        t_launch = timed(g.replay)
+        t_one = timed(lambda: qg.qg_probe_phases(src, rng, n, False, out, blocks))
+        err.zero_()
+        t_bar = timed(lambda: qg.qg_probe_phases(src, rng, n, True, out, blocks, flags, err),
+                      prep=flags.zero_)
+        torch.cuda.synchronize()
+        if int(err.item()):
+            raise RuntimeError("phase barrier exceeded its spin limit; timing void")
+        res[f"{wg_per_cu}_wg_per_cu"] = {
+            "blocks": blocks, "us_launch_per_range": round(t_launch, 1),
+            "us_one_launch": round(t_one, 1), "us_one_launch_barrier": round(t_bar, 1),
+            "us_per_launch_boundary": round((t_launch - t_one) / (n - 1), 3),
+            "us_per_barrier": round((t_bar - t_one) / (n - 1), 3),
+            "gbs_launch_per_range": round(nbytes / (t_launch * 1e-6) / 1e9, 1),
+            "gbs_one_launch": round(nbytes / (t_one * 1e-6) / 1e9, 1),
+            "gbs_one_launch_barrier": round(nbytes / (t_bar * 1e-6) / 1e9, 1)}
+        log(f"phases {wg_per_cu} wg/cu: {res[f'{wg_per_cu}_wg_per_cu']}")
+    best = min(res.values(), key=lambda r: r["us_launch_per_range"])
+    us = best["us_launch_per_range"]
+    dom = roofline(f"probe_phases_kernel ({n} ranges, one launch each)", nbytes / n, us / n)
+    peaks = probe_peaks(qg, dev)
+    cfg = {"layers": model["layers"], "ranges": n, "phases": res}
+    emit(args, "llama3-8b-shaped token byte ranges, read only (launch boundary vs grid barrier)",
+         cfg, nbytes, us * 1e-3, dom, peaks, None, "u32 (xor of the bytes read)")
+
+
 def run_attn(args, qg, synth, dev):
     """Decode attention of a Llama-3-8B-shaped model (32 query heads, 8 kv
     heads, head dimension 128) at context length --ctx: one step is the
@@ -892,7 +978,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="stack", choices=["stack", "single", "moe", "qwen", "attn"])
+    ap.add_argument("--config", default="stack",
+                    choices=["stack", "single", "moe", "qwen", "attn", "phases"])
     ap.add_argument("--ctx", type=int, default=8192, help="attn: context length (positions)")
     ap.add_argument("--bits", type=int, default=4, choices=[2, 4, 8, 16],
                     help="stack: code width (16 = dense fp16 weights, with --fmt 2)")
@@ -949,7 +1036,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     {"stack": run_stack, "single": run_single, "moe": run_moe, "qwen": run_qwen,
-     "attn": run_attn}[args.config](args, qg, synth, dev)
+     "attn": run_attn, "phases": run_phases}[args.config](args, qg, synth, dev)
 
 
 if __name__ == "__main__":

@@ -34,7 +34,7 @@ EXPORTED = ("qg_status_str", "qg_workspace_bytes", "qg_workspace_init", "qg_tune
             "qgemv_rmsnorm", "qswiglu", "qmoe_experts", "qmoe_experts_batch", "qlogits_topk",
             "qlogits_topk_noalloc", "qg_logits_topk_launches", "qlogits_sample",
             "qg_sample_topk", "qattn_decode", "qg_probe_read",
-            "qg_probe_copy")
+            "qg_probe_copy", "qg_probe_phases")
 
 
 class QgError(RuntimeError):
@@ -81,6 +81,7 @@ def lib():
         L.qattn_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, F, P, P, S, P]
         L.qg_probe_read.argtypes = [P, S, P, I, I, P]
         L.qg_probe_copy.argtypes = [P, P, S, I, P]
+        L.qg_probe_phases.argtypes = [P, S, P, I, I, P, P, P, I, I, P]
         for name in EXPORTED:
             if name != "qg_status_str":
                 getattr(L, name).restype = I
@@ -200,6 +201,16 @@ def qg_probe_copy(dst, src, blocks: int, stream=None):
     """Copies src to dst (copy bandwidth probe)."""
     _check(lib().qg_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), blocks,
                                _stream(stream)), "qg_probe_copy")
+
+
+def qg_probe_phases(src, ranges, nphases: int, barrier: bool, out, blocks: int, flags=None,
+                    err=None, spin_limit: int = 1 << 20, stream=None):
+    """Streams nphases byte ranges of src (ranges: int64 [2*nphases] device
+    tensor of offset, count) in one launch, with or without a grid barrier
+    between them (phase probe)."""
+    _check(lib().qg_probe_phases(_ptr(src), src.numel() * src.element_size(), _ptr(ranges),
+                                 nphases, 1 if barrier else 0, _ptr(flags), _ptr(out), _ptr(err),
+                                 blocks, spin_limit, _stream(stream)), "qg_probe_phases")
 
 
 def _ws_args(ws):

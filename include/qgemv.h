@@ -333,6 +333,23 @@ int qg_probe_read(const void *src, size_t bytes, uint32_t *out, int blocks, int 
                   hipStream_t stream);
 int qg_probe_copy(void *dst, const void *src, size_t bytes, int blocks, hipStream_t stream);
 
+/* qg_probe_phases -- one launch of `blocks` workgroups of 512 threads that
+ * reads nphases byte ranges of src in order, the way a persistent kernel
+ * would stream a whole token's matvecs ([F] TL;DR lever 3 and section 1:
+ * per-token overhead). ranges: device array [2 * nphases] uint64 of
+ * (byte offset, byte count), each a multiple of 16; a range is clipped to
+ * src_bytes. barrier = 1 adds a device-wide barrier between ranges (each
+ * workgroup publishes one coherent word, raises flags[block] to the range
+ * number and waits for every flag): flags [blocks] must be zero at launch,
+ * err [1] counts workgroups whose wait exceeded
+ * spin_limit polls (1 <= spin_limit <= 2^22; the launch then ends early and
+ * its timing is void). With barrier = 1, blocks must not exceed 1024 nor
+ * the workgroups that fit on the device at once (QG_EUNSUPPORTED). out
+ * [blocks * 512] receives one uint32 per thread. Measurement only. */
+int qg_probe_phases(const void *src, size_t src_bytes, const uint64_t *ranges, int nphases,
+                    int barrier, uint32_t *flags, uint32_t *out, uint32_t *err, int blocks,
+                    int spin_limit, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
