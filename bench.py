@@ -400,7 +400,8 @@ def emit(args, workload, cfg, step_bytes, ms, dom, peaks, cpu, dtype):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": dict({"workload": workload, "bytes_per_step": step_bytes}, **cfg),
+        "config": dict({"workload": workload, "bytes_per_step": step_bytes}, **cfg,
+                       **({"tune": args.tune} if args.tune else {})),
         "steps_per_s": round(1e3 / ms, 2),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "frac_of_read_peak": round(gbs / peaks["read_gbs"], 4),
@@ -991,6 +992,9 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE",
+                    help="qg_tune override applied before the run (repeatable), e.g. 6=1 for staged "
+                         "scale/bias rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-pass", action="store_true",
@@ -1035,6 +1039,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    for t in args.tune:
+        knob, value = (int(v) for v in t.split("="))
+        qg.qg_tune(knob, value)
     {"stack": run_stack, "single": run_single, "moe": run_moe, "qwen": run_qwen,
      "attn": run_attn, "phases": run_phases}[args.config](args, qg, synth, dev)
 

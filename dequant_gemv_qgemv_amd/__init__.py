@@ -73,7 +73,7 @@ def lib():
                                          S, P]
         L.qlogits_topk.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P, S, P]
         L.qlogits_topk_noalloc.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, P]
-        L.qg_logits_topk_launches.argtypes = [I, I, I, I, I, I, ctypes.POINTER(I)]
+        L.qg_logits_topk_launches.argtypes = [Q, I, I, I, I, I, I, ctypes.POINTER(I)]
         U64 = ctypes.c_uint64
         L.qlogits_sample.argtypes = [Q, I, I, I, I, I, P, I, P, F, P, I, P, P, F, F, U64, P, P,
                                      P, S, P]
@@ -183,10 +183,12 @@ def qg_tune(knob: int, value: int):
 
 
 def qg_logits_topk_launches(V: int, K: int, k: int, bits: int = 4, fmt: int = QG_AFFINE,
-                            group: int = 64) -> int:
-    """Kernels (1 or 2) that qlogits_topk enqueues for this head on the current device."""
+                            group: int = 64, W=None) -> int:
+    """Kernels (1 or 2) that qlogits_topk enqueues for this head (W: its QMat,
+    or None) on the current device."""
     out = ctypes.c_int(0)
-    _check(lib().qg_logits_topk_launches(V, K, group, bits, fmt, k, ctypes.byref(out)),
+    _check(lib().qg_logits_topk_launches(None if W is None else ctypes.byref(W.c), V, K, group,
+                                         bits, fmt, k, ctypes.byref(out)),
            "qg_logits_topk_launches")
     return out.value
 

@@ -53,6 +53,12 @@ DevInfo device_info() {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The scale and bias arrays of W start 16-byte aligned (staged scale/bias
+// rows load them 16 bytes at a time). NULL matrices do not count.
+bool sb_aligned16(const qg_qmat* W) {
+  return !W || (aligned(W->scales, 16) && aligned(W->biases, 16));
+}
+
 // [a, a+na) and [b, b+nb) overlap (byte ranges)
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || !na || !nb) return false;
@@ -140,6 +146,7 @@ struct MvShape {
   int N, K, bits, fmt, epi;
   int col_seg_chunks;  // K-segment length in chunks (0: one matrix along K)
   int seg;             // SegMode of the launch
+  bool sb_aligned;     // every scale/bias array starts 16-byte aligned
 };
 
 // Chooses lanes per row, rows per lane, split-K and grid for one launch.
@@ -165,14 +172,6 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
                 : (s.bits == 4 && s.fmt == QG_AFFINE && s.seg == kSegNone && s.K >= 8192 ? 2 : 1);
   if (s.epi == kEpiTopk) pl.rows = 1;  // the fused top-k keeps one row per lane slot
   pl.depth = g_knob[4].load() ? g_knob[4].load() : 2;
-  // Resident workgroups per CU: two 8-wave groups keep 16 waves in flight
-  // where the kernel's registers allow it. 2-bit codes take one: measured on
-  // MI355X, a second group slows them down (4096 x 14336 down 10.22 us
-  // against 8.96 at 64 lanes, 14336 x 4096 gate.up 12.14 against 11.40 at
-  // 32), while the 4-bit kernels gain from it (gate.up 14.22 against 14.88).
-  const int resident = mv_resident_per_cu(s.bits, s.fmt, s.epi, s.seg, pl);
-  const int wg_cap = s.bits == 2 ? 1 : 2;
-  const int wg_per_cu = g_knob[3].load() ? g_knob[3].load() : (resident < wg_cap ? resident : wg_cap);
   const int rpb = (64 / pl.lpr) * pl.rows;
   const int nbands = (s.N + rpb - 1) / rpb;
   const int tiles = (nbands + kWaves - 1) / kWaves;
@@ -196,6 +195,42 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
   pl.splits = (C + pl.slice_chunks - 1) / pl.slice_chunks;
   const int slice_npass = slice_passes;
   pl.lds_bytes = (size_t)slice_npass * pl.lpr * per_chunk + lut_bytes;
+  // Staged scale/bias rows (affine formats, one K segment), on request (knob
+  // 6 = 1): each band's row segments over the slice come with one or two
+  // 16-byte loads per lane into the wave's LDS area, and every pass reads its
+  // two values per row there. Needs 16-byte aligned row segments (K and the
+  // slice a multiple of 512 codes' groups) and the room in LDS. Not the
+  // default: measured on MI355X it halves the load instructions per wave but
+  // makes the Llama-3-8B-shaped layer slower (41.7 against 38.4 us; qkv 7.06
+  // against 6.12, o 6.33 against 5.55), the MoE layer unchanged (20.2 us).
+  pl.sbl = 0;
+  pl.sb_segp = 0;
+  if (s.fmt == QG_AFFINE && s.seg != kSegCols && s.sb_aligned && g_knob[6].load() == 1 &&
+      !(pl.rows == 2 && s.epi == kEpiSwiglu)) {
+    const int cpg = 64 / codes_per_chunk(s.bits);
+    const int gpr = s.K / 64;
+    const int gsl = (pl.slice_chunks < C ? pl.slice_chunks : C) / cpg;  // groups per slice
+    const int nacc = s.epi == kEpiSwiglu ? 2 : 1;
+    const int want = pl.rows == 2 ? 2 : 1;  // loads per lane and band the kernels provide
+    if ((gpr * 2) % 16 == 0 && (gsl * 2) % 16 == 0 && pl.slice_chunks % cpg == 0) {
+      const int segp = gsl * 2 / 16;
+      const int pieces = rpb * nacc * 2 * segp;
+      const size_t sb_bytes = (size_t)kWaves * pieces * 16;
+      if (pieces <= 64 * want && pl.lds_bytes + sb_bytes <= kLdsBudget) {
+        pl.sbl = want;
+        pl.sb_segp = segp;
+        pl.lds_bytes += sb_bytes;
+      }
+    }
+  }
+  // Resident workgroups per CU: two 8-wave groups keep 16 waves in flight
+  // where the kernel's registers allow it. 2-bit codes take one: measured on
+  // MI355X, a second group slows them down (4096 x 14336 down 10.22 us
+  // against 8.96 at 64 lanes, 14336 x 4096 gate.up 12.14 against 11.40 at
+  // 32), while the 4-bit kernels gain from it (gate.up 14.22 against 14.88).
+  const int resident = mv_resident_per_cu(s.bits, s.fmt, s.epi, s.seg, pl);
+  const int wg_cap = s.bits == 2 ? 1 : 2;
+  const int wg_per_cu = g_knob[3].load() ? g_knob[3].load() : (resident < wg_cap ? resident : wg_cap);
   int gx = tiles;
   const int cap = (cus * wg_per_cu + pl.splits - 1) / pl.splits;
   if (gx > cap) gx = cap;
@@ -337,7 +372,8 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   // Several vectors keep each vector's K in one slice (per-vector split-K
   // partials are not provided): planned as if a workspace were there, so a
   // K that needs slices is refused whatever workspace came with the call.
-  MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0, kSegNone}, dev.cus, M > 1 || have_ws);
+  const bool sb_al = sb_aligned16(A) && (epi != kEpiSwiglu || sb_aligned16(B));
+  MvPlan pl = plan_mv({N, K, bits, fmt, epi, 0, kSegNone, sb_al}, dev.cus, M > 1 || have_ws);
   if (M > 1 && pl.splits > 1) return QG_EUNSUPPORTED;
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;  // K too long for one slice: needs ws
   if (epi == kEpiTopk && (!tko || M != 1 || residual || !topk_fits(pl, N, tko->k))) return kNotFused;
@@ -364,6 +400,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
   p.slice_chunks = pl.slice_chunks;
   p.grid_x = pl.grid_x;
   p.tokens = M;
+  p.sb_segp = pl.sb_segp;
   if (epi == kEpiTopk) {
     p.tk_k = tko->k;
     p.tk_idx = tko->idx;
@@ -392,8 +429,14 @@ int mv_plan_internal(int bits, int fmt, int epi, MvParams* p, bool have_ws, void
                      size_t ws_bytes, size_t ws_offset, int tokens, MvPlan* plan) {
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;
+  bool sb_al = true;
+  auto al16 = [](const void* q) { return ((uintptr_t)q % 16) == 0; };
+  for (int i = 0; i < p->nseg && i < kMaxSeg; ++i)
+    sb_al = sb_al && al16(p->A[i].s) && al16(p->A[i].b) && al16(p->B[i].s) && al16(p->B[i].b);
+  sb_al = sb_al && al16(p->route.all_A.s) && al16(p->route.all_A.b) && al16(p->route.all_B.s) &&
+          al16(p->route.all_B.b);
   const MvPlan pl = plan_mv({p->N, p->K, bits, fmt, epi, p->seg_mode == kSegCols ? p->seg_len : 0,
-                             p->seg_mode}, dev.cus, have_ws);
+                             p->seg_mode, sb_al}, dev.cus, have_ws);
   if (pl.lds_bytes > kLdsBudget) return QG_EWORKSPACE;
   // a batched launch keeps each token's K in one slice (its split-K partials
   // and tickets would need one workspace region per token)
@@ -401,6 +444,7 @@ int mv_plan_internal(int bits, int fmt, int epi, MvParams* p, bool have_ws, void
   p->splits = pl.splits;
   p->slice_chunks = pl.slice_chunks;
   p->grid_x = pl.grid_x;
+  p->sb_segp = pl.sb_segp;
   *plan = pl;
   plan->tokens = tokens;
   p->tokens = tokens;
@@ -578,10 +622,11 @@ int qg_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
 
 // Tuning override for tests and benchmarks: knob 0 = split count, 1 = rows per
 // lane, 2 = lanes per row, 3 = workgroups per CU, 4 = pipeline depth, 5 = 1
-// for the two-launch logits top-k; value 0 restores automatic.
+// for the two-launch logits top-k, 6 = 1 for staged scale/bias rows instead
+// of per-pass loads; value 0 restores automatic.
 int qg_tune(int knob, int value) {
-  if (knob < 0 || knob > 5 || value < 0) return QG_EINVAL;
-  if (knob == 5 && value > 1) return QG_EINVAL;
+  if (knob < 0 || knob > 6 || value < 0) return QG_EINVAL;
+  if ((knob == 5 || knob == 6) && value > 1) return QG_EINVAL;
   if (knob == 4 && value != 0 && value != 2 && value != 4) return QG_EINVAL;
   if (knob == 1 && value != 0 && value != 1 && value != 2) return QG_EINVAL;
   if (knob == 2 && value != 0 && value != 16 && value != 32 && value != 64) return QG_EINVAL;
@@ -669,7 +714,8 @@ int qlogits_topk_noalloc(const qg_qmat* W, int V, int K, int group, int bits, in
                     need, DrawParams{}, stream, &pre);
 }
 
-int qg_logits_topk_launches(int V, int K, int group, int bits, int fmt, int k, int* launches) {
+int qg_logits_topk_launches(const qg_qmat* W, int V, int K, int group, int bits, int fmt, int k,
+                            int* launches) {
   if (!launches) return QG_EINVAL;
   int rc = check_common(V, K, 1, group, bits, fmt, QG_F32);
   if (rc) return rc;
@@ -677,7 +723,7 @@ int qg_logits_topk_launches(int V, int K, int group, int bits, int fmt, int k, i
   if (k > QG_MAX_TOPK) return QG_EUNSUPPORTED;
   const DevInfo dev = device_info();
   if (!dev.ok) return QG_EDEVICE;
-  const MvPlan pl = plan_mv({V, K, bits, fmt, kEpiTopk, 0, kSegNone}, dev.cus, true);
+  const MvPlan pl = plan_mv({V, K, bits, fmt, kEpiTopk, 0, kSegNone, sb_aligned16(W)}, dev.cus, true);
   *launches = (!g_knob[5].load() && topk_fits(pl, V, k)) ? 1 : 2;
   return QG_OK;
 }

@@ -95,6 +95,7 @@ struct MvParams {
   float* partials;    // [splits][n_acc][N] when splits > 1
   uint32_t* tickets;  // [grid_x] zero-initialized when splits > 1
   int tokens;         // vectors served by one launch (0 or 1: one; more: splits == 1)
+  int sb_segp;        // staged scale/bias rows: 16-byte pieces per row segment of the K slice
   // fused top-k (kEpiTopk)
   int tk_k;
   uint64_t* tk_cand;     // [grid_x][kTkList] workgroup lists, then [groups][kTkList] group lists
@@ -111,6 +112,8 @@ struct MvPlan {
   int slice_chunks;
   int grid_x;
   int depth;          // (band, pass) items in flight per wave: 2 or 4
+  int sbl;            // staged scale/bias rows: 0 (per-pass loads), or 16-byte loads per lane and band
+  int sb_segp;        // 16-byte pieces per staged row segment
   size_t lds_bytes;
   int tokens;         // expert launches: tokens in the batch (grid y; 0 or 1 = one)
 };

@@ -467,34 +467,35 @@ __device__ __forceinline__ int seg_rows(const MvParams& p, const int32_t* ids, i
   return p.seg_mode == kSegRows ? p.seg_len : p.N;
 }
 
-template <int R, bool TWO, int LUTN>
+template <int R, bool TWO, int LUTN, int SBL>
 struct PassData {
   u32x4 qa[R];
-  uint16_t sa[R], ba[R];
+  uint16_t sa[R], ba[R];  // this pass's scale/bias (SBL = 0)
   u32x4 qb[TWO ? R : 1];
   uint16_t sb[TWO ? R : 1], bb[TWO ? R : 1];
   uint16_t lut[LUTN > 0 ? LUTN : 1];  // LUT entries of the band, carried by its pass 0
+  u32x4 sbq[SBL > 0 ? SBL : 1];       // the band's scale/bias row pieces, carried by its pass 0
 };
 
 // One pass for the lane's R rows. qoff/soff are the byte offsets of the
 // lane's chunk (codes) and group (scales/biases) in each row for pass 0;
 // dq/ds move them to this pass. ok = false gives zero loads.
-template <int FMT, int R, bool TWO, int LUTN>
+template <int FMT, int R, bool TWO, int LUTN, int SBL>
 __device__ __forceinline__ void load_pass(const MatRsrc& ra, const MatRsrc& rb, const uint32_t* qoff,
                                           const uint32_t* soff, uint32_t dq, uint32_t ds, bool ok,
-                                          PassData<R, TWO, LUTN>& d) {
+                                          PassData<R, TWO, LUTN, SBL>& d) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t oq = ok ? qoff[r] + dq : kOOB;
     const uint32_t os = ok ? soff[r] + ds : kOOB;
     d.qa[r] = __builtin_amdgcn_raw_buffer_load_b128(ra.q, oq, 0, 2);
-    if constexpr (FMT == 0) {
+    if constexpr (FMT == 0 && SBL == 0) {
       d.sa[r] = __builtin_amdgcn_raw_buffer_load_b16(ra.s, os, 0, 0);
       d.ba[r] = __builtin_amdgcn_raw_buffer_load_b16(ra.b, os, 0, 0);
     }
     if constexpr (TWO) {
       d.qb[r] = __builtin_amdgcn_raw_buffer_load_b128(rb.q, oq, 0, 2);
-      if constexpr (FMT == 0) {
+      if constexpr (FMT == 0 && SBL == 0) {
         d.sb[r] = __builtin_amdgcn_raw_buffer_load_b16(rb.s, os, 0, 0);
         d.bb[r] = __builtin_amdgcn_raw_buffer_load_b16(rb.b, os, 0, 0);
       }
@@ -502,11 +503,31 @@ __device__ __forceinline__ void load_pass(const MatRsrc& ra, const MatRsrc& rb, 
   }
 }
 
-template <int BITS, int FMT, int LPR, int R, bool TWO, int LUTN>
-__device__ __forceinline__ void compute_pass(const PassData<R, TWO, LUTN>& d, const u32x4* xl,
+// sbw (SBL > 0): the lane's sub-wave's staged scale/bias row segments,
+// [R][NACC][scales, biases][segh halfwords] (group g of the slice at index
+// g); gsl groups hold this slice's values, a lane past them (a padding chunk,
+// whose codes load as zero) takes scale and bias 0 as the per-pass loads do.
+template <int BITS, int FMT, int LPR, int R, bool TWO, int LUTN, int SBL>
+__device__ __forceinline__ void compute_pass(const PassData<R, TWO, LUTN, SBL>& d, const u32x4* xl,
                                              const ChunkInfo* info, int pass, int j,
-                                             const float* tabs, float* acc_a, float* acc_b) {
+                                             const float* tabs, const uint16_t* sbw, int segh, int gsl,
+                                             float* acc_a, float* acc_b) {
   constexpr int PIECES = Geo<BITS, FMT>::kPieces;
+  // staged scale/bias values first: LDS reads complete in order, so they are
+  // in by the time the dot products over x need them
+  constexpr int NSB = (FMT == 0 && SBL > 0) ? R * (TWO ? 4 : 2) : 1;
+  uint16_t sbv[NSB];
+  uint16_t sbmask = 0;
+  if constexpr (FMT == 0 && SBL > 0) {
+    constexpr int CPG = Geo<BITS, FMT>::kChunksPerGroup;
+    const int gl = (pass * LPR + j) / CPG;
+    sbmask = gl < gsl ? (uint16_t)0xFFFF : (uint16_t)0;
+    const int glc = gl < segh ? gl : segh - 1;  // an address inside the segment either way
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int q = 0; q < (TWO ? 4 : 2); ++q) sbv[r * (TWO ? 4 : 2) + q] = sbw[(r * (TWO ? 4 : 2) + q) * segh + glc];
+  }
   u32x4 xr[PIECES];
   const u32x4* src = xl + pass * PIECES * LPR + j;
 #pragma unroll
@@ -527,16 +548,36 @@ __device__ __forceinline__ void compute_pass(const PassData<R, TWO, LUTN>& d, co
       if constexpr (TWO) acc_b[r] = fmaf(dot_f16w(d.qb[r], xr), back, acc_b[r]);
     }
   } else {
+    constexpr int NACC = TWO ? 2 : 1;
+    uint16_t sa[R], ba[R], sb2[TWO ? R : 1], bb2[TWO ? R : 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if constexpr (SBL > 0) {
+        sa[r] = sbv[r * NACC * 2] & sbmask;
+        ba[r] = sbv[r * NACC * 2 + 1] & sbmask;
+        if constexpr (TWO) {
+          sb2[r] = sbv[r * NACC * 2 + 2] & sbmask;
+          bb2[r] = sbv[r * NACC * 2 + 3] & sbmask;
+        }
+      } else {
+        sa[r] = d.sa[r];
+        ba[r] = d.ba[r];
+        if constexpr (TWO) {
+          sb2[r] = d.sb[r];
+          bb2[r] = d.bb[r];
+        }
+      }
+    }
     const float2 sb = *reinterpret_cast<const float2*>(&info[pass * LPR + j]);  // (xsum, back)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float da = (BITS == 4 ? dot_q4(d.qa[r], xr) : BITS == 8 ? dot_q8(d.qa[r], xr) : dot_q2(d.qa[r], xr)) * sb.y;
-      acc_a[r] = fmaf(f16_bits_to_f32(d.sa[r]), da, acc_a[r]);
-      acc_a[r] = fmaf(f16_bits_to_f32(d.ba[r]), sb.x, acc_a[r]);
+      acc_a[r] = fmaf(f16_bits_to_f32(sa[r]), da, acc_a[r]);
+      acc_a[r] = fmaf(f16_bits_to_f32(ba[r]), sb.x, acc_a[r]);
       if constexpr (TWO) {
         const float db = (BITS == 4 ? dot_q4(d.qb[r], xr) : BITS == 8 ? dot_q8(d.qb[r], xr) : dot_q2(d.qb[r], xr)) * sb.y;
-        acc_b[r] = fmaf(f16_bits_to_f32(d.sb[r]), db, acc_b[r]);
-        acc_b[r] = fmaf(f16_bits_to_f32(d.bb[r]), sb.x, acc_b[r]);
+        acc_b[r] = fmaf(f16_bits_to_f32(sb2[r]), db, acc_b[r]);
+        acc_b[r] = fmaf(f16_bits_to_f32(bb2[r]), sb.x, acc_b[r]);
       }
     }
   }
@@ -565,7 +606,7 @@ __device__ __forceinline__ float lanes_sum(float v) {
 // deep: the first DEPTH items are requested before x is staged, and a slot is
 // refilled with the item DEPTH ahead as soon as it has been consumed, across
 // band boundaries, so the memory queue never drains inside a wave.
-template <int BITS, int FMT, int LPR, int R, int EPI, int SEG, int DEPTH>
+template <int BITS, int FMT, int LPR, int R, int EPI, int SEG, int DEPTH, int SBL>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   constexpr int PIECES = Geo<BITS, FMT>::kPieces;
   constexpr int CPC = Geo<BITS, FMT>::kPerChunk;
@@ -576,7 +617,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   constexpr bool TOPK = (EPI == kEpiTopk);
   constexpr int NACC = TWO ? 2 : 1;
   constexpr int LUTN = (FMT == 1) ? (R * NACC * 16 + LPR - 1) / LPR : 0;
-  typedef PassData<R, TWO, LUTN> PD;
+  typedef PassData<R, TWO, LUTN, SBL> PD;
+  static_assert(SBL == 0 || (FMT == 0 && SEG != kSegCols), "staged scale/bias rows: affine, one K segment");
 
   extern __shared__ u32x4 smem[];
   __shared__ float red[2 * kWaves];
@@ -621,6 +663,33 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   // top-k launch keeps every workgroup: each takes its group's ticket)
   if (!TOPK && tile * kWaves >= nbands) return;
   const int band_stride = p.grid_x * kWaves;
+
+  // Staged scale/bias rows (SBL > 0): the scale and bias row segments over
+  // this K slice of a band's rows, [RPB][NACC][scales, biases][segp pieces of
+  // 16 bytes], come with SBL 16-byte loads per lane carried by the band's
+  // first pass, and go to the wave's LDS area when that pass is computed;
+  // every pass then reads its two values per row from there (instead of two
+  // 2-byte loads per row and matrix per pass). The piece a lane loads is the
+  // same in every band: (row, matrix, array, piece) from its lane number.
+  const int segp = SBL > 0 ? p.sb_segp : 1;
+  const int g0 = c0 / CPG;    // the slice's first group
+  const int gsl = nch / CPG;  // groups in this slice (a multiple of 8 when staged)
+  int sb_t[SBL > 0 ? SBL : 1], sb_a[SBL > 0 ? SBL : 1], sb_m[SBL > 0 ? SBL : 1], sb_rr[SBL > 0 ? SBL : 1];
+  bool sb_in[SBL > 0 ? SBL : 1];
+  const uint16_t* sb_src[SBL > 0 ? SBL : 1];
+  if constexpr (SBL > 0) {
+#pragma unroll
+    for (int i = 0; i < SBL; ++i) {
+      const int P = lane + 64 * i;
+      const int rest = P / segp;
+      sb_t[i] = P - rest * segp;
+      sb_a[i] = rest & 1;
+      sb_m[i] = (rest >> 1) % NACC;
+      sb_rr[i] = (rest >> 1) / NACC;
+      sb_in[i] = P < RPB * NACC * 2 * segp && sb_t[i] * 8 + 8 <= gsl;
+      sb_src[i] = p.A[0].s;
+    }
+  }
 
   // Quarter staging (one quarter unit of x per thread): x and the segment
   // routing weight are requested before the weight prefetch (loads return in
@@ -721,6 +790,29 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
       qoff[r] = ok ? (uint32_t)lr * (uint32_t)p.wpr * 4u + cfirst * 16u : kOOB;
       soff[r] = ok ? (uint32_t)lr * (uint32_t)p.gpr * 2u + (cfirst / CPG) * 2u : kOOB;
     }
+    if constexpr (SBL > 0) {
+      // the band's row matrices; a lane with no piece reads the first 16
+      // bytes of A's scales (always present) and keeps nothing of them
+      QMat ma, mb;
+      int rows_m;
+      if constexpr (SEG == kSegRows) {
+        ma = seg_mat(p, rids, ld_seg, false);
+        mb = TWO ? seg_mat(p, rids, ld_seg, true) : ma;
+        rows_m = seg_rows(p, rids, ld_seg);
+      } else {
+        ma = p.A[0];
+        mb = TWO ? p.B[0] : ma;
+        rows_m = p.N;
+      }
+#pragma unroll
+      for (int i = 0; i < SBL; ++i) {
+        const int n = band * RPB + sb_rr[i];
+        const int lr = (SEG == kSegRows) ? n - ld_seg * p.seg_len : n;
+        const bool ok = sb_in[i] && n < p.N && lr < rows_m;
+        const uint16_t* base = sb_m[i] ? (sb_a[i] ? mb.b : mb.s) : (sb_a[i] ? ma.b : ma.s);
+        sb_src[i] = ok ? base + (size_t)lr * p.gpr + g0 + sb_t[i] * 8 : ma.s;
+      }
+    }
   };
 
   // One request of the pipeline: item (ld_band, ld_pass), or loads that
@@ -732,6 +824,12 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   auto issue = [&](PD& d) {
     const bool have = ld_band < nbands;  // uniform
     if (have && ld_pass == 0) band_setup(ld_band);
+    if constexpr (SBL > 0) {
+      if (have && ld_pass == 0) {
+#pragma unroll
+        for (int i = 0; i < SBL; ++i) d.sbq[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sb_src[i]));
+      }
+    }
     if constexpr (FMT == 1) {
       // a band's tables ride along with its first pass
       const bool first = have && ld_pass == 0;
@@ -755,7 +853,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
       if (s_lo == s_hi) {
         ra = mat_rsrc(seg_mat(p, rids, s_lo, false), seg_rows(p, rids, s_lo), p.wpr, p.gpr);
         const int cl = cg - s_lo * p.seg_len;
-        load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u, (uint32_t)(cl / CPG) * 2u, ok,
+        load_pass<FMT, R, TWO, LUTN, SBL>(ra, rb, qoff, soff, (uint32_t)cl * 16u, (uint32_t)(cl / CPG) * 2u, ok,
                                      d);
       } else {
         // several segments in one pass: one masked load per segment, merged
@@ -769,7 +867,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
           PD t;
           ra = mat_rsrc(seg_mat(p, rids, sg, false), seg_rows(p, rids, sg), p.wpr, p.gpr);
           const int cl = cg - sg * p.seg_len;
-          load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)cl * 16u, (uint32_t)(cl / CPG) * 2u,
+          load_pass<FMT, R, TWO, LUTN, SBL>(ra, rb, qoff, soff, (uint32_t)cl * 16u, (uint32_t)(cl / CPG) * 2u,
                                        ok && mine == sg, t);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
@@ -780,7 +878,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
         }
       }
     } else {
-      load_pass<FMT, R, TWO, LUTN>(ra, rb, qoff, soff, (uint32_t)(ld_pass * LPR) * 16u,
+      load_pass<FMT, R, TWO, LUTN, SBL>(ra, rb, qoff, soff, (uint32_t)(ld_pass * LPR) * 16u,
                                    (uint32_t)(ld_pass * LPR / CPG) * 2u, ok, d);
     }
     if (have && ++ld_pass == npass) {
@@ -796,6 +894,9 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
   ChunkInfo* info = reinterpret_cast<ChunkInfo*>(smem + (size_t)npass * LPR * PIECES);
   float* tabs_all = reinterpret_cast<float*>(info + npass * LPR);  // LUT: [kWaves][SUB][R][2][16]
   float* tabs = tabs_all + (wave * SUB + sub) * R * 2 * 16;
+  // affine formats with staged scale/bias rows: [kWaves][RPB][NACC][2][segp] pieces there instead
+  u32x4* const sbw4 = reinterpret_cast<u32x4*>(info + npass * LPR) + (size_t)wave * RPB * NACC * 2 * segp;
+  const uint16_t* const sbw = reinterpret_cast<const uint16_t*>(sbw4) + (size_t)sub * R * NACC * 2 * segp * 8;
 
   // x first, then the weight prefetch, then the staging arithmetic: the
   // staging then waits for x only while the weights are in flight.
@@ -952,7 +1053,17 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
           wave_sync_lds();
         }
       }
-      compute_pass<BITS, FMT, LPR, R, TWO, LUTN>(d[k], xl, info, cur_pass, j, tabs, acc_a, acc_b);
+      if constexpr (SBL > 0) {
+        if (cur_pass == 0) {  // this band's scale/bias rows into the wave's LDS area
+          wave_sync_lds();
+#pragma unroll
+          for (int i = 0; i < SBL; ++i)
+            if (lane + 64 * i < RPB * NACC * 2 * segp) sbw4[lane + 64 * i] = d[k].sbq[i];
+          wave_sync_lds();
+        }
+      }
+      compute_pass<BITS, FMT, LPR, R, TWO, LUTN, SBL>(d[k], xl, info, cur_pass, j, tabs, sbw, segp * 8, gsl,
+                                                      acc_a, acc_b);
       issue(d[k]);
       if (++cur_pass == npass) {
         finish_band(cur_band);
@@ -1081,47 +1192,65 @@ __global__ void fill_u32_kernel(uint32_t* dst, size_t n, uint32_t v) {
 
 typedef void (*KernelFn)(const MvParams);
 
+// sbl: staged scale/bias rows (affine formats with one K segment; the host
+// asks for them only where the rows are 16-byte aligned and fit).
 template <int BITS, int FMT, int EPI, int SEG, int LPR>
-KernelFn pick_rd(int rows, int depth) {
-  if (rows == 2) return qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 2>;  // two rows: depth 2 only
-  return depth == 4 ? qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 4> : qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 2>;
+KernelFn pick_rd(int rows, int depth, int sbl) {
+  constexpr bool kSb = FMT == 0 && SEG != kSegCols;
+  if (rows == 2) {  // two rows: depth 2 only
+    // (two rows of two matrices stage four row segments: more than two loads
+    // per lane at the K >= 8192 that takes two rows)
+    if constexpr (kSb && EPI != kEpiSwiglu) {
+      if (sbl) return qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 2, 2>;
+    }
+    return qmv_kernel<BITS, FMT, LPR, 2, EPI, SEG, 2, 0>;
+  }
+  if constexpr (kSb) {
+    if (sbl)
+      return depth == 4 ? qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 4, 1> : qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 2, 1>;
+  }
+  return depth == 4 ? qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 4, 0> : qmv_kernel<BITS, FMT, LPR, 1, EPI, SEG, 2, 0>;
 }
 
 template <int BITS, int FMT, int EPI, int SEG>
-KernelFn pick_kernel(int lpr, int rows, int depth) {
-  if (lpr == 64) return pick_rd<BITS, FMT, EPI, SEG, 64>(rows, depth);
-  if (lpr == 32) return pick_rd<BITS, FMT, EPI, SEG, 32>(rows, depth);
-  if (lpr == 16) return pick_rd<BITS, FMT, EPI, SEG, 16>(rows, depth);
+KernelFn pick_kernel(int lpr, int rows, int depth, int sbl) {
+  if (lpr == 64) return pick_rd<BITS, FMT, EPI, SEG, 64>(rows, depth, sbl);
+  if (lpr == 32) return pick_rd<BITS, FMT, EPI, SEG, 32>(rows, depth, sbl);
+  if (lpr == 16) return pick_rd<BITS, FMT, EPI, SEG, 16>(rows, depth, sbl);
   return nullptr;
 }
 
 // the fused top-k: one row per lane slot, pipeline depth 2
 template <int BITS, int FMT, int LPR>
-KernelFn pick_topk(int rows) {
-  return rows == 1 ? qmv_kernel<BITS, FMT, LPR, 1, kEpiTopk, kSegNone, 2> : nullptr;
+KernelFn pick_topk(int rows, int sbl) {
+  if (rows != 1) return nullptr;
+  if constexpr (FMT == 0) {
+    if (sbl) return qmv_kernel<BITS, FMT, LPR, 1, kEpiTopk, kSegNone, 2, 1>;
+  }
+  return qmv_kernel<BITS, FMT, LPR, 1, kEpiTopk, kSegNone, 2, 0>;
 }
 
 template <int BITS, int FMT>
-KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows, int depth) {
+KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows, int depth, int sbl) {
   if (epi == kEpiTopk) {
     if (seg != kSegNone) return nullptr;
-    if (lpr == 64) return pick_topk<BITS, FMT, 64>(rows);
-    if (lpr == 32) return pick_topk<BITS, FMT, 32>(rows);
-    if (lpr == 16) return pick_topk<BITS, FMT, 16>(rows);
+    if (lpr == 64) return pick_topk<BITS, FMT, 64>(rows, sbl);
+    if (lpr == 32) return pick_topk<BITS, FMT, 32>(rows, sbl);
+    if (lpr == 16) return pick_topk<BITS, FMT, 16>(rows, sbl);
     return nullptr;
   }
   if constexpr (FMT != 0) {  // the LUT and dense formats are not gathered by experts
     if (seg != kSegNone) return nullptr;
-    if (epi == kEpiStore) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows, depth);
-    if (epi == kEpiSwiglu) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegNone>(lpr, rows, depth);
+    if (epi == kEpiStore) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows, depth, 0);
+    if (epi == kEpiSwiglu) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegNone>(lpr, rows, depth, 0);
     return nullptr;
   } else {
     if (epi == kEpiStore) {
-      if (seg == kSegNone) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows, depth);
-      if (seg == kSegCols) return pick_kernel<BITS, FMT, kEpiStore, kSegCols>(lpr, rows, depth);
+      if (seg == kSegNone) return pick_kernel<BITS, FMT, kEpiStore, kSegNone>(lpr, rows, depth, sbl);
+      if (seg == kSegCols) return pick_kernel<BITS, FMT, kEpiStore, kSegCols>(lpr, rows, depth, 0);
     } else if (epi == kEpiSwiglu) {
-      if (seg == kSegNone) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegNone>(lpr, rows, depth);
-      if (seg == kSegRows) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegRows>(lpr, rows, depth);
+      if (seg == kSegNone) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegNone>(lpr, rows, depth, sbl);
+      if (seg == kSegRows) return pick_kernel<BITS, FMT, kEpiSwiglu, kSegRows>(lpr, rows, depth, sbl);
     }
     return nullptr;
   }
@@ -1131,12 +1260,14 @@ KernelFn pick_kernel_epi(int epi, int seg, int lpr, int rows, int depth) {
 
 namespace {
 KernelFn select_mv(int bits, int fmt, int epi, int seg, const MvPlan& plan) {
-  if (bits == 4 && fmt == 0) return pick_kernel_epi<4, 0>(epi, seg, plan.lpr, plan.rows, plan.depth);
-  if (bits == 2 && fmt == 0) return pick_kernel_epi<2, 0>(epi, seg, plan.lpr, plan.rows, plan.depth);
-  if (bits == 8 && fmt == 0) return pick_kernel_epi<8, 0>(epi, seg, plan.lpr, plan.rows, plan.depth);
+  const int sbl = plan.sbl;
+  if (bits == 4 && fmt == 0) return pick_kernel_epi<4, 0>(epi, seg, plan.lpr, plan.rows, plan.depth, sbl);
+  if (bits == 2 && fmt == 0) return pick_kernel_epi<2, 0>(epi, seg, plan.lpr, plan.rows, plan.depth, sbl);
+  if (bits == 8 && fmt == 0) return pick_kernel_epi<8, 0>(epi, seg, plan.lpr, plan.rows, plan.depth, sbl);
   if (bits == 16 && fmt == 2 && seg == kSegNone)
-    return pick_kernel_epi<16, 2>(epi, seg, plan.lpr, plan.rows, plan.depth);
-  if (bits == 4 && fmt == 1 && seg == kSegNone) return pick_kernel_epi<4, 1>(epi, seg, plan.lpr, plan.rows, plan.depth);
+    return pick_kernel_epi<16, 2>(epi, seg, plan.lpr, plan.rows, plan.depth, 0);
+  if (bits == 4 && fmt == 1 && seg == kSegNone)
+    return pick_kernel_epi<4, 1>(epi, seg, plan.lpr, plan.rows, plan.depth, 0);
   return nullptr;
 }
 }  // namespace

@@ -154,7 +154,9 @@ int qg_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
  * knob 0 = number of K slices (split-K, needs a workspace), 1 = rows per lane
  * (1 or 2), 2 = lanes per row (16, 32 or 64), 3 = resident workgroups per
  * compute unit, 4 = (band, pass) items in flight per wave (2 or 4), 5 = 1 for
- * the two-launch form of qlogits_topk; value 0 restores the automatic choice.
+ * the two-launch form of qlogits_topk, 6 = 1 for scale/bias rows staged in
+ * LDS once per band (affine formats, 16-byte aligned rows) in place of two
+ * 2-byte loads per pass; value 0 restores the automatic choice.
  * Process-wide; affects calls made after it returns. QG_EINVAL for an unknown
  * knob or value. */
 int qg_tune(int knob, int value);
@@ -242,11 +244,13 @@ int qlogits_topk(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
                  void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* qg_logits_topk_launches -- *launches = the number of kernels (1 or 2) that
- * qlogits_topk and qlogits_topk_noalloc enqueue for this shape on the current
+ * qlogits_topk and qlogits_topk_noalloc enqueue for this head (W may be NULL:
+ * then its scale/bias arrays are taken as 16-byte aligned) on the current
  * device under the current tuning (for profilers and graph budgets; the
  * sampling call always takes 2). Enqueues nothing. Statuses as qlogits_topk;
  * QG_EDEVICE without a usable gfx950. */
-int qg_logits_topk_launches(int V, int K, int group, int bits, int fmt, int k, int *launches);
+int qg_logits_topk_launches(const qg_qmat *W, int V, int K, int group, int bits, int fmt, int k,
+                            int *launches);
 
 /* qlogits_topk_noalloc -- qlogits_topk without a workspace argument, for
  * callers that cannot allocate device memory: code under HIP graph capture,

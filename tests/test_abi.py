@@ -210,8 +210,9 @@ def test_tune_rejects_bad_values(L):
     assert L.qg_tune(0, 17) == qg.QG_EINVAL
     assert L.qg_tune(4, 3) == qg.QG_EINVAL
     assert L.qg_tune(5, 2) == qg.QG_EINVAL
-    assert L.qg_tune(6, 0) == qg.QG_EINVAL
-    for k in range(6):
+    assert L.qg_tune(6, 2) == qg.QG_EINVAL
+    assert L.qg_tune(7, 0) == qg.QG_EINVAL
+    for k in range(7):
         assert L.qg_tune(k, 0) == qg.QG_OK
 
 
@@ -231,12 +232,25 @@ def test_logits_workspace_holds_both_topk_forms(L):
 
 def test_launch_query_checks_arguments(L):
     n = ctypes.c_int(0)
-    assert L.qg_logits_topk_launches(1000, 1024, 64, 4, 0, 40, None) == qg.QG_EINVAL
-    assert L.qg_logits_topk_launches(1000, 1024, 64, 4, 0, 1001, ctypes.byref(n)) == qg.QG_EINVAL
-    assert L.qg_logits_topk_launches(1000, 1024, 64, 4, 0, 0, ctypes.byref(n)) == qg.QG_EINVAL
-    assert L.qg_logits_topk_launches(5000, 1024, 64, 4, 0, 1025, ctypes.byref(n)) == qg.QG_EUNSUPPORTED
-    assert L.qg_logits_topk_launches(1000, 1000, 64, 4, 0, 4, ctypes.byref(n)) == qg.QG_EINVAL
-    assert L.qg_logits_topk_launches(1000, 1024, 32, 4, 0, 4, ctypes.byref(n)) == qg.QG_EUNSUPPORTED
+    assert L.qg_logits_topk_launches(None, 1000, 1024, 64, 4, 0, 40, None) == qg.QG_EINVAL
+    assert L.qg_logits_topk_launches(None, 1000, 1024, 64, 4, 0, 1001, ctypes.byref(n)) == qg.QG_EINVAL
+    assert L.qg_logits_topk_launches(None, 1000, 1024, 64, 4, 0, 0, ctypes.byref(n)) == qg.QG_EINVAL
+    assert L.qg_logits_topk_launches(None, 5000, 1024, 64, 4, 0, 1025, ctypes.byref(n)) == qg.QG_EUNSUPPORTED
+    assert L.qg_logits_topk_launches(None, 1000, 1000, 64, 4, 0, 4, ctypes.byref(n)) == qg.QG_EINVAL
+    assert L.qg_logits_topk_launches(None, 1000, 1024, 32, 4, 0, 4, ctypes.byref(n)) == qg.QG_EUNSUPPORTED
+
+
+def test_phase_probe_checks_arguments(L):
+    p = ctypes.c_void_p(0x10000)
+    assert L.qg_probe_phases(None, 256, p, 1, 0, None, p, None, 4, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 250, p, 1, 0, None, p, None, 4, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 256, p, 0, 0, None, p, None, 4, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 256, p, 1, 2, None, p, None, 4, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 256, p, 1, 0, None, p, None, 0, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 256, p, 1, 0, None, p, None, 4, 0, None) == qg.QG_EINVAL
+    # the barrier needs its flags and error counter
+    assert L.qg_probe_phases(p, 256, p, 1, 1, None, p, p, 4, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 256, p, 1, 1, p, p, None, 4, 16, None) == qg.QG_EINVAL
 
 
 def test_empty_rows_is_a_no_op(L):

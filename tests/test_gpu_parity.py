@@ -31,7 +31,7 @@ def qg():
         pytest.skip("no GPU")
     qg.lib()
     yield qg
-    for k in range(6):
+    for k in range(7):
         qg.qg_tune(k, 0)
 
 
@@ -315,6 +315,78 @@ def test_qlogits_topk(qg, V, K, k, norm, path):
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
     qg.qg_tune(5, 0)
+
+
+@pytest.mark.parametrize("op,N,K,bits,splits", [
+    ("gemv", 4096, 14336, 4, 0), ("swiglu", 14336, 4096, 4, 0), ("rmsnorm", 6144, 4096, 2, 0),
+    ("gemv", 1024, 3072, 4, 0), ("swiglu", 3072, 1024, 4, 0), ("gemv", 4096, 4096, 4, 2),
+    ("gemv", 2048, 4096, 8, 0), ("swiglu", 1000, 2048, 2, 0), ("gemv", 1000, 4160, 4, 0),
+    ("gemv", 3001, 14336, 4, 0)])
+def test_staged_scale_rows_equal_per_pass_loads(qg, op, N, K, bits, splits):
+    """Scale/bias rows staged in LDS per band (knob 6, 16-byte aligned rows)
+    and the per-pass 2-byte loads give the same bits; both are the oracle's
+    result within the bar. Includes two rows per lane (K = 14336), a second
+    K slice starting mid-row, 2- and 8-bit codes and a K whose rows are not
+    16-byte aligned (per-pass loads on both sides)."""
+    say(f"staged scale rows {op} N={N} K={K} bits={bits} splits={splits}")
+    W = synth.qmat(16, ("sbl", op, N, K, bits), N, K, bits)
+    W2 = synth.qmat(16, ("sbl2", op, N, K, bits), N, K, bits) if op == "swiglu" else None
+    g = synth.norm_weight(16, ("sblg", K), K)
+    x = synth.activations(16, ("sblx", K), K, np.float32) * 2.0
+    ws = ws_for(qg, qg.QG_OP_SWIGLU, N, K)
+    Wd, W2d = dev_mat(qg, W), (dev_mat(qg, W2) if W2 is not None else None)
+    xd, gd = to_dev(x), to_dev(g)
+    outs = []
+    qg.qg_tune(0, splits)
+    try:
+        for knob in (0, 1, 0):
+            qg.qg_tune(6, knob)
+            if op == "gemv":
+                outs.append(qg.qgemv(Wd, xd, ws=ws))
+            elif op == "rmsnorm":
+                outs.append(qg.qgemv_rmsnorm(Wd, xd, gd, 1e-5, ws=ws))
+            else:
+                outs.append(qg.qswiglu(Wd, W2d, xd, gd, 1e-5, ws=ws))
+    finally:
+        qg.qg_tune(6, 0)
+        qg.qg_tune(0, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    rows = sample_rows(N, 200, 3)
+    y = outs[0].cpu().numpy()
+    if op == "gemv":
+        ref = oracle.gemv(rows_of(W, rows), x)
+    elif op == "rmsnorm":
+        ref = oracle.rmsnorm_gemv(rows_of(W, rows), x, g, 1e-5)
+    else:
+        ref = oracle.rmsnorm_swiglu(rows_of(W, rows), rows_of(W2, rows), x, g, 1e-5)
+    close(y[rows], ref, what=op)
+
+
+def test_staged_scale_rows_moe_layer(qg):
+    """The MoE layer (routed gate.up with staged rows of the chosen experts
+    and the shared expert) gives the same bits with and without staging."""
+    E, F, H, K = 64, 1024, 4096, 3
+    say("staged scale rows: moe layer")
+    gate, up, down, shared = moe_weights(17, E, F, H)
+    g = synth.norm_weight(17, "g", H)
+    lg = synth.router_logits(17, "route", E)
+    x = synth.activations(17, "x", H, np.float32)
+    Gd, Ud, Dd = (dev_mat(qg, W) for W in (gate, up, down))
+    Sd = tuple(dev_mat(qg, W) for W in shared)
+    ws = qg.workspace(qg.QG_OP_MOE, H, F, 1, 4, 0, K, DEV)
+    ys = []
+    try:
+        for knob in (0, 1):
+            qg.qg_tune(6, knob)
+            ys.append(qg.qmoe_experts(Gd, Ud, Dd, E, Sd, to_dev(lg), K, to_dev(x), to_dev(g), 1e-5,
+                                      ws=ws))
+    finally:
+        qg.qg_tune(6, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    yref, _, _ = oracle.moe_layer(gate, up, down, shared, lg, K, x, g, 1e-5, nthreads=8)
+    close(ys[1].cpu().numpy(), yref, what="moe")
 
 
 def test_topk_launch_count(qg):
