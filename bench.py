@@ -196,7 +196,10 @@ def summarize_trace(path):
     kernel-trace CSV."""
     import csv
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
-    q = [r for r in rows if "qmv_kernel" in r["Kernel_Name"]]
+    # M = 1 runs on qmv_kernel<bits, fmt, lanes, rows, epilogue, ...>, M = 2..8 (4- and 2-bit
+    # codes, tables) on qmm_kernel<bits, fmt, epilogue>
+    mm = not any("qmv_kernel" in r["Kernel_Name"] for r in rows)
+    q = [r for r in rows if ("qmm_kernel" if mm else "qmv_kernel") in r["Kernel_Name"]]
     names = ["qkv: rmsnorm + 6144x4096", "o: 4096x4096 + residual",
              "gate.up: swiglu 2 x 14336x4096", "down: 4096x14336 + residual"]
     # stored bytes per weight from the kernel's (bits, fmt) template arguments
@@ -209,8 +212,9 @@ def summarize_trace(path):
     dur = [[] for _ in names]
     i = 0
     while i + 3 < len(q):
-        # template arguments: bits, fmt, lanes per row, rows, epilogue (1 = SwiGLU), ...
-        swi = [q[i + k]["Kernel_Name"].split("<", 1)[1].split(",")[4].strip() == "1"
+        # the epilogue argument (1 = SwiGLU): fifth of qmv_kernel's, third of qmm_kernel's
+        ep = 2 if mm else 4
+        swi = [q[i + k]["Kernel_Name"].split("<", 1)[1].split(">", 1)[0].split(",")[ep].strip() == "1"
                for k in range(4)]
         if swi != [False, False, True, False]:
             i += 1
@@ -222,6 +226,9 @@ def summarize_trace(path):
     print("|---|---|---|---|---|---|")
     for k, name in enumerate(names):
         v = dur[k]
+        if not v:
+            print(f"| {name} | 0 | - | - | {nbytes[k]} | - |")
+            continue
         avg = sum(v) / len(v) / 1e3
         print(f"| {name} | {len(v)} | {avg:.2f} | {min(v) / 1e3:.2f} | {nbytes[k]} | "
               f"{nbytes[k] / avg / 1e3:.0f} |")
