@@ -325,6 +325,7 @@ struct TopkOut {
   int k;
   int32_t* idx;
   float* vals;
+  DrawParams dp;      // dp.token set: draw one token from the top-k too
   uint32_t* tickets;  // [kTkMaxGroups + 1], zero at rest
   uint64_t* cand;     // [grid_x + groups][kTkList]
 };
@@ -407,6 +408,7 @@ int run_mv(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int group, i
     p.tk_vals = tko->vals;
     p.tk_tickets = tko->tickets;
     p.tk_cand = tko->cand;
+    p.tk_draw = tko->dp;
   }
   if (pl.splits > 1) {
     const size_t tickets = ((size_t)(N + 7) / 8 + 64) * 4;
@@ -483,9 +485,10 @@ int check_logits(int V, int K, int group, int bits, int fmt, int x_dtype, const 
 }
 
 // The logits matvec and its top-k ([F] section 1: both on the GPU, only the
-// chosen entries come back). Without a draw, and where the plan allows it, one
-// launch: the matvec's workgroups merge their rows' keys themselves
-// (kEpiTopk). Otherwise the matvec, then the top-k kernel (which also draws).
+// chosen entries, or the drawn token, come back). Where the plan allows it,
+// one launch: the matvec's workgroups merge their rows' keys themselves and
+// the last merger draws the token (kEpiTopk). Otherwise the matvec, then the
+// top-k kernel (which also draws).
 // ws starts with the top-k region (topk_workspace_bytes), the matvec's follows.
 int run_logits(const qg_qmat* W, int V, int K, int group, int bits, int fmt, const void* x,
                int x_dtype, const uint16_t* norm_w, float eps, float* logits, int k, int32_t* idx,
@@ -493,8 +496,8 @@ int run_logits(const qg_qmat* W, int V, int K, int group, int bits, int fmt, con
                const PreLaunch* pre) {
   const size_t tk = topk_workspace_bytes(V, k);
   char* const base = static_cast<char*>(ws);
-  if (!dp.token && !g_knob[5].load()) {
-    const TopkOut tko{k, idx, vals, reinterpret_cast<uint32_t*>(base + kTkFusedTicketOffset),
+  if (!g_knob[5].load()) {
+    const TopkOut tko{k, idx, vals, dp, reinterpret_cast<uint32_t*>(base + kTkFusedTicketOffset),
                       reinterpret_cast<uint64_t*>(base + kTkTicketBytes)};
     const int rc = run_mv(W, nullptr, V, K, 1, group, bits, fmt, kEpiTopk, x, x_dtype, norm_w, eps,
                           nullptr, logits, base + tk, ws_bytes - tk, stream, pre, &tko);

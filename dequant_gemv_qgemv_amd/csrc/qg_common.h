@@ -453,6 +453,74 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---------------------------------------------------------------------------
+// The draw. The page names the step, not its rule; the reading used:
+// temperature 0 is greedy (the first candidate); otherwise the weights
+// w_i = exp((v_i - v_0) / T) of the k candidates in order (v_0 the largest),
+// the shortest prefix whose weight sum reaches top_p of the total (at least
+// one candidate), and the first candidate whose running sum exceeds u times
+// that prefix sum. u is the top 53 bits of output number `counter` of the
+// SplitMix64 generator started at `seed` (Steele, Lea and Flood, "Fast
+// splittable pseudorandom number generators", OOPSLA 2014: the state advances
+// by the golden-ratio increment and each output is the state through two
+// xor-shift-multiply rounds and a final xor-shift). Double precision; the
+// lanes compute the weights, one lane forms the sums in index order, so the
+// choice is that of a plain sequential evaluation (the device exp may differ
+// from another library's in the last bit, which can only matter when u lands
+// within a few ulps of a boundary).
+
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t counter) {
+  uint64_t z = seed + (counter + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Called by all 64 lanes of one wave. val(i), id(i): candidate i of k
+// (larger first). w: LDS scratch for k doubles. Every call consumes one draw
+// number (also the greedy ones), so a captured graph replayed n times draws
+// n successive numbers.
+template <class Val, class Id>
+__device__ void draw_token(int k, Val val, Id id, const DrawParams& dp, double* w) {
+  const int lane = threadIdx.x & 63;
+  const bool greedy = dp.temperature == 0.f;
+  if (!greedy) {
+    const double T = (double)dp.temperature;
+    const double v0 = (double)val(0);
+    for (int i = lane; i < k; i += 64) w[i] = exp(((double)val(i) - v0) / T);
+  }
+  wave_sync_lds();
+  if (lane == 0) {
+    const uint64_t c = dp.counter ? *dp.counter : 0ull;
+    int pick = 0;
+    if (!greedy) {
+      const double u = (double)(splitmix64_at(dp.seed, c) >> 11) * 0x1.0p-53;
+      double total = 0.0;
+      for (int i = 0; i < k; ++i) total += w[i];
+      const double cut = (double)dp.top_p * total;
+      int m = 0;
+      double prefix = 0.0;
+      while (m < k) {
+        prefix += w[m];
+        ++m;
+        if (prefix >= cut) break;
+      }
+      const double target = u * prefix;
+      double run = 0.0;
+      pick = m - 1;
+      for (int i = 0; i < m; ++i) {
+        run += w[i];
+        if (run > target) {
+          pick = i;
+          break;
+        }
+      }
+    }
+    *dp.token = id(pick);
+    if (dp.counter) *dp.counter = c + 1ull;
+  }
+}
+
 
 }  // namespace
 }  // namespace qg

@@ -70,6 +70,16 @@ struct Routing {
   float* sel_w;
 };
 
+// One token drawn from a sorted top-k list (temperature, top-p, a uniform
+// number from draw `*counter` of SplitMix64 started at `seed`).
+struct DrawParams {
+  float temperature;  // 0: greedy
+  float top_p;        // in (0, 1]
+  uint64_t seed;
+  uint64_t* counter;  // device; read, then advanced by one; nullptr: draw 0
+  int32_t* token;     // device; nullptr: no draw
+};
+
 struct MvParams {
   QMat A[kMaxSeg];
   QMat B[kMaxSeg];
@@ -102,6 +112,7 @@ struct MvParams {
   uint32_t* tk_tickets;  // [kTkMaxGroups + 1], zero between calls
   int32_t* tk_idx;       // [tk_k]
   float* tk_vals;        // [tk_k]
+  DrawParams tk_draw;    // a token drawn from the top-k as well (tk_draw.token set)
 };
 
 // Launch configuration chosen on the host.
@@ -128,16 +139,6 @@ int mv_resident_per_cu(int bits, int fmt, int epi, int seg, const MvPlan& plan);
 hipError_t launch_mm(int bits, int fmt, int epi, const MvPlan& plan, const MvParams& p,
                      hipStream_t stream);
 int mm_slice_codes();
-
-// One token drawn from a sorted top-k list (temperature, top-p, a uniform
-// number from draw `*counter` of SplitMix64 started at `seed`).
-struct DrawParams {
-  float temperature;  // 0: greedy
-  float top_p;        // in (0, 1]
-  uint64_t seed;
-  uint64_t* counter;  // device; read, then advanced by one; nullptr: draw 0
-  int32_t* token;     // device; nullptr: no draw
-};
 
 size_t topk_workspace_bytes(int V, int k);
 // Top-k of logits[V] into idx/vals; with dp.token set, the last workgroup

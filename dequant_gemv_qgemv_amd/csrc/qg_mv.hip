@@ -1152,6 +1152,14 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
         p.tk_vals[lane] = val;
       }
       if (lane == 0) handoff_store(&p.tk_tickets[kTkMaxGroups], 0u);
+      if (p.tk_draw.token) {
+        // and one token drawn from them, as the two-launch form draws it
+        // (tk_keys[0] holds the sorted list, tk_keys[1] is free for the weights)
+        draw_token(
+            p.tk_k, [&](int i) { return key_value(tk_keys[0][i]); },
+            [&](int i) { return (int32_t)key_index(tk_keys[0][i]); }, p.tk_draw,
+            reinterpret_cast<double*>(&tk_keys[1][0]));
+      }
     }
     return;
   }

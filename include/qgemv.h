@@ -246,8 +246,8 @@ int qlogits_topk(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
 /* qg_logits_topk_launches -- *launches = the number of kernels (1 or 2) that
  * qlogits_topk and qlogits_topk_noalloc enqueue for this head (W may be NULL:
  * then its scale/bias arrays are taken as 16-byte aligned) on the current
- * device under the current tuning (for profilers and graph budgets; the
- * sampling call always takes 2). Enqueues nothing. Statuses as qlogits_topk;
+ * device under the current tuning (for profilers and graph budgets;
+ * qlogits_sample takes the same number). Enqueues nothing. Statuses as qlogits_topk;
  * QG_EDEVICE without a usable gfx950. */
 int qg_logits_topk_launches(const qg_qmat *W, int V, int K, int group, int bits, int fmt, int k,
                             int *launches);
@@ -259,7 +259,7 @@ int qg_logits_topk_launches(const qg_qmat *W, int V, int K, int group, int bits,
  * memory (top-k candidates, split-K partials and tickets) is a
  * library-held device array of 24 MiB per GPU, kept until the process ends;
  * a call whose workspace need (qg_workspace_bytes(QG_OP_LOGITS_TOPK, V, K, 1,
- * bits, fmt, k)) exceeds it returns QG_EUNSUPPORTED (this is about V <= 390000
+ * bits, fmt, k)) exceeds it returns QG_EUNSUPPORTED (this is V <= 385828
  * for k = 40). The call itself allocates and frees nothing; its first call on
  * a device clears the array with a fill kernel on `stream`, ahead of its own
  * kernels. Every call on one GPU shares that GPU's array and leaves it ready
@@ -290,8 +290,8 @@ int qlogits_topk_noalloc(const qg_qmat *W, int V, int K, int group, int bits, in
  * QG_EINVAL for an argument outside these ranges. */
 
 /* qlogits_sample -- qlogits_topk (same arguments, workspace and results)
- * followed by the draw from its k candidates, in the same launch as the
- * top-k. */
+ * followed by the draw from its k candidates, in the launch that finishes the
+ * top-k (the matvec's own launch where qlogits_topk takes one). */
 int qlogits_sample(const qg_qmat *W, int V, int K, int group, int bits, int fmt,
                    const void *x, int x_dtype, const uint16_t *norm_w, float eps,
                    float *logits, int k, int32_t *idx, float *vals,

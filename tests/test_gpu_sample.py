@@ -35,6 +35,7 @@ def qg():
         pytest.skip("no GPU")
     qg.lib()
     yield qg
+    qg.qg_tune(5, 0)
 
 
 def say(msg):
@@ -91,10 +92,16 @@ def test_sample_without_counter_uses_draw_zero(qg):
     assert toks == oracle_tokens(vals, idx, 1.0, 1.0, 42, [0, 0, 0])
 
 
+@pytest.mark.parametrize("path", ["one_launch", "two_launch"])
 @pytest.mark.parametrize("V,K,k,T,top_p", [(151936, 1024, 40, 0.8, 0.95), (5000, 256, 1, 1.0, 1.0),
-                                            (9000, 64, 1024, 1.0, 1.0), (777, 128, 40, 0.0, 1.0)])
-def test_qlogits_sample_matches_topk_and_oracle(qg, V, K, k, T, top_p):
-    say(f"qlogits_sample V={V} K={K} k={k} T={T} top_p={top_p}")
+                                            (9000, 64, 1024, 1.0, 1.0), (777, 128, 40, 0.0, 1.0),
+                                            (32000, 4096, 64, 1.3, 0.7)])
+def test_qlogits_sample_matches_topk_and_oracle(qg, V, K, k, T, top_p, path):
+    """The draw in the launch that finishes the top-k: the matvec's own (one
+    launch, k <= 64) or the separate top-k kernel (knob 5, and k > 64); the
+    tokens are the oracle's draws from the GPU's top-k, draw by draw."""
+    say(f"qlogits_sample V={V} K={K} k={k} T={T} top_p={top_p} {path}")
+    qg.qg_tune(5, 1 if path == "two_launch" else 0)
     W = qg.QMat.from_host(synth.qmat(21, ("lm", V, K), V, K, 4), DEV)
     g = torch.from_numpy(synth.norm_weight(21, "gf", K)).to(DEV)
     x = torch.from_numpy(synth.activations(21, "x", K, np.float32) * 5.0).to(DEV)
@@ -110,6 +117,7 @@ def test_qlogits_sample_matches_topk_and_oracle(qg, V, K, k, T, top_p):
         torch.cuda.synchronize()
         assert torch.equal(z, z_ref) and torch.equal(idx, idx_ref) and torch.equal(vals, vals_ref)
         toks.append(int(tok.item()))
+    qg.qg_tune(5, 0)
     assert int(counter.item()) == start + n
     assert toks == oracle_tokens(vals_ref.cpu().numpy(), idx_ref.cpu().numpy(), T, top_p, seed,
                                  range(start, start + n))
