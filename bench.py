@@ -421,11 +421,9 @@ def emit(args, workload, cfg, step_bytes, ms, dom, peaks, cpu, dtype):
 
 
 def arith_dtype(bits, fmt, m):
-    """The arithmetic the path computes in: affine and dense weights as fp16
-    x fp16 products (codes are exact fp16 values; x is staged in fp16 after a
-    power-of-two range scale) accumulated in fp32; table weights in fp32."""
-    if fmt == 1 and m == 1:
-        return "f32 (fp16 table entries x fp32 x, fp32 accumulate)"
+    """The arithmetic the path computes in: fp16 x fp16 products (codes are
+    exact fp16 values, table entries are fp16, x is staged in fp16 after a
+    power-of-two range scale) accumulated in fp32."""
     core = "mfma f16xf16->f32" if (m > 1 and bits in (2, 4)) else "f16xf16->f32"
     return f"{core} (x staged in fp16 after a power-of-two scale, fp32 accumulate)"
 

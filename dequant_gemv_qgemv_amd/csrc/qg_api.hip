@@ -110,7 +110,7 @@ int codes_per_chunk(int bits) { return 128 / bits; }
 // 16-byte pieces of staged x per chunk: fp16 pairs for the affine and dense
 // formats, fp32 for the LUT format.
 int pieces_per_chunk(int bits, int fmt) {
-  if (fmt == QG_LUT) return 8;
+  if (fmt == QG_LUT) return 4;
   return bits == 16 ? 1 : bits == 8 ? 2 : bits == 4 ? 4 : 8;
 }
 
@@ -172,11 +172,20 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
                 : (s.bits == 4 && s.fmt == QG_AFFINE && s.seg == kSegNone && s.K >= 8192 ? 2 : 1);
   if (s.epi == kEpiTopk) pl.rows = 1;  // the fused top-k keeps one row per lane slot
   pl.depth = g_knob[4].load() ? g_knob[4].load() : 2;
+  const int nacc = s.epi == kEpiSwiglu ? 2 : 1;
+  if (s.fmt == QG_LUT) {
+    // the table format keeps a 1 KB pair table per row in flight: wider rows
+    // (fewer rows per band) where the tables would take more than three
+    // quarters of the LDS budget (the rest stages x)
+    while (pl.lpr < 64 &&
+           (size_t)kWaves * (64 / pl.lpr) * pl.rows * nacc * kLutRowWords * 4 > kLdsBudget * 3 / 4)
+      pl.lpr *= 2;
+  }
   const int rpb = (64 / pl.lpr) * pl.rows;
   const int nbands = (s.N + rpb - 1) / rpb;
   const int tiles = (nbands + kWaves - 1) / kWaves;
   const size_t per_chunk = (size_t)pieces_per_chunk(s.bits, s.fmt) * 16 + 16;  // + ChunkInfo
-  const size_t lut_bytes = (s.fmt == QG_LUT) ? (size_t)kWaves * rpb * 2 * 16 * 4 : 0;
+  const size_t lut_bytes = (s.fmt == QG_LUT) ? (size_t)kWaves * rpb * nacc * kLutRowWords * 4 : 0;
   int max_chunks = (int)((kLdsBudget - lut_bytes) / per_chunk);
   max_chunks = (max_chunks / pl.lpr) * pl.lpr;
   const int passes = (C + pl.lpr - 1) / pl.lpr;
@@ -210,7 +219,6 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
     const int cpg = 64 / codes_per_chunk(s.bits);
     const int gpr = s.K / 64;
     const int gsl = (pl.slice_chunks < C ? pl.slice_chunks : C) / cpg;  // groups per slice
-    const int nacc = s.epi == kEpiSwiglu ? 2 : 1;
     const int want = pl.rows == 2 ? 2 : 1;  // loads per lane and band the kernels provide
     if ((gpr * 2) % 16 == 0 && (gsl * 2) % 16 == 0 && pl.slice_chunks % cpg == 0) {
       const int segp = gsl * 2 / 16;

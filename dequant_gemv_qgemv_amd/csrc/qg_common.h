@@ -33,8 +33,8 @@ struct Geo<2, 0> {  // 64 codes; x as 32 fp16 pairs = 8 pieces
   static constexpr int kPerChunk = 64, kPieces = 8, kChunksPerGroup = 1;
 };
 template <>
-struct Geo<4, 1> {  // LUT: 32 codes; x as 32 fp32 = 8 pieces
-  static constexpr int kPerChunk = 32, kPieces = 8, kChunksPerGroup = 2;
+struct Geo<4, 1> {  // LUT: 32 codes; x as 16 fp16 pairs in natural order = 4 pieces
+  static constexpr int kPerChunk = 32, kPieces = 4, kChunksPerGroup = 2;
 };
 template <>
 struct Geo<8, 0> {  // 16 codes; x as 8 fp16 pairs = 2 pieces
@@ -52,14 +52,18 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 }
 
 // Writes the staged pieces of one chunk: v holds the chunk's x already
-// multiplied by the range scale (affine) or as is (LUT).
+// multiplied by the range scale.
 template <int BITS, int FMT>
 __device__ __forceinline__ void write_pieces(const float* v, u32x4* dst, int stride) {
   if constexpr (FMT == 1) {
+    // table format: piece p holds the pairs (x[8p+2b], x[8p+2b+1]), b = 0..3,
+    // matching byte b of code word p (codes 2b and 2b+1)
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-      dst[p * stride] = u32x4{__float_as_uint(v[4 * p]), __float_as_uint(v[4 * p + 1]),
-                              __float_as_uint(v[4 * p + 2]), __float_as_uint(v[4 * p + 3])};
+    for (int p = 0; p < 4; ++p) {
+      const float* w = v + 8 * p;
+      dst[p * stride] = u32x4{pack_f16(w[0], w[1]), pack_f16(w[2], w[3]), pack_f16(w[4], w[5]),
+                              pack_f16(w[6], w[7])};
+    }
   } else if constexpr (FMT == 2) {
     // dense fp16: word i holds weights (2i, 2i+1)
     dst[0] = u32x4{pack_f16(v[0], v[1]), pack_f16(v[2], v[3]), pack_f16(v[4], v[5]),

@@ -32,6 +32,11 @@ enum Epi : int {
 // and keeps its 64 largest; groups of kTkGroup workgroups and then the groups
 // are merged by the last to finish (integer tickets). Limits of the fused
 // form (the host falls back to a separate top-k launch beyond them).
+// Table format: per row in flight, a table of the 256 code pairs (lut[lo],
+// lut[hi]) as fp16 pairs (indexed by the byte of a code word holding two
+// codes) plus the row's 16 entries it is built from.
+constexpr int kLutPairWords = 256;
+constexpr int kLutRowWords = kLutPairWords + 8;  // + 16 fp16 entries
 constexpr int kTkList = 64;       // keys per list (k <= kTkList)
 constexpr int kTkGroup = 16;      // workgroups per first-level group (the last may be short)
 constexpr int kTkMaxGroups = 32;  // so at most 512 workgroups

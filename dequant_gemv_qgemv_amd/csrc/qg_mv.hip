@@ -37,7 +37,9 @@
 // multiplied by 16 (mask 0x00F000F0) and 2-bit fields by 4^j; their x is
 // pre-divided by that power of two when staged. x is staged in fp16 after an
 // exact power-of-two range scale 2^-e chosen from max|x| over the slice; the
-// chunk result is multiplied back by 2^(24+e). The LUT format keeps x in fp32.
+// chunk result is multiplied back by 2^(24+e). The table format stages x the
+// same way, as natural-order fp16 pairs that meet the row's table of code
+// pairs (lut[lo], lut[hi]) in v_dot2_f32_f16.
 #include <mutex>
 #include <type_traits>
 #include <unordered_map>
@@ -117,22 +119,22 @@ __device__ __forceinline__ float dot_f16w(const u32x4 q, const u32x4* xr) {
   return a0 + a1;
 }
 
-// LUT (4-bit codes, 16-entry table per row, held in this wave's LDS slot):
-// sum_k lut[code_k] x_k over the chunk's 32 codes (x in natural order, fp32).
-__device__ __forceinline__ float dot_lut(const u32x4 q, const u32x4* xr, const float* tab) {
+// LUT (4-bit codes, 16-entry table per row): sum_k lut[code_k] x_k over the
+// chunk's 32 codes, two codes per step. Byte b of code word i holds codes
+// 2b (low nibble) and 2b + 1; as an index into the row's table of the 256
+// pairs (lut[lo], lut[hi]) (fp16, in the sub-wave's LDS slot) it gives both
+// weights at once, and v_dot2_f32_f16 takes them with the fp16 pair
+// (x[8i+2b], x[8i+2b+1]) staged in piece i.
+__device__ __forceinline__ float dot_lut(const u32x4 q, const u32x4* xr, const uint32_t* ptab) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4 u = xr[2 * i], v = xr[2 * i + 1];
-    a0 = fmaf(tab[(w[i] >> 0) & 15u], __uint_as_float(u.x), a0);
-    a1 = fmaf(tab[(w[i] >> 4) & 15u], __uint_as_float(u.y), a1);
-    a0 = fmaf(tab[(w[i] >> 8) & 15u], __uint_as_float(u.z), a0);
-    a1 = fmaf(tab[(w[i] >> 12) & 15u], __uint_as_float(u.w), a1);
-    a0 = fmaf(tab[(w[i] >> 16) & 15u], __uint_as_float(v.x), a0);
-    a1 = fmaf(tab[(w[i] >> 20) & 15u], __uint_as_float(v.y), a1);
-    a0 = fmaf(tab[(w[i] >> 24) & 15u], __uint_as_float(v.z), a0);
-    a1 = fmaf(tab[(w[i] >> 28) & 15u], __uint_as_float(v.w), a1);
+    const u32x4 u = xr[i];
+    a0 = dot2(ptab[w[i] & 0xFFu], u.x, a0);
+    a1 = dot2(ptab[(w[i] >> 8) & 0xFFu], u.y, a1);
+    a0 = dot2(ptab[(w[i] >> 16) & 0xFFu], u.z, a0);
+    a1 = dot2(ptab[w[i] >> 24], u.w, a1);
   }
   return a0 + a1;
 }
@@ -236,7 +238,7 @@ __device__ __forceinline__ float stage_chunk(const MvParams& p, const float* rw,
     m = fmaxf(m, fabsf(v[i]));
   }
   float back = 1.0f;
-  if constexpr (FMT != 1) {  // x staged in fp16 (affine codes, dense fp16 weights)
+  {  // x staged in fp16 (every format)
     const float inv = range_scale(m, &back);
 #pragma unroll
     for (int i = 0; i < CPC; ++i) v[i] *= inv;
@@ -318,11 +320,9 @@ __device__ __forceinline__ float quarter_seg_weight(const MvParams& p, const flo
 // affine formats): the same pieces write_pieces produces for those values.
 template <int BITS, int FMT>
 __device__ __forceinline__ void write_quarter(const float* w, u32x4* dst, int stride, int q) {
-  if constexpr (FMT == 1) {
-    dst[(2 * q) * stride] = u32x4{__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]),
-                                  __float_as_uint(w[3])};
-    dst[(2 * q + 1) * stride] = u32x4{__float_as_uint(w[4]), __float_as_uint(w[5]), __float_as_uint(w[6]),
-                                      __float_as_uint(w[7])};
+  if constexpr (FMT == 1) {  // natural-order fp16 pairs of code word q
+    dst[q * stride] = u32x4{pack_f16(w[0], w[1]), pack_f16(w[2], w[3]), pack_f16(w[4], w[5]),
+                            pack_f16(w[6], w[7])};
   } else if constexpr (BITS == 4) {
     constexpr float r16 = 1.0f / 16.0f;
     dst[q * stride] = u32x4{pack_f16(w[0], w[4]), pack_f16(w[1] * r16, w[5] * r16), pack_f16(w[2], w[6]),
@@ -405,7 +405,7 @@ __device__ __forceinline__ float stage_quarter(const MvParams& p, const u32x4* x
   s = quad_sum(s);
   m = quad_max(m);
   float back = 1.0f;
-  if constexpr (FMT != 1) {
+  {
     const float inv = range_scale(m, &back);
 #pragma unroll
     for (int i = 0; i < QV; ++i) v[i] *= inv;
@@ -510,7 +510,7 @@ __device__ __forceinline__ void load_pass(const MatRsrc& ra, const MatRsrc& rb, 
 template <int BITS, int FMT, int LPR, int R, bool TWO, int LUTN, int SBL>
 __device__ __forceinline__ void compute_pass(const PassData<R, TWO, LUTN, SBL>& d, const u32x4* xl,
                                              const ChunkInfo* info, int pass, int j,
-                                             const float* tabs, const uint16_t* sbw, int segh, int gsl,
+                                             const uint32_t* ptab, const uint16_t* sbw, int segh, int gsl,
                                              float* acc_a, float* acc_b) {
   constexpr int PIECES = Geo<BITS, FMT>::kPieces;
   // staged scale/bias values first: LDS reads complete in order, so they are
@@ -533,10 +533,15 @@ __device__ __forceinline__ void compute_pass(const PassData<R, TWO, LUTN, SBL>& 
 #pragma unroll
   for (int i = 0; i < PIECES; ++i) xr[i] = src[i * LPR];
   if constexpr (FMT == 1) {
+    // x was staged in fp16 after the chunk's range scale: the back factor
+    // carries 2^24 for the codes' subnormal scale, which table weights lack
+    constexpr int NACC = TWO ? 2 : 1;
+    const float back = info[pass * LPR + j].back * 0x1p-24f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      acc_a[r] += dot_lut(d.qa[r], xr, tabs + (2 * r) * 16);
-      if constexpr (TWO) acc_b[r] += dot_lut(d.qb[r], xr, tabs + (2 * r + 1) * 16);
+      acc_a[r] = fmaf(dot_lut(d.qa[r], xr, ptab + (r * NACC) * kLutPairWords), back, acc_a[r]);
+      if constexpr (TWO)
+        acc_b[r] = fmaf(dot_lut(d.qb[r], xr, ptab + (r * NACC + 1) * kLutPairWords), back, acc_b[r]);
     }
   } else if constexpr (FMT == 2) {
     // dense fp16 weights: the chunk's back factor carries 2^24 for the codes'
@@ -892,8 +897,10 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
 
   u32x4* xl = smem;
   ChunkInfo* info = reinterpret_cast<ChunkInfo*>(smem + (size_t)npass * LPR * PIECES);
-  float* tabs_all = reinterpret_cast<float*>(info + npass * LPR);  // LUT: [kWaves][SUB][R][2][16]
-  float* tabs = tabs_all + (wave * SUB + sub) * R * 2 * 16;
+  // table format: per sub-wave, [R][NACC] pair tables of kLutPairWords words,
+  // then the [R][NACC][16] fp16 entries they are built from
+  uint32_t* const ptab = reinterpret_cast<uint32_t*>(info + npass * LPR) + (size_t)(wave * SUB + sub) * R * NACC * kLutRowWords;
+  uint16_t* const l16 = reinterpret_cast<uint16_t*>(ptab + R * NACC * kLutPairWords);
   // affine formats with staged scale/bias rows: [kWaves][RPB][NACC][2][segp] pieces there instead
   u32x4* const sbw4 = reinterpret_cast<u32x4*>(info + npass * LPR) + (size_t)wave * RPB * NACC * 2 * segp;
   const uint16_t* const sbw = reinterpret_cast<const uint16_t*>(sbw4) + (size_t)sub * R * NACC * 2 * segp * 8;
@@ -1044,11 +1051,20 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
           wave_sync_lds();
 #pragma unroll
           for (int q = 0; q < LUTN; ++q) {
-            const int e = j + q * LPR;
-            if (e < R * NACC * 16) {
-              const int r = e / (NACC * 16), m = (e / 16) % NACC, t = e % 16;
-              tabs[(2 * r + m) * 16 + t] = f16_bits_to_f32(d[k].lut[q]);
-            }
+            const int e = j + q * LPR;  // entry t of table (r, m) at (r * NACC + m) * 16 + t
+            if (e < R * NACC * 16) l16[e] = d[k].lut[q];
+          }
+          wave_sync_lds();
+          // the pair tables: slot s of a table (64 per table) writes the four
+          // pairs (lut[4(s&3) + i], lut[s>>2]), i = 0..3, at 16 (s>>2) + 4 (s&3)
+#pragma unroll
+          for (int s2 = j; s2 < R * NACC * 64; s2 += LPR) {
+            const int tb = s2 >> 6, sl = s2 & 63;
+            const uint16_t* L = l16 + tb * 16;
+            const uint32_t hi = (uint32_t)L[sl >> 2] << 16;
+            const int lo4 = 4 * (sl & 3);
+            *reinterpret_cast<u32x4*>(ptab + tb * kLutPairWords + (sl >> 2) * 16 + lo4) =
+                u32x4{L[lo4] | hi, L[lo4 + 1] | hi, L[lo4 + 2] | hi, L[lo4 + 3] | hi};
           }
           wave_sync_lds();
         }
@@ -1062,7 +1078,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(const MvParams p) {
           wave_sync_lds();
         }
       }
-      compute_pass<BITS, FMT, LPR, R, TWO, LUTN, SBL>(d[k], xl, info, cur_pass, j, tabs, sbw, segp * 8, gsl,
+      compute_pass<BITS, FMT, LPR, R, TWO, LUTN, SBL>(d[k], xl, info, cur_pass, j, ptab, sbw, segp * 8, gsl,
                                                       acc_a, acc_b);
       issue(d[k]);
       if (++cur_pass == npass) {
