@@ -389,6 +389,66 @@ def test_staged_scale_rows_moe_layer(qg):
     close(ys[1].cpu().numpy(), yref, what="moe")
 
 
+def test_handoff_under_alternating_inputs(qg):
+    """The hand-off between workgroups of one launch (split-K partials and
+    their tickets; the one-launch top-k's lists, tickets and logit reloads)
+    uses agent-coherent stores and loads and relaxed integer tickets. Two
+    inputs alternate over 48 calls replayed from a graph: the partials, lists
+    and tickets sit at the same workspace addresses in every call, so a read
+    that saw the previous call's data instead of its own would change that
+    call's result. Every call must give the same bits as the first call on
+    its input."""
+    say("hand-off stress: split-K and one-launch top-k, alternating inputs")
+    N, K = 4096, 16384
+    W = dev_mat(qg, synth.qmat(18, "handoff", N, K, 4))
+    xs = [to_dev(synth.activations(18, ("hox", i), K, np.float32)) for i in range(2)]
+    ws = ws_for(qg, qg.QG_OP_SWIGLU, N, K)
+    V, KH, k = 151936, 1024, 40
+    H = dev_mat(qg, synth.qmat(18, "handoff_head", V, KH, 4))
+    hx = [to_dev(synth.activations(18, ("hhx", i), KH, np.float32) * 4.0) for i in range(2)]
+    wsh = qg.workspace(qg.QG_OP_LOGITS_TOPK, V, KH, 1, 4, 0, k, DEV)
+    n = 48
+    ys = [torch.empty(N, dtype=torch.float32, device=DEV) for _ in range(n)]
+    zs = [torch.empty(V, dtype=torch.float32, device=DEV) for _ in range(n)]
+    ids = [torch.empty(k, dtype=torch.int32, device=DEV) for _ in range(n)]
+    vs = [torch.empty(k, dtype=torch.float32, device=DEV) for _ in range(n)]
+    try:
+        def calls():
+            for i in range(n):
+                qg.qg_tune(0, 4)  # the matvec in four K slices (planned at the call)
+                qg.qgemv(W, xs[i % 2], y=ys[i], ws=ws)
+                qg.qg_tune(0, 0)  # the head in one launch
+                qg.qlogits_topk(H, hx[i % 2], k, logits=zs[i], idx=ids[i], vals=vs[i], ws=wsh)
+        calls()
+        torch.cuda.synchronize()
+        refs = [(ys[j].clone(), ids[j].clone(), vs[j].clone(), zs[j].clone()) for j in range(2)]
+        for i in range(n):
+            r = refs[i % 2]
+            assert torch.equal(ys[i], r[0]) and torch.equal(ids[i], r[1]) and torch.equal(vs[i], r[2])
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            calls()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        for rep in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            for i in range(n):
+                r = refs[i % 2]
+                assert torch.equal(ys[i], r[0]), f"replay {rep} call {i}: split-K result"
+                assert torch.equal(ids[i], r[1]) and torch.equal(vs[i], r[2]), f"replay {rep} call {i}: top-k"
+                assert torch.equal(zs[i], r[3]), f"replay {rep} call {i}: logits"
+    finally:
+        qg.qg_tune(0, 0)
+    assert not torch.equal(refs[0][0], refs[1][0]) and not torch.equal(refs[0][1], refs[1][1])
+    ridx, _ = oracle.topk(refs[0][3].cpu().numpy(), k)
+    assert np.array_equal(refs[0][1].cpu().numpy(), ridx)
+    assert qg.qg_logits_topk_launches(V, KH, k, W=H) == 1
+
+
 def test_topk_launch_count(qg):
     """One launch for the Qwen-shaped head at k <= 64, two past 64 keys, for
     more rows per wave than a key list holds, and under knob 5."""
