@@ -979,6 +979,15 @@ def run_attn(args, qg, synth, dev):
          cfg, layer_bytes * L, ms, dom, peaks, cpu, "f16 cache x f32 query, f32 accumulate")
 
 
+def tune_arg(text):
+    """KNOB=VALUE with small non-negative integers (checked again by qg_tune)."""
+    import argparse
+    parts = text.split("=")
+    if len(parts) != 2 or not all(p.strip().isdigit() for p in parts) or int(parts[0]) > 15:
+        raise argparse.ArgumentTypeError(f"--tune expects KNOB=VALUE (integers), got {text!r}")
+    return f"{int(parts[0])}={int(parts[1])}"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -997,7 +1006,7 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
-    ap.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE",
+    ap.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE", type=tune_arg,
                     help="qg_tune override applied before the run (repeatable), e.g. 6=1 for staged "
                          "scale/bias rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")

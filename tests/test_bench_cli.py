@@ -20,6 +20,9 @@ def run(*args):
     (["--fmt", "2"], "--bits 16 --fmt 2"),
     (["--fmt", "1", "--bits", "2"], "4-bit codes"),
     (["--m", "9"], "--m must be 1..8"),
+    (["--tune", "6"], "KNOB=VALUE"),
+    (["--tune", "a=1"], "KNOB=VALUE"),
+    (["--config", "nope"], "invalid choice"),
 ])
 def test_rejected_before_any_gpu_work(args, needle):
     r = run(*args)
