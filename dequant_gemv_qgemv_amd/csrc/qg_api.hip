@@ -247,10 +247,14 @@ MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
   return pl;
 }
 
+// Tickets, then the fp32 partials of every slice; several vectors (the
+// matrix-core kernels) add each slice's per-vector sums of squares.
+constexpr size_t kMmSsqBytes = (size_t)kMaxSplits * 8 * 4;
 size_t mv_ws_bytes(int N, int M, int epi) {
   const size_t tickets = ((size_t)(N + 7) / 8 + 64) * 4;
   const size_t tickets_al = (tickets + 255) / 256 * 256;
-  return tickets_al + (size_t)kMaxSplits * (epi == kEpiSwiglu ? 2 : 1) * M * N * 4;
+  return tickets_al + (size_t)kMaxSplits * (epi == kEpiSwiglu ? 2 : 1) * M * N * 4 +
+         (M > 1 ? kMmSsqBytes : 0);
 }
 
 // Work to enqueue right before a call's first kernel, once every check has
@@ -278,7 +282,8 @@ int check_mm(const qg_qmat* A, const qg_qmat* B, int K, int fmt) {
 
 // M = 2..8: matrix-core kernels. K is cut into slices of mm_slice_codes()
 // codes (one workgroup each per band set); more than one slice needs the
-// workspace for the fp32 partials.
+// workspace for the fp32 partials (and, with a norm, each slice's sums of
+// squares).
 int run_mm(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int bits, int fmt, int epi,
            const void* x, int x_dtype, const uint16_t* norm_w, float eps, const float* residual,
            float* y, void* ws, bool have_ws, int cus, hipStream_t stream, const PreLaunch* pre) {
@@ -320,8 +325,10 @@ int run_mm(const qg_qmat* A, const qg_qmat* B, int N, int K, int M, int bits, in
   if (splits > 1) {
     const size_t tickets = ((size_t)(N + 7) / 8 + 64) * 4;
     const size_t tickets_al = (tickets + 255) / 256 * 256;
+    const size_t partial_bytes = (size_t)kMaxSplits * (epi == kEpiSwiglu ? 2 : 1) * M * N * 4;
     p.tickets = static_cast<uint32_t*>(ws);
     p.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + tickets_al);
+    p.mm_ssq = reinterpret_cast<float*>(static_cast<char*>(ws) + tickets_al + partial_bytes);
   }
   const hipError_t e = launch_mm(bits, fmt, epi, pl, p, stream);
   return e == hipSuccess ? QG_OK : QG_ELAUNCH;

@@ -111,6 +111,7 @@ struct MvParams {
   uint32_t* tickets;  // [grid_x] zero-initialized when splits > 1
   int tokens;         // vectors served by one launch (0 or 1: one; more: splits == 1)
   int sb_segp;        // staged scale/bias rows: 16-byte pieces per row segment of the K slice
+  float* mm_ssq;      // M = 2..8 kernels: [splits][8] per-slice sums of squares per vector (norm, splits > 1)
   // fused top-k (kEpiTopk)
   int tk_k;
   uint64_t* tk_cand;     // [grid_x][kTkList] workgroup lists, then [groups][kTkList] group lists

@@ -226,9 +226,9 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
   constexpr int DB = (BITS == 2 && !LUT ? 4 : 2) / NACC;
 
   __shared__ float red[2][NACC][kWaves][kTok][kBand];
-  __shared__ float ssq[kWaves][kTok];
-  __shared__ float bk[kWaves][kTok];
-  __shared__ float xsq[kWaves][kTok][kGW];       // group sums of x per token
+  __shared__ float ssq[kWaves][kTok];            // per wave range: sum of squares per token
+  __shared__ float bk[kWaves][kTok];             // per wave range: back scale per token
+  __shared__ float xsq[kWaves][kTok][kGW];       // per wave range: group sums of x per token
   __shared__ u32x4 xst[kWaves][8 * 4 * kTok];    // staged pieces, half a range
   __shared__ uint16_t luts[LUT ? kWaves : 1][kBand * kLutStride];
   __shared__ int last_flag;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
   const int M = p.M;
   const int C = p.K / CODES;
   const int cw0 = (slice * kWaves + wave) * KW;  // first chunk of this wave's range
-  const int gw0 = cw0 / CPG;                     // first group of this wave's range
+  const int gw0 = cw0 / CPG;                   // first group of this wave's range
   const bool norm = p.norm_w != nullptr;
 
   QMat mats[2] = {p.A[0], EPI == kEpiSwiglu ? p.B[0] : p.A[0]};
@@ -308,31 +308,43 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
 
   // ---- stage this wave's share of X (M x 512 activations) ---------------------
   // Conversion jobs: (token t, group g, quarter r) = 16 activations, elements
-  // 16r..16r+15 of group g of this wave's range. Job 32t + 4g + r runs on lane
+  // 16r..16r+15 of group g of the range. Job 32t + 4g + r runs on lane
   // (32t + 4g + r) % 64 in round t / 2: a group's quarters sit on one quad and a
   // token's eight groups on 32 lanes, so the group sums and the token maximum
   // are DPP / row-swap reductions, and the work grows with M only.
   const int jt = lane >> 5, jg = (lane >> 2) & 7, jr = lane & 3;
-  u32x4 pc[kTok / 2][2];  // converted pieces of each round's job
   const int k0 = (gw0 + jg) * 64 + 16 * jr;  // the job's first column (same in every round)
   const bool gok = gw0 + jg < p.gpr;
-  // every round's activation loads first: one memory round trip for the range
-  float v[kTok / 2][16];
-  float gv[16];
-  if (norm && gok) {
-    load_f16<8>(p.norm_w, k0, gv);
-    load_f16<8>(p.norm_w, k0 + 8, gv + 8);
+  // Every round's activations and the norm weights first, as buffer loads of
+  // raw bits (a masked job reads zeros; only wave-uniform branches, so the
+  // conversion of each round waits for its own loads alone): one memory
+  // round trip for the range.
+  const uint32_t elem = p.x_f32 ? 4u : 2u;
+  const uint32_t tok_bytes = (uint32_t)p.K * elem;
+  const uint32_t job_bytes = 16u * elem;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)M * tok_bytes);
+  u32x4 xr[kTok / 2][4];
+  u32x4 gr[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  if (norm) {
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.norm_w, (uint32_t)p.K * 2u);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      gr[h] = __builtin_amdgcn_raw_buffer_load_b128(rg, gok ? (uint32_t)k0 * 2u + 16u * h : kOOB, 0, 0);
   }
 #pragma unroll
   for (int rd = 0; rd < kTok / 2; ++rd) {
+    xr[rd][0] = xr[rd][1] = xr[rd][2] = xr[rd][3] = u32x4{0u, 0u, 0u, 0u};
+    if (2 * rd >= M) continue;  // wave-uniform
     const int t = 2 * rd + jt;
-    if (2 * rd < M && t < M && gok) {
-      const char* xt = static_cast<const char*>(p.x) + (size_t)t * p.K * (p.x_f32 ? 4 : 2);
-      load_x<8>(xt, p.x_f32, k0, v[rd]);
-      load_x<8>(xt, p.x_f32, k0 + 8, v[rd] + 8);
-    } else {
+    const bool ok = t < M && gok;
+    const uint32_t base = (uint32_t)t * tok_bytes + (uint32_t)k0 * elem;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[rd][i] = 0.f;
+    for (int h = 0; h < 2; ++h)
+      xr[rd][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? base + 16u * h : kOOB, 0, 0);
+    if (p.x_f32) {  // wave-uniform
+#pragma unroll
+      for (int h = 2; h < 4; ++h)
+        xr[rd][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? base + 16u * h : kOOB, 0, 0);
     }
   }
   // then the first bands' codes: they stream in while the activations, which
@@ -343,17 +355,35 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
 #pragma unroll
     for (int a = 0; a < NACC; ++a) issue_band(band + d * p.grid_x, a, d);
   asm volatile("" ::: "memory");
+  float gv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t w = i < 8 ? gr[0][(i >> 1) & 3] : gr[1][(i >> 1) & 3];
+    gv[i] = f16_bits_to_f32((uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
+  }
+  u32x4 pc[kTok / 2][2];  // converted pieces of each round's job
 #pragma unroll
   for (int rd = 0; rd < kTok / 2; ++rd) {
     pc[rd][0] = pc[rd][1] = u32x4{0u, 0u, 0u, 0u};
     if (2 * rd >= M) continue;  // wave-uniform
     const int t = 2 * rd + jt;
+    float v[16];
+    if (p.x_f32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(xr[rd][i >> 2][i & 3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t w = xr[rd][i >> 3][(i >> 1) & 3];
+        v[i] = f16_bits_to_f32((uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
+      }
+    }
     if (norm) {
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        ss = fmaf(v[rd][i], v[rd][i], ss);
-        v[rd][i] *= gok ? gv[i] : 0.f;
+        ss = fmaf(v[i], v[i], ss);
+        v[i] *= gv[i];
       }
       ss = half_sum(ss);  // over the token's 32 lanes
       if ((lane & 31) == 0 && t < M) ssq[wave][t] = ss;
@@ -361,8 +391,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
     float sm = 0.f, mx = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sm += v[rd][i];
-      mx = fmaxf(mx, fabsf(v[rd][i]));
+      sm += v[i];
+      mx = fmaxf(mx, fabsf(v[i]));
     }
     sm = quad_sum(sm);
     mx = half_max(mx);
@@ -372,8 +402,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
     if ((lane & 31) == 0 && t < M) bk[wave][t] = ldexpf(1.0f, BACK_BIAS + E);
     const float inv = ldexpf(1.0f, -E);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[rd][i] *= inv;
-    job_pieces<BITS, FMT>(v[rd], pc[rd]);
+    for (int i = 0; i < 16; ++i) v[i] *= inv;
+    job_pieces<BITS, FMT>(v, pc[rd]);
   }
   // pieces -> LDS -> operands, one half of the range (groups 0-3, then 4-7) at a
   // time: operand P of lane (q, col) is piece (P, q) of token col
@@ -419,33 +449,23 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
       xb = f16x8_of(d[0], d[1], d[2], d[3]);
     }
   }
-
-  // sum of squares per token for the norm over all of K when the row is split
-  // over several workgroups (otherwise the eight waves' shares above)
-  if (norm && p.splits > 1) {
-    __syncthreads();  // the per-range shares above are replaced
-    for (int j = 0; j < M; ++j) {
-      float part = 0.f;
-      const char* xj = static_cast<const char*>(p.x) + (size_t)j * p.K * (p.x_f32 ? 4 : 2);
-      for (int k = threadIdx.x * 8; k < p.K; k += kThreads * 8) {
-        float v[8];
-        load_x<8>(xj, p.x_f32, k, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) part = fmaf(v[i], v[i], part);
-      }
-      part = wave_sum(part);
-      if (lane == 0) ssq[wave][j] = part;
-    }
-  }
   __syncthreads();
   // the thread that finishes output (token ot, row orow) of each band
   const int ot = threadIdx.x >> 4, orow = threadIdx.x & 15;
   const bool out_thread = threadIdx.x < kBand * M;
+  // Sum of squares of the slice per token (the waves' ranges in order); when
+  // the row is cut into slices, the workgroup that adds them takes the norm
+  // over all of K from every slice's sum.
   float rs = 1.f;
   if (norm && out_thread) {
     float t = 0.f;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) t += ssq[w][ot];
-    rs = 1.0f / sqrtf(t / (float)p.K + p.eps);
+    if (p.splits > 1) {
+      if (orow == 0) handoff_store(&p.mm_ssq[slice * kTok + ot], t);
+    } else {
+      rs = 1.0f / sqrtf(t / (float)p.K + p.eps);
+    }
   }
 
   auto finish = [&](int n, const float* v) {
@@ -488,9 +508,9 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
         const uint32_t xs4[4] = {X.x, X.y, X.z, X.w}, ys4[4] = {Y.x, Y.y, Y.z, Y.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t xr = row_ror8(xs4[j]), yr = row_ror8(ys4[j]);
-          w[j] = lo ? xs4[j] : yr;
-          w[4 + j] = lo ? xr : ys4[j];
+          const uint32_t xr4 = row_ror8(xs4[j]), yr4 = row_ror8(ys4[j]);
+          w[j] = lo ? xs4[j] : yr4;
+          w[4 + j] = lo ? xr4 : ys4[j];
         }
         cross_rows_4x4(w[0], w[1], w[2], w[3]);
         cross_rows_4x4(w[4], w[5], w[6], w[7]);
@@ -568,6 +588,11 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const MvParams p) {
     __syncthreads();
     if (!last_flag) return;
     if (out_thread) {
+      if (norm) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.mm_ssq, (uint32_t)(p.splits * kTok * 4));
+        const float t = coherent_sum(rq, (uint32_t)(ot * 4), (uint32_t)(kTok * 4), p.splits);
+        rs = 1.0f / sqrtf(t / (float)p.K + p.eps);
+      }
       const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.partials, (uint32_t)(p.splits * NACC * M * p.N * 4));
       const uint32_t sstride = (uint32_t)(NACC * M * p.N * 4);
       for (int b = tile; b < nbands; b += p.grid_x) {

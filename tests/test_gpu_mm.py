@@ -31,7 +31,7 @@ def qg():
         pytest.skip("no GPU")
     qg.lib()
     yield qg
-    for k in range(5):
+    for k in range(7):
         qg.qg_tune(k, 0)
 
 
