@@ -903,17 +903,23 @@ def run_phases(args, qg, synth, dev):
         err.zero_()
         t_bar = timed(lambda: qg.qg_probe_phases(src, rng, n, True, out, blocks, flags, err),
                       prep=flags.zero_)
+        # the barrier with each range's first loads issued before the wait
+        t_pre = timed(lambda: qg.qg_probe_phases(src, rng, n, 2, out, blocks, flags, err),
+                      prep=flags.zero_)
         torch.cuda.synchronize()
         if int(err.item()):
             raise RuntimeError("phase barrier exceeded its spin limit; timing void")
         res[f"{wg_per_cu}_wg_per_cu"] = {
             "blocks": blocks, "us_launch_per_range": round(t_launch, 1),
             "us_one_launch": round(t_one, 1), "us_one_launch_barrier": round(t_bar, 1),
+            "us_one_launch_barrier_prefetch": round(t_pre, 1),
             "us_per_launch_boundary": round((t_launch - t_one) / (n - 1), 3),
             "us_per_barrier": round((t_bar - t_one) / (n - 1), 3),
+            "us_per_barrier_prefetch": round((t_pre - t_one) / (n - 1), 3),
             "gbs_launch_per_range": round(nbytes / (t_launch * 1e-6) / 1e9, 1),
             "gbs_one_launch": round(nbytes / (t_one * 1e-6) / 1e9, 1),
-            "gbs_one_launch_barrier": round(nbytes / (t_bar * 1e-6) / 1e9, 1)}
+            "gbs_one_launch_barrier": round(nbytes / (t_bar * 1e-6) / 1e9, 1),
+            "gbs_one_launch_barrier_prefetch": round(nbytes / (t_pre * 1e-6) / 1e9, 1)}
         log(f"phases {wg_per_cu} wg/cu: {res[f'{wg_per_cu}_wg_per_cu']}")
     best = min(res.values(), key=lambda r: r["us_launch_per_range"])
     us = best["us_launch_per_range"]

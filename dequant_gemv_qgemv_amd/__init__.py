@@ -205,13 +205,15 @@ def qg_probe_copy(dst, src, blocks: int, stream=None):
                                _stream(stream)), "qg_probe_copy")
 
 
-def qg_probe_phases(src, ranges, nphases: int, barrier: bool, out, blocks: int, flags=None,
+def qg_probe_phases(src, ranges, nphases: int, barrier, out, blocks: int, flags=None,
                     err=None, spin_limit: int = 1 << 20, stream=None):
     """Streams nphases byte ranges of src (ranges: int64 [2*nphases] device
     tensor of offset, count) in one launch, with or without a grid barrier
-    between them (phase probe)."""
+    between them (phase probe). barrier: False / True (= 1), or 2 for the
+    barrier with the next range's first loads issued before the wait."""
+    mode = int(barrier)
     _check(lib().qg_probe_phases(_ptr(src), src.numel() * src.element_size(), _ptr(ranges),
-                                 nphases, 1 if barrier else 0, _ptr(flags), _ptr(out), _ptr(err),
+                                 nphases, mode, _ptr(flags), _ptr(out), _ptr(err),
                                  blocks, spin_limit, _stream(stream)), "qg_probe_phases")
 
 

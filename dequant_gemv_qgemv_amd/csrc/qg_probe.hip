@@ -61,6 +61,9 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(u32x4* __rest
 // for its outputs), waits for that store, raises its flag to the phase
 // number, and wave 0 polls every flag until all have reached it. The poll is
 // bounded: past spin_limit rounds the workgroup counts an error and stops.
+// Mode 2 issues each thread's first loads of the next range before the wait
+// (a matvec's weights do not depend on the barrier, only its x does), so the
+// memory pipe has work while the workgroup waits.
 constexpr int kPhaseThreads = 512;
 constexpr int kPhaseMaxBlocks = 1024;  // with the barrier
 
@@ -74,12 +77,24 @@ __global__ __launch_bounds__(kPhaseThreads) void probe_phases_kernel(
   const size_t stride = (size_t)G * kPhaseThreads;
   if (threadIdx.x == 0) stop = 0;
   uint32_t acc = 0;
-  for (int q = 0; q < nphases; ++q) {
-    // a range past the end of src is clipped to it
+  u32x4 pre[kUnroll];  // mode 2: the next range's first loads
+  bool have_pre = false;
+  // a range past the end of src is clipped to it
+  auto range_of = [&](int q, size_t* n16) {
     const size_t off16 = min((size_t)(ranges[2 * q] / 16), src16);
-    const size_t n16 = min((size_t)(ranges[2 * q + 1] / 16), src16 - off16);
-    const u32x4* const base = src + off16;
+    *n16 = min((size_t)(ranges[2 * q + 1] / 16), src16 - off16);
+    return src + off16;
+  };
+  for (int q = 0; q < nphases; ++q) {
+    size_t n16;
+    const u32x4* const base = range_of(q, &n16);
     size_t i = tid;
+    if (have_pre) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc ^= pre[u].x ^ pre[u].y ^ pre[u].z ^ pre[u].w;
+      i = tid + kUnroll * stride;
+      have_pre = false;
+    }
     for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
       u32x4 v[kUnroll];
 #pragma unroll
@@ -92,12 +107,27 @@ __global__ __launch_bounds__(kPhaseThreads) void probe_phases_kernel(
       acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     if (!barrier || q + 1 == nphases) continue;
+    auto prefetch = [&]() {
+      if (barrier != 2) return;
+      size_t nn;
+      const u32x4* const nb = range_of(q + 1, &nn);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const size_t j = tid + u * stride;
+        pre[u] = j < nn ? __builtin_nontemporal_load(nb + j) : u32x4{0u, 0u, 0u, 0u};
+      }
+      have_pre = true;
+    };
+    // wave 0 issues its loads after raising its flag (its wait for its own
+    // stores would wait for them too)
+    if (wave != 0) prefetch();
     __syncthreads();
     if (wave == 0) {
       if (lane == 0) handoff_store(&out[(size_t)g * kPhaseThreads], acc);
       stores_done();
       const uint32_t want = (uint32_t)(q + 1);
       if (lane == 0) handoff_store(&flags[g], want);
+      prefetch();
       const __amdgpu_buffer_rsrc_t rf = make_rsrc(flags, (uint32_t)G * 4u);
       for (int spins = 0;; ++spins) {
         asm volatile("" ::: "memory");  // a fresh read of the flags every round
@@ -151,7 +181,7 @@ int qg_probe_phases(const void* src, size_t src_bytes, const uint64_t* ranges, i
                     int spin_limit, hipStream_t stream) {
   if (!src || !ranges || !out || src_bytes % 16 || ((uintptr_t)src % 16) ||
       ((uintptr_t)ranges % 8) || nphases < 1 || nphases > 4096 || blocks < 1 || blocks > 65536 ||
-      (barrier != 0 && barrier != 1) || spin_limit < 1 || spin_limit > (1 << 22))
+      barrier < 0 || barrier > 2 || spin_limit < 1 || spin_limit > (1 << 22))
     return QG_EINVAL;
   if (barrier) {
     if (!flags || !err || ((uintptr_t)flags % 4)) return QG_EINVAL;

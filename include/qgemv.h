@@ -344,7 +344,10 @@ int qg_probe_copy(void *dst, const void *src, size_t bytes, int blocks, hipStrea
  * (byte offset, byte count), each a multiple of 16; a range is clipped to
  * src_bytes. barrier = 1 adds a device-wide barrier between ranges (each
  * workgroup publishes one coherent word, raises flags[block] to the range
- * number and waits for every flag): flags [blocks] must be zero at launch,
+ * number and waits for every flag); barrier = 2 does the same and issues
+ * each thread's first loads of the next range before the wait (as a
+ * persistent kernel would fetch the next matvec's weights, which do not
+ * depend on the barrier). With a barrier, flags [blocks] must be zero at launch,
  * err [1] counts workgroups whose wait exceeded
  * spin_limit polls (1 <= spin_limit <= 2^22; the launch then ends early and
  * its timing is void). With barrier = 1, blocks must not exceed 1024 nor

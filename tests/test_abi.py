@@ -245,12 +245,14 @@ def test_phase_probe_checks_arguments(L):
     assert L.qg_probe_phases(None, 256, p, 1, 0, None, p, None, 4, 16, None) == qg.QG_EINVAL
     assert L.qg_probe_phases(p, 250, p, 1, 0, None, p, None, 4, 16, None) == qg.QG_EINVAL
     assert L.qg_probe_phases(p, 256, p, 0, 0, None, p, None, 4, 16, None) == qg.QG_EINVAL
-    assert L.qg_probe_phases(p, 256, p, 1, 2, None, p, None, 4, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 256, p, 1, 3, None, p, None, 4, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 256, p, 1, -1, None, p, None, 4, 16, None) == qg.QG_EINVAL
     assert L.qg_probe_phases(p, 256, p, 1, 0, None, p, None, 0, 16, None) == qg.QG_EINVAL
     assert L.qg_probe_phases(p, 256, p, 1, 0, None, p, None, 4, 0, None) == qg.QG_EINVAL
     # the barrier needs its flags and error counter
     assert L.qg_probe_phases(p, 256, p, 1, 1, None, p, p, 4, 16, None) == qg.QG_EINVAL
     assert L.qg_probe_phases(p, 256, p, 1, 1, p, p, None, 4, 16, None) == qg.QG_EINVAL
+    assert L.qg_probe_phases(p, 256, p, 1, 2, None, p, p, 4, 16, None) == qg.QG_EINVAL
 
 
 def test_empty_rows_is_a_no_op(L):

@@ -52,11 +52,12 @@ def test_read_and_copy_probes(qg):
     assert torch.equal(dst, src)
 
 
-@pytest.mark.parametrize("barrier", [False, True])
+@pytest.mark.parametrize("barrier", [0, 1, 2])
 def test_phase_probe_reads_every_range_once(qg, barrier):
     """Five ragged ranges (one clipped at the end of src), 48 workgroups:
-    the XOR over the output is the XOR of the words in the ranges, with and
-    without the barrier between them, and no barrier wait ran out."""
+    the XOR over the output is the XOR of the words in the ranges, without
+    the barrier between them, with it, and with it and the next range's
+    first loads issued before the wait; no barrier wait ran out."""
     print(f"phase probe barrier={barrier}", flush=True)
     sys.stdout.flush()
     n = 1 << 20
