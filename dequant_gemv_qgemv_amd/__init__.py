@@ -108,6 +108,46 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _need(t, n: int, name: str, dtypes=None):
+    """A tensor handed to the library by pointer must be contiguous, of one of
+    `dtypes` (torch dtypes) when given, and hold at least n elements: the
+    C-ABI cannot see its size, so an undersized buffer is refused here."""
+    if t is None:
+        return
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{name}: {t.numel()} elements, needs at least {n}")
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _f16():
+    """fp16 data, as float16 or as its raw 16-bit patterns"""
+    import torch
+    return (torch.float16, torch.int16)
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
+
+
+def _x_for(x, W_K: int, name: str = "x"):
+    """M of an activation tensor [K] or [M, K] whose row length is W_K."""
+    import torch
+    M = 1 if x.dim() == 1 else x.shape[0]
+    _need(x, M * W_K, name, (torch.float16, torch.float32))
+    if x.shape[-1] != W_K or x.dim() > 2:
+        raise ValueError(f"{name}: shape {tuple(x.shape)}, expected [{W_K}] or [M, {W_K}]")
+    return M
+
+
 def _xdtype(x):
     import torch
     if x.dtype == torch.float16:
@@ -129,6 +169,13 @@ class QMat:
                  fmt: int = QG_AFFINE, group: int = 64):
         self.q, self.scales, self.biases, self.lut = q, scales, biases, lut
         self.N, self.K, self.bits, self.fmt, self.group = N, K, bits, fmt, group
+        words = N * (K * (16 if fmt == QG_DENSE else bits) // 32)
+        _need(q, words, "q")
+        if fmt == QG_AFFINE:
+            _need(scales, N * (K // max(group, 1)), "scales", _f16())
+            _need(biases, N * (K // max(group, 1)), "biases", _f16())
+        if fmt == QG_LUT:
+            _need(lut, N * 16, "lut", _f16())
         self.c = qg_qmat(q.data_ptr() if q is not None else None,
                          scales.data_ptr() if scales is not None else None,
                          biases.data_ptr() if biases is not None else None,
@@ -226,9 +273,11 @@ def _ws_args(ws):
 def qgemv(W: QMat, x, residual=None, y=None, ws=None, stream=None):
     """y = residual + W x  (x: [K] or [M, K] fp16/fp32; y fp32)."""
     import torch
-    M = 1 if x.dim() == 1 else x.shape[0]
+    M = _x_for(x, W.K)
     if y is None:
         y = torch.empty((W.N,) if x.dim() == 1 else (M, W.N), dtype=torch.float32, device=x.device)
+    _need(y, M * W.N, "y", _f32())
+    _need(residual, M * W.N, "residual", _f32())
     wp, wn = _ws_args(ws)
     _check(lib().qgemv(ctypes.byref(W.c), W.N, W.K, M, W.group, W.bits, W.fmt, _ptr(x),
                        _xdtype(x), _ptr(residual), _ptr(y), wp, wn, _stream(stream)), "qgemv")
@@ -239,9 +288,12 @@ def qgemv_rmsnorm(W: QMat, x, norm_w, eps: float = 1e-5, residual=None, y=None, 
                   stream=None):
     """y = residual + W rmsnorm(x; norm_w, eps)."""
     import torch
-    M = 1 if x.dim() == 1 else x.shape[0]
+    M = _x_for(x, W.K)
     if y is None:
         y = torch.empty((W.N,) if x.dim() == 1 else (M, W.N), dtype=torch.float32, device=x.device)
+    _need(y, M * W.N, "y", _f32())
+    _need(residual, M * W.N, "residual", _f32())
+    _need(norm_w, W.K, "norm_w", _f16())
     wp, wn = _ws_args(ws)
     _check(lib().qgemv_rmsnorm(ctypes.byref(W.c), W.N, W.K, M, W.group, W.bits, W.fmt, _ptr(x),
                                _xdtype(x), _ptr(norm_w), float(eps), _ptr(residual), _ptr(y), wp,
@@ -253,10 +305,12 @@ def qswiglu(Wgate: QMat, Wup: QMat, x, norm_w=None, eps: float = 1e-5, u=None, w
             stream=None):
     """u = silu(Wgate x') * (Wup x'), x' = rmsnorm(x) when norm_w is given."""
     import torch
-    M = 1 if x.dim() == 1 else x.shape[0]
+    M = _x_for(x, Wgate.K)
     if u is None:
         u = torch.empty((Wgate.N,) if x.dim() == 1 else (M, Wgate.N), dtype=torch.float32,
                         device=x.device)
+    _need(u, M * Wgate.N, "u", _f32())
+    _need(norm_w, Wgate.K, "norm_w", _f16())
     wp, wn = _ws_args(ws)
     _check(lib().qswiglu(ctypes.byref(Wgate.c), ctypes.byref(Wup.c), Wgate.N, Wgate.K, M,
                          Wgate.group, Wgate.bits, Wgate.fmt, _ptr(x), _xdtype(x), _ptr(norm_w),
@@ -273,8 +327,14 @@ def qmoe_experts(gate_all: QMat, up_all: QMat, down_all: QMat, n_experts: int, s
     import torch
     F = gate_all.N // n_experts
     H = gate_all.K
+    _need(x, H, "x", _f32())
     if y is None:
         y = torch.empty_like(x)
+    _need(y, H, "y", _f32())
+    _need(router_logits, n_experts, "router_logits", _f32())
+    _need(norm_w, H, "norm_w", _f16())
+    _need(sel_ids, top_k, "sel_ids", _i32())
+    _need(sel_w, top_k, "sel_w", _f32())
     sh = None
     if shared3 is not None:
         arr = (qg_qmat * 3)(shared3[0].c, shared3[1].c, shared3[2].c)
@@ -297,8 +357,14 @@ def qmoe_experts_batch(gate_all: QMat, up_all: QMat, down_all: QMat, n_experts: 
     F = gate_all.N // n_experts
     H = gate_all.K
     M = x.shape[0]
+    _need(x, M * H, "x", _f32())
     if y is None:
         y = torch.empty_like(x)
+    _need(y, M * H, "y", _f32())
+    _need(router_logits, M * n_experts, "router_logits", _f32())
+    _need(norm_w, H, "norm_w", _f16())
+    _need(sel_ids, M * top_k, "sel_ids", _i32())
+    _need(sel_w, M * top_k, "sel_w", _f32())
     sh = None
     if shared3 is not None:
         arr = (qg_qmat * 3)(shared3[0].c, shared3[1].c, shared3[2].c)
@@ -323,6 +389,11 @@ def qlogits_topk(W: QMat, x, k: int, norm_w=None, eps: float = 1e-5, logits=None
         idx = torch.empty(k, dtype=torch.int32, device=dev)
     if vals is None:
         vals = torch.empty(k, dtype=torch.float32, device=dev)
+    _need(x, W.K, "x", (torch.float16, torch.float32))
+    _need(norm_w, W.K, "norm_w", _f16())
+    _need(logits, W.N, "logits", _f32())
+    _need(idx, k, "idx", _i32())
+    _need(vals, k, "vals", _f32())
     wp, wn = _ws_args(ws)
     _check(lib().qlogits_topk(ctypes.byref(W.c), W.N, W.K, W.group, W.bits, W.fmt, _ptr(x),
                               _xdtype(x), _ptr(norm_w), float(eps), _ptr(logits), k, _ptr(idx),
@@ -341,6 +412,11 @@ def qlogits_topk_noalloc(W: QMat, x, k: int, norm_w=None, eps: float = 1e-5, log
         idx = torch.empty(k, dtype=torch.int32, device=dev)
     if vals is None:
         vals = torch.empty(k, dtype=torch.float32, device=dev)
+    _need(x, W.K, "x", (torch.float16, torch.float32))
+    _need(norm_w, W.K, "norm_w", _f16())
+    _need(logits, W.N, "logits", _f32())
+    _need(idx, k, "idx", _i32())
+    _need(vals, k, "vals", _f32())
     _check(lib().qlogits_topk_noalloc(ctypes.byref(W.c), W.N, W.K, W.group, W.bits, W.fmt, _ptr(x),
                                       _xdtype(x), _ptr(norm_w), float(eps), _ptr(logits), k,
                                       _ptr(idx), _ptr(vals), _stream(stream)),
@@ -362,8 +438,15 @@ def qlogits_sample(W: QMat, x, k: int, temperature: float, top_p: float, seed: i
         idx = torch.empty(k, dtype=torch.int32, device=dev)
     if vals is None:
         vals = torch.empty(k, dtype=torch.float32, device=dev)
+    _need(x, W.K, "x", (torch.float16, torch.float32))
+    _need(norm_w, W.K, "norm_w", _f16())
+    _need(logits, W.N, "logits", _f32())
+    _need(idx, k, "idx", _i32())
+    _need(vals, k, "vals", _f32())
     if token is None:
         token = torch.empty(1, dtype=torch.int32, device=dev)
+    _need(token, 1, "token", _i32())
+    _need(counter, 1, "counter", (torch.int64,))
     wp, wn = _ws_args(ws)
     _check(lib().qlogits_sample(ctypes.byref(W.c), W.N, W.K, W.group, W.bits, W.fmt, _ptr(x),
                                 _xdtype(x), _ptr(norm_w), float(eps), _ptr(logits), k, _ptr(idx),
@@ -381,8 +464,16 @@ def qattn_decode(q, k_cache, v_cache, pos: int, scale: float, k_new=None, v_new=
     import torch
     H, d = q.shape
     Hkv, T_max, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != (Hkv, T_max, d):
+        raise ValueError("k_cache / v_cache must both be [Hkv][T_max][d] with q's d")
+    _need(q, H * d, "q", _f32())
+    _need(k_cache, Hkv * T_max * d, "k_cache", _f16())
+    _need(v_cache, Hkv * T_max * d, "v_cache", _f16())
+    _need(k_new, Hkv * d, "k_new", _f32())
+    _need(v_new, Hkv * d, "v_new", _f32())
     if out is None:
         out = torch.empty(H, d, dtype=torch.float32, device=q.device)
+    _need(out, H * d, "out", _f32())
     wp, wn = _ws_args(ws)
     _check(lib().qattn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                               H, Hkv, d, T_max, int(pos), float(scale), _ptr(out), wp, wn,
@@ -396,6 +487,10 @@ def qg_sample_topk(idx, vals, temperature: float, top_p: float, seed: int, count
     import torch
     if token is None:
         token = torch.empty(1, dtype=torch.int32, device=idx.device)
+    _need(idx, 1, "idx", _i32())
+    _need(vals, idx.numel(), "vals", _f32())
+    _need(token, 1, "token", _i32())
+    _need(counter, 1, "counter", (torch.int64,))
     _check(lib().qg_sample_topk(_ptr(idx), _ptr(vals), int(idx.numel()), float(temperature),
                                 float(top_p), seed & (2**64 - 1), _ptr(counter), _ptr(token),
                                 _stream(stream)), "qg_sample_topk")
