@@ -312,7 +312,7 @@ def probe_peaks(qg, dev):
 
     def best(fn, moved):
         rates = []
-        for blocks in (1024, 2048, 4096, 8192, 16384):
+        for blocks in (256, 512, 1024, 2048, 4096, 8192, 16384):
             fn(blocks)
             torch.cuda.synchronize()
             e0.record()
@@ -331,7 +331,7 @@ def probe_peaks(qg, dev):
     torch.cuda.empty_cache()
     return {"read_gbs": round(read, 1), "copy_gbs": round(copy, 1), "torch_copy_gbs": round(tcopy, 1),
             "how": "qg_probe_read / qg_probe_copy over 1 GiB, 16-byte accesses (read: non-temporal "
-                   "and cached, copy: non-temporal), best of 1024..16384 workgroups of 256 threads, "
+                   "and cached, copy: non-temporal), best of 256..16384 workgroups of 256 threads, "
                    "10 launches each; copy counts read + write bytes"}
 
 
