@@ -527,14 +527,51 @@ def run_stack(args, qg, synth, dev):
         for d in layers:
             qg.qswiglu(d["gate"], d["up"], h, d["g_ffn"], EPS, u=u, ws=ws)
 
-    sw_us = time_launches(swiglu_all, len(layers), graph is not None)
+    sw_us = time_launches(swiglu_all, len(layers), graph is not None, reps=10)
     fmt_name = {0: f"{bits}-bit g64 planar", 1: "4-bit 16-entry table per row",
                 2: "dense fp16 weights"}[fmt]
     path = "matrix cores" if bits in (2, 4) else "one pass per vector"
     kname = ("qswiglu" if M == 1 else f"qswiglu M={M} ({path})") + \
         " 14336x4096 x2 (gate.up, rmsnorm)"
     dom = roofline(kname, sw_bytes, sw_us, traffic_of(args, "gate.up"))
+    marginal = None
+    if M == 1:
+        # The same launch over the first 4096, 8192 and 12288 rows of the same
+        # matrices: a least-squares line through the four (bytes, time)
+        # points gives the rate of the extra rows and the part of a launch
+        # that does not depend on its size.
+        pts = [(sw_bytes, sw_us)]
+        row_bytes = (d0["gate"].nbytes() + d0["up"].nbytes()) // FF + 4 * M
+        sizes = [n for n in (4096, 8192, 12288) if n < FF]
+        for n_rows in sizes:
+            def rows(m, n=n_rows):
+                cut = lambda t: None if t is None else t[:n]
+                return qg.QMat(cut(m.q), cut(m.scales), cut(m.biases), cut(m.lut), N=n, K=m.K,
+                               bits=m.bits, fmt=m.fmt, group=m.group)
+
+            part = [(rows(d["gate"]), rows(d["up"]), d["g_ffn"]) for d in layers]
+
+            def swiglu_part(part=part, n=n_rows):
+                for gt, up, gn in part:
+                    qg.qswiglu(gt, up, h, gn, EPS, u=u[:n], ws=ws)
+
+            pts.append((sw_bytes - (FF - n_rows) * row_bytes,
+                        time_launches(swiglu_part, len(layers), graph is not None, reps=10)))
+        bx = np.array([p[0] for p in pts], np.float64)
+        ty = np.array([p[1] for p in pts], np.float64)
+        slope, icpt = np.polyfit(bx, ty, 1) if len(pts) > 2 else (0.0, 0.0)  # us per byte, us
+        if slope > 0:
+            marginal = {"gbs": round(1e-3 / slope, 1), "fixed_us": round(float(icpt), 3),
+                        "points_us": {str(int(n)): round(float(t), 3)
+                                      for n, t in zip([FF] + sizes, ty)},
+                        "how": "the launch at 4096, 8192, 12288 and all 14336 rows of the same "
+                               "matrices (graph replays); least-squares line of time against "
+                               "bytes: its slope gives the rate of the extra rows, its intercept "
+                               "the size-independent part of a launch"}
+            dom["marginal"] = marginal
     peaks = probe_peaks(qg, dev)
+    if marginal:
+        marginal["frac_of_read_peak"] = round(marginal["gbs"] / peaks["read_gbs"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
