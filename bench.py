@@ -69,7 +69,8 @@ def traffic_name(args) -> str:
     """File stem of a workload's counter summary under profiles/."""
     if args.config == "stack":
         fmt = {0: f"{args.bits}bit", 1: "lut", 2: "dense_f16"}[args.fmt]
-        return f"traffic_llama3_8b_stack_{fmt}_m{args.m}"
+        tp = f"_tp{args.tp}" if getattr(args, "tp", 1) > 1 else ""
+        return f"traffic_llama3_8b_stack_{fmt}_m{args.m}{tp}"
     return {"single": "traffic_qgemv_2048x2048_single", "moe": f"traffic_qmoe_512_experts_m{args.m}",
             "qwen": "traffic_qwen3_06b_stack_logits", "attn": "traffic_qattn",
             "phases": "traffic_phases"}[args.config]
@@ -447,7 +448,7 @@ def run_stack(args, qg, synth, dev):
     """Llama-3-8B-shaped decode stack; M activation vectors per step."""
     import torch
     bits, fmt, M = args.bits, args.fmt, args.m
-    model = dict(synth.LLAMA3_8B)
+    model = synth.tp_shard(synth.LLAMA3_8B, args.tp)
     model["layers"] = args.layers
     H, FF, QD, NQ = model["hidden"], model["ffn"], model["q_dim"], model["qkv"]
 
@@ -483,7 +484,7 @@ def run_stack(args, qg, synth, dev):
     a = torch.empty(shp(QD), dtype=torch.float32, device=dev)
     h = torch.empty(shp(H), dtype=torch.float32, device=dev)
     u = torch.empty(shp(FF), dtype=torch.float32, device=dev)
-    ws = qg.workspace(qg.QG_OP_SWIGLU, FF, FF, M, bits, fmt, 1, dev)
+    ws = qg.workspace(qg.QG_OP_SWIGLU, max(FF, H), max(FF, H), M, bits, fmt, 1, dev)
 
     def layer_calls(d):
         qg.qgemv_rmsnorm(d["qkv"], x, d["g_attn"], EPS, y=qkv, ws=ws)
@@ -532,7 +533,7 @@ def run_stack(args, qg, synth, dev):
                 2: "dense fp16 weights"}[fmt]
     path = "matrix cores" if bits in (2, 4) else "one pass per vector"
     kname = ("qswiglu" if M == 1 else f"qswiglu M={M} ({path})") + \
-        " 14336x4096 x2 (gate.up, rmsnorm)"
+        f" {FF}x{H} x2 (gate.up, rmsnorm)"
     dom = roofline(kname, sw_bytes, sw_us, traffic_of(args, "gate.up"))
     marginal = None
     if M == 1:
@@ -597,8 +598,11 @@ def run_stack(args, qg, synth, dev):
                                  f"{done / 1e9:.3f} GB of weights) in {dt:.1f} s, fp64 scalar C"),
             lambda n, done, dt: {"steps_per_s": round(n / len(host_layers) / dt, 6)})
     workload = f"llama3-8b-shaped decode stack, {fmt_name}, M={M}"
+    if args.tp > 1:
+        workload += (f", one GPU's shard at tensor parallelism {args.tp} (qkv {NQ} rows, o {H}x{QD}, "
+                     f"gate.up {FF} rows, down {H}x{FF}; no all-reduce)")
     cfg = {"layers": model["layers"], "hidden": H, "qkv": NQ, "ffn": FF, "bits": bits, "fmt": fmt,
-           "m": M, "graph": graph is not None}
+           "m": M, "graph": graph is not None, **({"tp": args.tp} if args.tp > 1 else {})}
     emit(args, workload, cfg, step_bytes, ms, dom, peaks, cpu, arith_dtype(bits, fmt, M))
 
 
@@ -1047,6 +1051,10 @@ def main():
     ap.add_argument("--m", type=int, default=1,
                     help="stack: activation vectors per step; moe: tokens per batched call (1..8)")
     ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--tp", type=int, default=1, choices=[1, 2, 4, 8],
+                    help="stack, M = 1: the layers of one GPU's shard under tensor parallelism "
+                         "TP (qkv and gate/up rows, o and down inputs divided by TP; the "
+                         "all-reduces are not run)")
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--tune", action="append", default=[], metavar="KNOB=VALUE", type=tune_arg,
@@ -1082,6 +1090,9 @@ def main():
         sys.exit(2)
     if not 1 <= args.m <= 8:
         print("bench.py: --m must be 1..8", file=sys.stderr)
+        sys.exit(2)
+    if args.tp > 1 and (args.config != "stack" or args.m != 1):
+        print("bench.py: --tp is for --config stack with --m 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

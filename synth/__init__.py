@@ -123,6 +123,21 @@ MOE_397B = dict(name="moe-397b-expert-layer", hidden=4096, ffn=1024, experts=512
                 top_k=3, draws=60)
 
 
+def tp_shard(model: dict, tp: int) -> dict:
+    """The decode layer one GPU holds under tensor parallelism `tp` (rows of
+    qkv and gate/up, and the inputs of o and down, divided by tp; hidden size
+    and layer count unchanged). Its weights are drawn from their own streams."""
+    m = dict(model)
+    if tp == 1:
+        return m
+    for k in ("qkv", "q_dim", "o_in", "ffn"):
+        if tp < 1 or model[k] % (tp * 64):
+            raise ValueError(f"{k} = {model[k]} does not split into {tp} shards of whole groups")
+        m[k] = model[k] // tp
+    m["name"] = f"{model['name']} tp{tp} shard"
+    return m
+
+
 def layer_shapes(model: dict) -> dict:
     """(N, K) of each matvec in one decode layer."""
     H = model["hidden"]

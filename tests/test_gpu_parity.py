@@ -549,6 +549,34 @@ def test_llama_layer_full_size(qg):
     close(y.cpu().numpy(), ref, what="layer")
 
 
+@pytest.mark.parametrize("tp", [2, 8])
+def test_llama_tp_shard_layer(qg, tp):
+    """One GPU's shard of the Llama-3-8B-shaped layer under tensor
+    parallelism (qkv 6144/tp rows, o 4096 x 4096/tp, gate.up 14336/tp rows,
+    down 4096 x 14336/tp): the four fused calls at those shapes, each against
+    the oracle on its own input (the all-reduces are outside the path)."""
+    say(f"llama tp{tp} shard layer")
+    model = synth.tp_shard(synth.LLAMA3_8B, tp)
+    w = synth.layer_weights(1234, model, 0)
+    H, QD = model["hidden"], model["q_dim"]
+    x = synth.activations(1234, ("x0", tp), H, np.float32)
+    d = {k: dev_mat(qg, v) for k, v in w.items() if isinstance(v, dict)}
+    ws = qg.workspace(qg.QG_OP_SWIGLU, max(model["ffn"], H), H, 1, 4, 0, 1, DEV)
+    xd = to_dev(x)
+    qkv = qg.qgemv_rmsnorm(d["qkv"], xd, to_dev(w["g_attn"]), 1e-5, ws=ws)
+    h = qg.qgemv(d["o"], qkv[:QD], residual=xd, ws=ws)
+    u = qg.qswiglu(d["gate"], d["up"], h, to_dev(w["g_ffn"]), 1e-5, ws=ws)
+    y = qg.qgemv(d["down"], u, residual=h, ws=ws)
+    torch.cuda.synchronize()
+    qkv_h, h_h, u_h = qkv.cpu().numpy(), h.cpu().numpy(), u.cpu().numpy()
+    close(qkv_h, oracle.rmsnorm_gemv(w["qkv"], x, w["g_attn"], 1e-5, nthreads=8), what="qkv")
+    close(h_h, oracle.gemv(w["o"], qkv_h[:QD].astype(np.float64), x, nthreads=8), what="o")
+    close(u_h, oracle.rmsnorm_swiglu(w["gate"], w["up"], h_h.astype(np.float64), w["g_ffn"], 1e-5,
+                                     nthreads=8), what="gate.up")
+    close(y.cpu().numpy(), oracle.gemv(w["down"], u_h.astype(np.float64), h_h, nthreads=8),
+          what="down")
+
+
 def test_graph_replay_matches_eager(qg):
     """Two Llama-shaped layers captured in a HIP graph, replayed several times
     with eager work between the replays; every replay equals the eager run."""
