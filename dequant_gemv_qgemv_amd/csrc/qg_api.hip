@@ -120,13 +120,19 @@ int pieces_per_chunk(int bits, int fmt) {
 // items instead of one per item: 151936 x 1024 logits 18.1 us against 20.4,
 // 3072 x 1024 gate.up 4.57 against 4.74). Rows of 96..127 chunks: 64 lanes
 // with a partly empty last pass, which keeps twice the bands of 32 lanes for
-// short matrices (1024 x 3072: 3.64 us against 4.27). Rows of 33..64 chunks
-// (2-bit codes at K = 4096): two passes of 32 lanes (4096 x 4096 2-bit
-// 4.46 us against 4.52 with one pass of 64, 14336 x 4096 gate.up 11.40
-// against 12.02).
-int pick_lpr(int C) {
+// short matrices (1024 x 3072: 3.64 us against 4.27). Rows of 33..64 chunks:
+// two passes of 32 lanes up to 8192 rows (4096 x 4096 2-bit 4.46 us against
+// 4.52 with one pass of 64; 4096 x 1792 4-bit 4.35 against 4.96), and beyond
+// that 16 lanes unless they idle more lanes (more rows per band, fewer
+// bands: 14336 x 4096 2-bit gate.up 11.60 against 11.97 with 32 lanes,
+// 14336 x 2048 4-bit 6.22 against 6.39).
+int pick_lpr(int C, int N) {
   if (C > 16 && C <= 32) return 16;
-  if (C > 32 && C <= 64 && C % 32 == 0) return 32;
+  if (C > 32 && C <= 64) {
+    const double e32 = (double)C / (double)(((C + 31) / 32) * 32);
+    const double e16 = (double)C / (double)(((C + 15) / 16) * 16);
+    return (N > 8192 && e16 >= e32) ? 16 : 32;
+  }
   if (C >= 96 && C < 128) return 64;
   const int cands[3] = {64, 32, 16};
   int best = 64;
@@ -153,7 +159,7 @@ struct MvShape {
 MvPlan plan_mv(const MvShape& s, int cus, bool have_ws) {
   MvPlan pl{};
   const int C = s.K / codes_per_chunk(s.bits);
-  pl.lpr = g_knob[2].load() ? g_knob[2].load() : pick_lpr(C);
+  pl.lpr = g_knob[2].load() ? g_knob[2].load() : pick_lpr(C, s.N);
   if (s.col_seg_chunks > 0 && !g_knob[2].load()) {
     // keep every pass inside one K segment when the segments allow it
     for (int l : {64, 32, 16})
