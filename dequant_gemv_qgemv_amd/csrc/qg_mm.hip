@@ -20,7 +20,8 @@
 // LDS) so that each lane holds one row's words, and issues one MFMA per 32
 // codes. The eight waves' results for a band are summed
 // in LDS in a fixed order. K longer than one slice is split across
-// workgroups, combined by the last one to finish (integer ticket).
+// workgroups, combined by the last one to finish (integer ticket), which
+// also takes the norm from every slice's sums of squares.
 //
 // Arithmetic (page "Optimisation FMA du noyau de dequantification":
 // fma(code, s*x, b*x) per group). Codes become fp16 operands exactly: masking
