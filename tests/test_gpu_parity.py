@@ -95,7 +95,8 @@ def ws_for(qg, op, N, K, k=1):
 
 
 # ---------------------------------------------------------------------------
-SHAPES = [(1, 64), (7, 128), (300, 1024), (1000, 3072), (513, 4096), (64, 14336), (2048, 2048)]
+SHAPES = [(1, 64), (7, 128), (300, 1024), (1000, 3072), (513, 4096), (64, 14336), (2048, 2048),
+          (10001, 1792)]  # rows of 56 chunks past 8192 rows: 16 lanes, ragged last band
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
