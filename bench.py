@@ -63,6 +63,8 @@ def kernel_hash() -> str:
 
 
 REF_READ_BYTES = 64 << 20  # reference streaming read of known size for counter calibration
+# where a counter pass writes its launch labels (QG_PMC_DIR overrides)
+PMC_DIR = os.environ.get("QG_PMC_DIR", os.path.join(ROOT, "pmc_out"))
 
 
 def traffic_name(args) -> str:
@@ -94,10 +96,10 @@ def pmc_pass(args, qg, dev, run_once, labels, nbytes, outputs):
     pmc_reference_reads(qg, dev)
     run_once()
     torch.cuda.synchronize()
-    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    os.makedirs(PMC_DIR, exist_ok=True)
     meta = {"workload": traffic_name(args), "labels": labels, "bytes": nbytes, "outputs": outputs,
             "argv": sys.argv[1:], "kernel_hash": kernel_hash()}
-    with open(os.path.join(ROOT, "gpurun_out", "pmc_labels.json"), "w") as fh:
+    with open(os.path.join(PMC_DIR, "pmc_labels.json"), "w") as fh:
         json.dump(meta, fh, indent=1)
     log(f"pmc pass done: {len(labels)} launches")
 
@@ -147,7 +149,7 @@ def summarize_pmc(fetch_csv, write_csv, labels_json):
            "counter_scale": round(scale, 4),
            "argv": meta["argv"], "launches": {}}
     lines = [f"# HBM traffic per launch: {meta['workload']}", "",
-             "Two counter passes, each on its own run (GPU box, repository root as $R):", "",
+             "Two counter passes, each on its own run (on the MI355X, repository root as $R):", "",
              f"    cd /tmp && timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "
              f"$R/{rel(os.path.dirname(fetch_csv))} -o run -- python3 $R/bench.py {' '.join(meta['argv'])}",
              f"    cd /tmp && timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "
@@ -1064,7 +1066,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="two reference reads of 64 MiB, then the workload's launches once, eagerly "
-                         "(for rocprofv3 --pmc counter passes; writes gpurun_out/pmc_labels.json)")
+                         "(for rocprofv3 --pmc counter passes; writes pmc_labels.json under $QG_PMC_DIR, "
+                         "default pmc_out/)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LABELS_JSON"),
                     help="turn the counter CSVs of two --pmc-pass runs into profiles/traffic_*.{json,md}")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
