@@ -730,7 +730,9 @@ def run_moe(args, qg, synth, dev):
     us_layer = ms * 1e3 / L
     kname = ("qmoe_experts (route, gate.up of 4 experts, down + combine)" if M == 1 else
              f"qmoe_experts_batch M={M} (route, gate.up of 4 experts per token, down + combine)")
-    dom = roofline(kname, sum(layer_bytes) / L, us_layer)
+    parts = [traffic_of(args, "route + gate.up"), traffic_of(args, "down + combine")]
+    dom = roofline(kname, sum(layer_bytes) / L, us_layer,
+                   None if None in parts else sum(parts))
     peaks = probe_peaks(qg, dev)
     cpu = None
     if not args.no_cpu_baseline:
@@ -850,8 +852,11 @@ def run_qwen(args, qg, synth, dev):
     # algorithmic bytes: weights, x, norm weight and logits once, top-k out
     # (the two-launch form reads the logits back)
     head_alg = head_bytes + H * 4 + H * 2 + V * 4 + topk * 8 + (V * 4 if head_launches == 2 else 0)
+    parts = ([traffic_of(args, "logits + top-40 (one launch)")] if head_launches == 1 else
+             [traffic_of(args, "logits (rmsnorm + matvec)"), traffic_of(args, "top-40")])
     dom = roofline(f"qlogits_topk 151936x1024 4-bit + final norm + top-40 ({head_launches} launch"
-                   f"{'es' if head_launches > 1 else ''})", head_alg, head_us)
+                   f"{'es' if head_launches > 1 else ''})", head_alg, head_us,
+                   None if None in parts else sum(parts))
     peaks = probe_peaks(qg, dev)
     cpu = None
     if not args.no_cpu_baseline:
